@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c3|c5|c4_h16_q1_bf16|...]
+
+Default workload: the Llama-70B-like GQA decode (64 requests, q_len 1, 64 query
+/ 8 KV heads, head_dim 128, bf16, page 16, KV lengths uniform in [512, 8192]).
+A step is one call of the hot path over the whole batch (every kernel that call
+launches).  Inputs are resident in HBM before the timed region; the timed region
+is bracketed by torch.cuda.synchronize() on both sides.  Prints one JSON line.
+
+Algorithmic bytes count each needed KV row once per KV head (a shared latent
+row once; a broadcast KV batch once), the page ids, Q, O and LSE, and for split
+runs the fp32 partial states written and read.  Flops count 2*Dqk + 2*Dvo per
+(row, allowed token).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2516.6      # dense bf16/fp16 MFMA, TFLOP/s
+METRIC = ("decode attn µs/step + achieved HBM GB/s (% peak); "
+          "prefill TFLOP/s (% MFMA)")
+
+
+def make_workload(name: str):
+    from paged_kv_attention_prefill_amd import workloads as W
+    if name == "c1":
+        return W.config1(poison=False)
+    if name == "c2":
+        return W.config2(poison=False)
+    if name == "c3":
+        return W.config3(poison=False)
+    if name == "c5":
+        return W.config5(poison=False)
+    if name.startswith("c4"):
+        _, h, q, dt = name.split("_")
+        return W.config4(num_heads=int(h[1:]), q_len=int(q[1:]),
+                         kv_dtype=W.DT_FP8 if dt == "fp8" else W.DT_BF16, poison=False)
+    raise SystemExit(f"unknown workload {name}")
+
+
+def allowed_tokens(w) -> np.ndarray:
+    """|J| per query token (all heads share it)."""
+    out = np.empty(w.total_q, dtype=np.int64)
+    for b in range(w.batch):
+        kb = 0 if w.kv_broadcast else b
+        L = int(w.kv_lens[kb])
+        t0, t1 = int(w.qo_indptr[b]), int(w.qo_indptr[b + 1])
+        qb = t1 - t0
+        i = np.arange(qb)
+        out[t0:t1] = np.clip(L - qb + i + 1, 0, L) if w.causal else L
+    return out
+
+
+def algorithmic_counts(w, num_states: int = 1):
+    """(attention-kernel bytes, merge bytes, flops) of one step."""
+    from paged_kv_attention_prefill_amd import workloads as W
+    kvb = W.DT_BYTES[w.kv_dtype]
+    qb = W.DT_BYTES[w.q_dtype]
+    ob = 2 if w.q_dtype != W.DT_F32 else 4
+    lens = w.kv_lens[:1] if w.kv_broadcast else w.kv_lens
+    row_elems = w.head_dim_qk if w.shared_kv else (w.head_dim_qk + w.head_dim_vo)
+    kv_bytes = int(lens.sum()) * w.num_kv_heads * row_elems * kvb
+    table = int(w.kv_indptr[-1]) * 4 + (len(w.kv_indptr) + len(w.kv_last_page_len)) * 4
+    rows = w.total_q * w.num_qo_heads
+    q_bytes = rows * w.head_dim_qk * qb
+    flops = int(allowed_tokens(w).sum()) * w.num_qo_heads * 2 * (w.head_dim_qk + w.head_dim_vo)
+    if num_states > 1:
+        part = num_states * rows * (w.head_dim_vo + 1) * 4
+        attn = kv_bytes + table + q_bytes + part
+        merge = part + rows * (w.head_dim_vo * ob + 4)
+    else:
+        attn = kv_bytes + table + q_bytes + rows * (w.head_dim_vo * ob + 4)
+        merge = 0
+    return attn, merge, flops
+
+
+def cpu_baseline(w, target_s: float = 15.0):
+    """Time the oracle on a bounded sample of query batches (whole batches, all heads),
+    scaled to the whole workload by the sample's share of (row x allowed token) work."""
+    import dataclasses
+    from oracle import oracle as OR
+    work = allowed_tokens(w) * w.num_qo_heads
+    per_batch = np.array([work[w.qo_indptr[b]:w.qo_indptr[b + 1]].sum() for b in range(w.batch)],
+                         dtype=np.float64)
+    order = np.argsort(-per_batch)
+    # calibrate on the smallest batch first
+    rows_of = lambda b: np.arange(w.qo_indptr[b] * w.num_qo_heads,
+                                  w.qo_indptr[b + 1] * w.num_qo_heads, dtype=np.int64)
+    t0 = time.perf_counter()
+    b_small = int(order[-1])
+    OR.attention(w, rows=rows_of(b_small), num_kv_splits=1)
+    t_small = time.perf_counter() - t0
+    rate = per_batch[b_small] / max(t_small, 1e-6)
+    budget = rate * target_s
+    chosen, acc = [], 0.0
+    for b in order[::-1]:  # small to large, so the sample spans several batches
+        if acc + per_batch[b] > budget and chosen:
+            break
+        chosen.append(int(b))
+        acc += per_batch[b]
+    rows = np.concatenate([rows_of(b) for b in chosen])
+    t0 = time.perf_counter()
+    OR.attention(w, rows=rows, num_kv_splits=1)
+    elapsed = time.perf_counter() - t0
+    frac = acc / per_batch.sum()
+    return elapsed / frac, dict(batches=len(chosen), rows=int(rows.size), seconds=elapsed,
+                                fraction=frac, threads=OR.num_threads())
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {a.gpus}); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    from paged_kv_attention_prefill_amd import binding as B
+    from paged_kv_attention_prefill_amd import runner as R
+
+    B.load_library()
+    w = make_workload(a.workload)
+    d = R.upload(w, "cuda:0")
+    stream = torch.cuda.current_stream()
+    call = R.prepare(d)
+
+    for _ in range(a.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(a.steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / a.steps
+
+    # the dominant (attention) kernel alone, same launch configuration, timed with
+    # events on the stream it is launched on
+    attn_ms = call.time_attention_kernel(a.steps)
+    states = call.num_states
+    attn_bytes, merge_bytes, flops = algorithmic_counts(w, states)
+    step_bytes = attn_bytes + merge_bytes
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    decode_like = w.q_len is not None
+    bound_hbm = (attn_bytes / PEAK_HBM_GBS) >= (flops / PEAK_BF16_TFLOPS / 1e3)
+    if bound_hbm:
+        ach = attn_bytes / (attn_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        ach = flops / (attn_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    roof["kernel"] = call.attention_kernel_name
+    roof["kernel_ms"] = round(attn_ms, 5)
+    roof["bytes_per_launch"] = attn_bytes
+    roof["flops_per_launch"] = flops
+
+    if decode_like:
+        value, unit = gbs, "GB/s"
+    else:
+        value, unit = tflops, "TFLOP/s"
+    from paged_kv_attention_prefill_amd import workloads as W
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 5),
+        "us_per_step": round(ms * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": W.DT_NAMES[w.kv_dtype],
+        "data": "synthetic: seeded N(0,1) values, seeded lengths and shuffled page table",
+        "config": {"workload": w.name, **{k: v for k, v in w.manifest().items()
+                                          if k not in ("name",)}},
+        "achieved_hbm_gbs": round(gbs, 1),
+        "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "achieved_tflops": round(tflops, 2),
+        "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": roof,
+    }
+    if not a.no_cpu_baseline:
+        full_s, info = cpu_baseline(w, a.cpu_seconds)
+        cpu_val = (step_bytes / full_s / 1e9) if decode_like else (flops / full_s / 1e12)
+        line["cpu_baseline"] = {"value": round(cpu_val, 6), "unit": unit,
+                                "cores": info["threads"], "kind": "oracle",
+                                "sample": (f"{info['batches']} whole query batches "
+                                           f"({info['rows']} rows, {info['fraction']:.3f} of the "
+                                           f"work) in {info['seconds']:.1f} s, scaled to the "
+                                           "full workload"),
+                                "seconds_full_workload": round(full_s, 2)}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,297 @@
+// C-ABI entry points of libpaged_attn: host-side validation, kernel choice
+// (decided on the host and launched as a specialised kernel rather than
+// branching inside the kernel — FlashInfer PR #4736 analysis, "lessons"
+// section), workspace planning, launch on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/paged_attn.h"
+#include "params.h"
+
+namespace {
+
+using pa::AttnParams;
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("PA_LOG");
+    return e && e[0] == '1';
+  }();
+  return on;
+}
+
+int elem_bytes(int dt) { return dt == PA_F32 ? 4 : dt == PA_FP8_E4M3 ? 1 : 2; }
+bool known_dtype(int dt) { return dt >= PA_F32 && dt <= PA_FP8_E4M3; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_dims(int dqk, int dvo) {
+  return (dqk == 64 && dvo == 64) || (dqk == 128 && dvo == 128) || (dqk == 256 && dvo == 256) ||
+         (dqk == 576 && dvo == 512);
+}
+
+bool supported_combo(int qdt, int kvdt) {
+  return (qdt == PA_F32 && kvdt == PA_F32) || (qdt == PA_F16 && kvdt == PA_F16) ||
+         (qdt == PA_BF16 && kvdt == PA_BF16) || (qdt == PA_BF16 && kvdt == PA_FP8_E4M3) ||
+         (qdt == PA_F16 && kvdt == PA_FP8_E4M3);
+}
+
+// Checks shared by decode and prefill.  Returns PA_OK or the first failure.
+int check_common(const void* q, int q_dtype, int num_qo_heads, const pa_paged_kv& kv,
+                 int kv_broadcast, int expect_kv_batches, const void* o, int o_dtype) {
+  if (!q || !kv.k || !kv.v || !kv.kv_indptr || !kv.kv_indices || !kv.kv_last_page_len || !o)
+    return PA_ERR_NULL;
+  if (!known_dtype(q_dtype) || !known_dtype(kv.kv_dtype) || !known_dtype(o_dtype))
+    return PA_ERR_DTYPE;
+  if (q_dtype == PA_FP8_E4M3 || o_dtype == PA_FP8_E4M3) return PA_ERR_DTYPE;
+  if (num_qo_heads < 1 || kv.num_kv_heads < 1 || kv.page_size < 1) return PA_ERR_SHAPE;
+  if (num_qo_heads % kv.num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (kv.num_kv_batches < 1) return PA_ERR_SHAPE;
+  if (kv_broadcast ? kv.num_kv_batches != 1 : kv.num_kv_batches != expect_kv_batches)
+    return PA_ERR_SHAPE;
+  if (kv.max_kv_len_hint < 0) return PA_ERR_SHAPE;
+  if (kv.head_dim_qk < 1 || kv.head_dim_vo < 1) return PA_ERR_SHAPE;
+  for (int i = 0; i < 3; ++i)
+    if (kv.k_stride[i] < 0 || kv.v_stride[i] < 0) return PA_ERR_SHAPE;
+  if (kv.k == kv.v) {
+    if (kv.head_dim_vo > kv.head_dim_qk) return PA_ERR_SHAPE;
+    for (int i = 0; i < 3; ++i)
+      if (kv.k_stride[i] != kv.v_stride[i]) return PA_ERR_SHAPE;
+  }
+  if (!(std::isfinite(kv.k_scale) && std::isfinite(kv.v_scale))) return PA_ERR_SHAPE;
+  if (!supported_combo(q_dtype, kv.kv_dtype)) return PA_ERR_UNSUPPORTED;
+  if (!supported_dims(kv.head_dim_qk, kv.head_dim_vo)) return PA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(kv.k) || !aligned16(kv.v) || !aligned16(o)) return PA_ERR_ALIGN;
+  const int eb = elem_bytes(kv.kv_dtype);
+  for (int i = 0; i < 3; ++i)
+    if ((kv.k_stride[i] * eb) % 16 != 0 || (kv.v_stride[i] * eb) % 16 != 0) return PA_ERR_ALIGN;
+  return PA_OK;
+}
+
+void fill_kv(AttnParams& p, const pa_paged_kv& kv) {
+  p.k = kv.k;
+  p.v = kv.v;
+  p.ks0 = kv.k_stride[0]; p.ks1 = kv.k_stride[1]; p.ks2 = kv.k_stride[2];
+  p.vs0 = kv.v_stride[0]; p.vs1 = kv.v_stride[1]; p.vs2 = kv.v_stride[2];
+  p.page_size = kv.page_size;
+  p.dqk = kv.head_dim_qk;
+  p.dvo = kv.head_dim_vo;
+  p.k_scale = kv.k_scale;
+  p.v_scale = kv.v_scale;
+  p.kv_indptr = kv.kv_indptr;
+  p.kv_indices = kv.kv_indices;
+  p.kv_last = kv.kv_last_page_len;
+  p.kv_dtype = kv.kv_dtype;
+  p.max_kv_len = kv.max_kv_len_hint;
+}
+
+int check_decode(const pa_decode_args* a) {
+  if (!a) return PA_ERR_NULL;
+  if (a->batch < 1 || a->q_len < 1) return PA_ERR_SHAPE;
+  if (a->num_kv_splits < 1 || a->num_kv_splits > 1024) return PA_ERR_SHAPE;
+  if (!std::isfinite(a->sm_scale)) return PA_ERR_SHAPE;
+  int st = check_common(a->q, a->q_dtype, a->num_qo_heads, a->kv, a->kv_broadcast, a->batch, a->o,
+                        a->o_dtype);
+  if (st != PA_OK) return st;
+  if (a->num_kv_splits > 1) {
+    if (!a->lse) return PA_ERR_NULL;
+    if (a->o_dtype != PA_F32) return PA_ERR_DTYPE;
+  }
+  if ((int64_t)a->batch * a->q_len > INT32_MAX / 2) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+int check_prefill(const pa_prefill_args* a) {
+  if (!a) return PA_ERR_NULL;
+  if (!a->qo_indptr) return PA_ERR_NULL;
+  if (a->batch < 1 || a->total_q < 0 || a->max_q_len_hint < 0) return PA_ERR_SHAPE;
+  if (!std::isfinite(a->sm_scale)) return PA_ERR_SHAPE;
+  return check_common(a->q, a->q_dtype, a->num_qo_heads, a->kv, a->kv_broadcast, a->batch, a->o,
+                      a->o_dtype);
+}
+
+AttnParams params_decode(const pa_decode_args* a) {
+  AttnParams p{};
+  p.q = a->q;
+  p.qo_indptr = nullptr;
+  p.batch = a->batch;
+  p.q_len = a->q_len;
+  p.total_q = a->batch * a->q_len;
+  p.max_q_len = a->q_len;
+  p.num_qo_heads = a->num_qo_heads;
+  fill_kv(p, a->kv);
+  p.num_kv_heads = a->kv.num_kv_heads;
+  p.group = a->num_qo_heads / a->kv.num_kv_heads;
+  p.sm_scale = a->sm_scale;
+  p.broadcast = a->kv_broadcast ? 1 : 0;
+  p.causal = a->causal ? 1 : 0;
+  p.num_splits = a->num_kv_splits;
+  p.partial_out = a->num_kv_splits > 1;
+  p.o = a->o;
+  p.lse = a->lse;
+  p.mx = a->row_max;
+  p.o_split_stride = (int64_t)p.total_q * p.num_qo_heads * p.dvo;
+  p.s_split_stride = (int64_t)p.total_q * p.num_qo_heads;
+  p.q_dtype = a->q_dtype;
+  p.o_dtype = a->o_dtype;
+  return p;
+}
+
+AttnParams params_prefill(const pa_prefill_args* a) {
+  AttnParams p{};
+  p.q = a->q;
+  p.qo_indptr = a->qo_indptr;
+  p.batch = a->batch;
+  p.q_len = 0;
+  p.total_q = a->total_q;
+  p.max_q_len = a->max_q_len_hint > 0 ? a->max_q_len_hint : a->total_q;
+  p.num_qo_heads = a->num_qo_heads;
+  fill_kv(p, a->kv);
+  p.num_kv_heads = a->kv.num_kv_heads;
+  p.group = a->num_qo_heads / a->kv.num_kv_heads;
+  p.sm_scale = a->sm_scale;
+  p.broadcast = a->kv_broadcast ? 1 : 0;
+  p.causal = a->causal ? 1 : 0;
+  p.num_splits = 1;
+  p.partial_out = 0;
+  p.o = a->o;
+  p.lse = a->lse;
+  p.mx = a->row_max;
+  p.o_split_stride = (int64_t)p.total_q * p.num_qo_heads * p.dvo;
+  p.s_split_stride = (int64_t)p.total_q * p.num_qo_heads;
+  p.q_dtype = a->q_dtype;
+  p.o_dtype = a->o_dtype;
+  return p;
+}
+
+// The plan of one call: which kernels run and how much workspace they need.
+struct Plan {
+  enum Kind { GENERIC } kind = GENERIC;
+  size_t workspace = 0;
+  const char* name = "generic";
+};
+
+Plan make_plan(const AttnParams& p, uint32_t flags) {
+  (void)p;
+  (void)flags;
+  Plan pl;
+  return pl;
+}
+
+int run_plan(const Plan& pl, const AttnParams& p, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (pl.workspace > 0 && (!ws || ws_bytes < pl.workspace)) return PA_ERR_WORKSPACE;
+  if (log_enabled())
+    std::fprintf(stderr, "[paged_attn] kernel=%s total_q=%d Hq=%d Hkv=%d dqk=%d dvo=%d splits=%d\n",
+                 pl.name, p.total_q, p.num_qo_heads, p.num_kv_heads, p.dqk, p.dvo, p.num_splits);
+  hipError_t e = hipSuccess;
+  switch (pl.kind) {
+    case Plan::GENERIC:
+      e = pa::launch_generic(p, stream);
+      break;
+  }
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case PA_ERR_DTYPE: return "dtype unknown or not allowed for this buffer";
+    case PA_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+    case PA_ERR_UNSUPPORTED: return "no kernel for this head-dim / dtype combination";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP runtime error while launching";
+    default: return "unknown status";
+  }
+}
+
+const char* paged_attn_decode_plan_name(const pa_decode_args* args) {
+  if (check_decode(args) != PA_OK) return nullptr;
+  return make_plan(params_decode(args), args->flags).name;
+}
+
+const char* paged_attn_prefill_plan_name(const pa_prefill_args* args) {
+  if (check_prefill(args) != PA_OK) return nullptr;
+  return make_plan(params_prefill(args), args->flags).name;
+}
+
+int paged_attn_decode_workspace_size(const pa_decode_args* args, size_t* bytes) {
+  if (!bytes) return PA_ERR_NULL;
+  const int st = check_decode(args);
+  if (st != PA_OK) return st;
+  *bytes = make_plan(params_decode(args), args->flags).workspace;
+  return PA_OK;
+}
+
+int paged_attn_prefill_workspace_size(const pa_prefill_args* args, size_t* bytes) {
+  if (!bytes) return PA_ERR_NULL;
+  const int st = check_prefill(args);
+  if (st != PA_OK) return st;
+  *bytes = make_plan(params_prefill(args), args->flags).workspace;
+  return PA_OK;
+}
+
+int paged_attn_decode(const pa_decode_args* args, void* workspace, size_t workspace_bytes,
+                      pa_stream_t stream) {
+  const int st = check_decode(args);
+  if (st != PA_OK) return st;
+  const AttnParams p = params_decode(args);
+  return run_plan(make_plan(p, args->flags), p, workspace, workspace_bytes,
+                  static_cast<hipStream_t>(stream));
+}
+
+int paged_attn_prefill(const pa_prefill_args* args, void* workspace, size_t workspace_bytes,
+                       pa_stream_t stream) {
+  const int st = check_prefill(args);
+  if (st != PA_OK) return st;
+  if (args->total_q == 0) return PA_OK;
+  const AttnParams p = params_prefill(args);
+  return run_plan(make_plan(p, args->flags), p, workspace, workspace_bytes,
+                  static_cast<hipStream_t>(stream));
+}
+
+int merge_states(const void* v_states, pa_dtype v_dtype, const float* s_states,
+                 int32_t num_states, int64_t rows, int32_t head_dim, void* v_out,
+                 pa_dtype out_dtype, float* s_out, pa_stream_t stream) {
+  if (!v_states || !s_states || !v_out) return PA_ERR_NULL;
+  if (!known_dtype(v_dtype) || !known_dtype(out_dtype)) return PA_ERR_DTYPE;
+  if (v_dtype == PA_FP8_E4M3 || out_dtype == PA_FP8_E4M3) return PA_ERR_DTYPE;
+  if (num_states < 1 || num_states > 1024 || rows < 0) return PA_ERR_SHAPE;
+  if (head_dim < 4 || head_dim > 1024 || head_dim % 4 != 0) return PA_ERR_SHAPE;
+  if (!aligned16(v_states) || !aligned16(v_out)) return PA_ERR_ALIGN;
+  if (rows == 0) return PA_OK;
+  const hipError_t e =
+      pa::launch_merge(v_states, v_dtype, s_states, num_states, rows, head_dim, rows * head_dim,
+                       rows, v_out, out_dtype, s_out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int paged_attn_check_tables(const int32_t* h_indptr, const int32_t* h_indices,
+                            const int32_t* h_last_page_len, int32_t num_kv_batches,
+                            int32_t num_pool_pages, int32_t page_size) {
+  if (!h_indptr || !h_last_page_len) return PA_ERR_NULL;
+  if (num_kv_batches < 1 || num_pool_pages < 0 || page_size < 1) return PA_ERR_SHAPE;
+  if (h_indptr[0] != 0) return PA_ERR_SHAPE;
+  for (int b = 0; b < num_kv_batches; ++b) {
+    const int n = h_indptr[b + 1] - h_indptr[b];
+    if (n < 0) return PA_ERR_SHAPE;
+    if (n > 0 && (h_last_page_len[b] < 1 || h_last_page_len[b] > page_size)) return PA_ERR_SHAPE;
+  }
+  const int total = h_indptr[num_kv_batches];
+  if (total > 0 && !h_indices) return PA_ERR_NULL;
+  for (int i = 0; i < total; ++i)
+    if (h_indices[i] < 0 || h_indices[i] >= num_pool_pages) return PA_ERR_SHAPE;
+  return PA_OK;
+}
+
+}  // extern "C"

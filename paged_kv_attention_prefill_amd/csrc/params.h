@@ -1,0 +1,45 @@
+// Internal kernel parameters of libpaged_attn (host and device).  Not part of
+// the C ABI: the entry points in api.cpp translate pa_*_args into this.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum Dt : int { F32 = 0, F16 = 1, BF16 = 2, FP8 = 3 };
+
+// One attention launch over "query tokens" t in [0, total_q) and query heads.
+// Decode calls arrive with qo_indptr == nullptr and a uniform q_len.
+struct AttnParams {
+  const void* q;
+  const int32_t* qo_indptr;  // device, [batch+1]; nullptr => uniform q_len
+  int32_t batch, q_len, total_q, num_qo_heads, num_kv_heads, group;
+  const void* k;
+  const void* v;
+  int64_t ks0, ks1, ks2, vs0, vs1, vs2;
+  int32_t page_size, dqk, dvo;
+  float k_scale, v_scale, sm_scale;
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const int32_t* kv_last;
+  int32_t broadcast, causal;
+  int32_t num_splits;       // states written per row (1: final result)
+  int32_t partial_out;      // 1: write unnormalised-merge-ready partial states (fp32 O, LSE)
+  void* o;                  // [S][total_q][Hq][dvo]
+  float* lse;               // [S][total_q][Hq] or nullptr
+  float* mx;                // [S][total_q][Hq] or nullptr
+  int64_t o_split_stride;   // elements between states
+  int64_t s_split_stride;   // elements between states of lse/mx
+  int32_t q_dtype, kv_dtype, o_dtype;
+  int32_t max_kv_len;       // host hint (0 unknown)
+  int32_t max_q_len;        // host hint: >= every q_b
+};
+
+// Launchers (one per kernel family).  Return hipSuccess or the launch error.
+hipError_t launch_generic(const AttnParams& p, hipStream_t stream);
+hipError_t launch_merge(const void* v, int v_dtype, const float* s, int num_states, int64_t rows,
+                        int head_dim, int64_t v_state_stride, int64_t s_state_stride, void* out,
+                        int out_dtype, float* s_out, hipStream_t stream);
+
+}  // namespace pa

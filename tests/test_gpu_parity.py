@@ -1,0 +1,180 @@
+"""GPU parity: the HIP path through the C ABI vs the CPU oracle, element by
+element on the same seeded bytes, at sizes the oracle finishes in seconds that
+still span several tiles and ragged tails; plus the invariants and edge cases.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as OR
+from paged_kv_attention_prefill_amd import binding as B
+from paged_kv_attention_prefill_amd import runner as R
+from paged_kv_attention_prefill_amd import workloads as W
+from gpu_check import check_rows, to64, tolerances
+
+pytestmark = pytest.mark.gpu
+
+
+def small(name):
+    return {
+        "c1": lambda: W.config1(),
+        "c2": lambda: W.config2(batch=6, min_len=1, max_len=1200),
+        "c2_hnd": lambda: W.config2(batch=4, min_len=1, max_len=700, k_layout="HND",
+                                    v_layout="HND"),
+        "c2_mixed": lambda: W.config2(batch=4, min_len=1, max_len=700, k_layout="NHD",
+                                      v_layout="HND"),
+        "c3": lambda: W.config3(batch=3, min_q=1, max_q=300, max_prefix=400),
+        "c3_fresh": lambda: W.config3(batch=2, min_q=100, max_q=260, max_prefix=0),
+        "c5": lambda: W.config5(num_queries=8, kv_len=5000, num_kv_splits=16),
+        "c5_long": lambda: W.config5(num_queries=3, kv_len=131072, num_kv_splits=16),
+    }[name]()
+
+
+def c4_small(h, ql, dt):
+    return W.config4(num_heads=h, q_len=ql, kv_dtype=dt, batch=3, min_len=1, max_len=900)
+
+
+def run_and_check(w, label, flags=0, **kw):
+    d = R.upload(w)
+    res = R.run(d, flags=flags, **kw)
+    torch.cuda.synchronize()
+    o, lse, mx = OR.attention(w, num_kv_splits=1)
+    return check_rows(w, to64(res["o"]), to64(res["lse"]), o, lse,
+                      None if res.get("mx") is None else to64(res["mx"]), mx, label=label), res
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c2_hnd", "c2_mixed", "c3", "c3_fresh", "c5",
+                                  "c5_long"])
+def test_parity_small(name):
+    print(f"case {name}", flush=True)
+    run_and_check(small(name), name)
+
+
+@pytest.mark.parametrize("h", W.C4_HEADS)
+@pytest.mark.parametrize("ql", W.C4_QLENS)
+@pytest.mark.parametrize("dt", [W.DT_BF16, W.DT_FP8])
+def test_parity_mla_small(h, ql, dt):
+    label = f"c4 h{h} q{ql} {W.DT_NAMES[dt]}"
+    print(label, flush=True)
+    run_and_check(c4_small(h, ql, dt), label)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5"])
+def test_parity_generic_kernel(name):
+    print(f"generic {name}", flush=True)
+    run_and_check(small(name), name + " generic", flags=B.FLAG_FORCE_GENERIC)
+
+
+def test_split_partials_and_merge():
+    w = small("c2")
+    d = R.upload(w)
+    S = 5
+    res = R.run(d, num_kv_splits=S)
+    torch.cuda.synchronize()
+    po, pl, pm = OR.attention(w, num_kv_splits=S)
+    for c in range(S):
+        check_rows(w, to64(res["po"][c]), to64(res["plse"][c]), po[c], pl[c],
+                   to64(res["pmx"][c]), pm[c], label=f"partial {c}")
+    o, lse, _ = OR.attention(w, num_kv_splits=1)
+    check_rows(w, to64(res["o"]), to64(res["lse"]), o, lse, label="merged")
+
+
+def test_merge_states_against_oracle_merge():
+    rng = np.random.default_rng(5)
+    S, rows, D = 7, 300, 128
+    v = rng.standard_normal((S, rows, D)).astype(np.float32)
+    s = (rng.standard_normal((S, rows)) * 4).astype(np.float32)
+    s[:, 0] = -np.inf          # a row with no state
+    s[2:5, 1] = -np.inf        # some empty states
+    vo_ref, so_ref = OR.merge_states(v.astype(np.float64), s.astype(np.float64))
+    for odt in (torch.float32, torch.bfloat16):
+        vo, so = B.merge_states(torch.from_numpy(v).cuda(), torch.from_numpy(s).cuda(),
+                                out_dtype=odt)
+        torch.cuda.synchronize()
+        tol = 1e-5 if odt == torch.float32 else 2e-2
+        assert np.abs(to64(vo) - vo_ref).max() <= tol
+        so64 = to64(so)
+        assert np.isneginf(so64[0]) and (to64(vo)[0] == 0).all()
+        assert np.abs(so64[1:] - so_ref[1:]).max() <= 1e-5
+
+
+def test_page_permutation_bitwise():
+    from test_oracle import _permute_pages
+    w = small("c2")
+    a = R.run(R.upload(w))
+    b = R.run(R.upload(_permute_pages(w, 3)))
+    torch.cuda.synchronize()
+    assert torch.equal(a["o"], b["o"]) and torch.equal(a["lse"], b["lse"])
+
+
+def test_same_kv_strides_variant_equals_general_bitwise():
+    w = small("c2")
+    d = R.upload(w)
+    a = R.run(d)
+    b = R.run(d, flags=B.FLAG_FORCE_GENERAL_STRIDES)
+    torch.cuda.synchronize()
+    assert torch.equal(a["o"], b["o"]) and torch.equal(a["lse"], b["lse"])
+
+
+def test_repeat_runs_bitwise_identical():
+    w = small("c3")
+    d = R.upload(w)
+    a = R.run(d)
+    for _ in range(3):
+        b = R.run(d)
+        torch.cuda.synchronize()
+        assert torch.equal(a["o"], b["o"]) and torch.equal(a["lse"], b["lse"])
+
+
+def test_broadcast_equals_replicated():
+    w = small("c5")
+    a = R.run(R.upload(w))
+    r = W.replicate_broadcast(w)
+    b = R.run(R.upload(r))
+    torch.cuda.synchronize()
+    tol_o, tol_l = tolerances(w)
+    assert (to64(a["o"]) - to64(b["o"])).__abs__().max() <= tol_o
+    assert (to64(a["lse"]) - to64(b["lse"])).__abs__().max() <= tol_l
+
+
+def test_prefill_entry_on_decode_shapes():
+    # the prefill entry point with uniform q lengths computes what decode computes
+    w = c4_small(16, 4, W.DT_BF16)
+    d = R.upload(w)
+    res = R.run(d, force_prefill=True)
+    torch.cuda.synchronize()
+    o, lse, _ = OR.attention(w)
+    check_rows(w, to64(res["o"]), to64(res["lse"]), o, lse, label="prefill entry, MLA shapes")
+
+
+def test_edge_lengths_and_empty_batches():
+    rng = np.random.default_rng(77)
+    # empty KV batch, one token, a partial page, exactly one page, a page + 1
+    kv_lens = [0, 1, 7, 16, 17, 33, 0, 250]
+    w = W.build(rng, 77, "edges", q_lens=[1] * len(kv_lens), kv_lens=kv_lens, num_qo_heads=64,
+                num_kv_heads=8, head_dim_qk=128, head_dim_vo=128, page_size=16,
+                q_dtype=W.DT_BF16, kv_dtype=W.DT_BF16, pool_pages=40)
+    run_and_check(w, "edge lengths")
+    for S in (3, 40):  # more splits than pages: empty partial states
+        run_and_check(dataclasses.replace(w, num_kv_splits=S), f"edge lengths S={S}")
+
+
+def test_causal_rows_that_see_nothing():
+    # q_len 4 against KV lengths 1..3: the first queries see no token
+    w = W.config4(num_heads=16, q_len=4, batch=6, min_len=1, max_len=3)
+    run_and_check(w, "MLA empty causal rows")
+    w2 = W.config4(num_heads=128, q_len=2, kv_dtype=W.DT_FP8, batch=4, min_len=1, max_len=2)
+    run_and_check(w2, "MLA fp8 empty causal rows")
+
+
+def test_output_dtypes():
+    w = small("c2")
+    d = R.upload(w)
+    o, lse, _ = OR.attention(w)
+    for odt in (torch.float32, torch.float16, torch.bfloat16):
+        res = R.run(d, out_dtype=odt)
+        torch.cuda.synchronize()
+        assert res["o"].dtype == odt
+        check_rows(w, to64(res["o"]), to64(res["lse"]), o, lse, label=f"out {odt}")

@@ -132,6 +132,9 @@ typedef struct {
   float* lse;               /* [S][batch, q_len, num_qo_heads]; may be NULL only if S == 1 */
   float* row_max;           /* same shape as lse; NULL to skip */
   uint32_t flags;           /* PA_FLAG_* */
+  void* timing_events[2];   /* optional hipEvent_t pair recorded on `stream` right before and
+                               right after the attention kernel (not around a merge launch);
+                               NULL to skip */
 } pa_decode_args;
 
 /* Prefill: ragged query batches; the new tokens' K/V are already in the cache
@@ -153,6 +156,7 @@ typedef struct {
   float* lse;               /* [total_q, num_qo_heads]; NULL to skip */
   float* row_max;           /* NULL to skip */
   uint32_t flags;
+  void* timing_events[2];   /* as in pa_decode_args */
 } pa_prefill_args;
 
 int pa_abi_version(void);

@@ -46,7 +46,7 @@ class DecodeArgs(ctypes.Structure):
                 ("num_qo_heads", c_i32), ("kv", PagedKV), ("kv_broadcast", c_i32),
                 ("causal", c_i32), ("sm_scale", c_f32), ("num_kv_splits", c_i32), ("o", c_vp),
                 ("o_dtype", ctypes.c_int), ("lse", c_vp), ("row_max", c_vp),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("timing_events", c_vp * 2)]
 
 
 class PrefillArgs(ctypes.Structure):
@@ -54,7 +54,7 @@ class PrefillArgs(ctypes.Structure):
                 ("total_q", c_i32), ("max_q_len_hint", c_i32), ("num_qo_heads", c_i32),
                 ("kv", PagedKV), ("kv_broadcast", c_i32), ("causal", c_i32),
                 ("sm_scale", c_f32), ("o", c_vp), ("o_dtype", ctypes.c_int), ("lse", c_vp),
-                ("row_max", c_vp), ("flags", ctypes.c_uint32)]
+                ("row_max", c_vp), ("flags", ctypes.c_uint32), ("timing_events", c_vp * 2)]
 
 
 class PagedAttnError(RuntimeError):

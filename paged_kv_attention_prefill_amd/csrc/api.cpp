@@ -169,29 +169,89 @@ AttnParams params_prefill(const pa_prefill_args* a) {
 
 // The plan of one call: which kernels run and how much workspace they need.
 struct Plan {
-  enum Kind { GENERIC } kind = GENERIC;
+  enum Kind { GENERIC, GQA_DECODE } kind = GENERIC;
+  bool same_strides = false;  // V offsets reuse K offsets (equal K/V strides)
+  int chunk_tokens = 0;       // internal KV chunking (0: none)
+  int max_chunks = 0;
   size_t workspace = 0;
   const char* name = "generic";
 };
 
+bool equal_kv_strides(const AttnParams& p) {
+  return p.ks0 == p.vs0 && p.ks1 == p.vs1 && p.ks2 == p.vs2;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Internal chunk size for the folded-GQA decode: fixed-size chunks bound the
+// longest work item, so the dispatcher can balance ragged KV lengths over the
+// 256 CUs.  Decided from host values only (identical for the size query and
+// the launch), never from device state.
+int decode_chunk_tokens(const AttnParams& p, uint32_t flags) {
+  if ((flags & PA_FLAG_NO_INTERNAL_SPLIT) || p.num_splits != 1 || p.max_kv_len <= 0) return 0;
+  const int64_t items = (int64_t)p.batch * p.num_kv_heads;
+  int c = 2048;
+  // few (batch, head) items: smaller chunks so that there are enough workgroups
+  while (c > 256 && items * ((p.max_kv_len + c - 1) / c) < 1536) c /= 2;
+  // chunk starts must be page aligned (tiles never straddle a page-id window)
+  c = (c + p.page_size - 1) / p.page_size * p.page_size;
+  if (p.max_kv_len <= c) return 0;
+  return c;
+}
+
 Plan make_plan(const AttnParams& p, uint32_t flags) {
-  (void)p;
-  (void)flags;
   Plan pl;
+  const bool same = equal_kv_strides(p) && !(flags & PA_FLAG_FORCE_GENERAL_STRIDES);
+  if (flags & PA_FLAG_FORCE_GENERIC) return pl;
+  if (pa::gqa_decode_supported(p)) {
+    pl.kind = Plan::GQA_DECODE;
+    pl.same_strides = same;
+    pl.name = same ? "gqa_decode_mfma_same_strides" : "gqa_decode_mfma";
+    pl.chunk_tokens = decode_chunk_tokens(p, flags);
+    if (pl.chunk_tokens > 0) {
+      pl.max_chunks = (p.max_kv_len + pl.chunk_tokens - 1) / pl.chunk_tokens;
+      const size_t rows = (size_t)p.batch * p.num_kv_heads * pl.max_chunks * 16;
+      pl.workspace = align256(rows * p.dvo * 4) + 2 * align256(rows * 4);
+    }
+    return pl;
+  }
   return pl;
 }
 
-int run_plan(const Plan& pl, const AttnParams& p, void* ws, size_t ws_bytes, hipStream_t stream) {
+int run_plan(const Plan& pl, AttnParams p, void* ws, size_t ws_bytes, void* const* events,
+             hipStream_t stream) {
   if (pl.workspace > 0 && (!ws || ws_bytes < pl.workspace)) return PA_ERR_WORKSPACE;
   if (log_enabled())
-    std::fprintf(stderr, "[paged_attn] kernel=%s total_q=%d Hq=%d Hkv=%d dqk=%d dvo=%d splits=%d\n",
-                 pl.name, p.total_q, p.num_qo_heads, p.num_kv_heads, p.dqk, p.dvo, p.num_splits);
+    std::fprintf(stderr,
+                 "[paged_attn] kernel=%s total_q=%d Hq=%d Hkv=%d dqk=%d dvo=%d splits=%d "
+                 "chunk=%d x%d ws=%zu\n",
+                 pl.name, p.total_q, p.num_qo_heads, p.num_kv_heads, p.dqk, p.dvo, p.num_splits,
+                 pl.chunk_tokens, pl.max_chunks, pl.workspace);
+  p.chunk_tokens = pl.chunk_tokens;
+  p.max_chunks = pl.max_chunks;
+  if (pl.chunk_tokens > 0) {
+    const size_t rows = (size_t)p.batch * p.num_kv_heads * pl.max_chunks * 16;
+    char* w = static_cast<char*>(ws);
+    p.ws_o = reinterpret_cast<float*>(w);
+    p.ws_lse = reinterpret_cast<float*>(w + align256(rows * p.dvo * 4));
+    p.ws_mx = reinterpret_cast<float*>(w + align256(rows * p.dvo * 4) + align256(rows * 4));
+  }
+  const bool timed = events && events[0] && events[1];
+  if (timed && hipEventRecord(static_cast<hipEvent_t>(events[0]), stream) != hipSuccess)
+    return PA_ERR_HIP;
   hipError_t e = hipSuccess;
   switch (pl.kind) {
     case Plan::GENERIC:
       e = pa::launch_generic(p, stream);
       break;
+    case Plan::GQA_DECODE:
+      e = pa::launch_gqa_decode(p, pl.same_strides, stream);
+      break;
   }
+  if (e != hipSuccess) return PA_ERR_HIP;
+  if (timed && hipEventRecord(static_cast<hipEvent_t>(events[1]), stream) != hipSuccess)
+    return PA_ERR_HIP;
+  if (pl.chunk_tokens > 0) e = pa::launch_chunk_merge(p, stream);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -246,7 +306,7 @@ int paged_attn_decode(const pa_decode_args* args, void* workspace, size_t worksp
   const int st = check_decode(args);
   if (st != PA_OK) return st;
   const AttnParams p = params_decode(args);
-  return run_plan(make_plan(p, args->flags), p, workspace, workspace_bytes,
+  return run_plan(make_plan(p, args->flags), p, workspace, workspace_bytes, args->timing_events,
                   static_cast<hipStream_t>(stream));
 }
 
@@ -256,7 +316,7 @@ int paged_attn_prefill(const pa_prefill_args* args, void* workspace, size_t work
   if (st != PA_OK) return st;
   if (args->total_q == 0) return PA_OK;
   const AttnParams p = params_prefill(args);
-  return run_plan(make_plan(p, args->flags), p, workspace, workspace_bytes,
+  return run_plan(make_plan(p, args->flags), p, workspace, workspace_bytes, args->timing_events,
                   static_cast<hipStream_t>(stream));
 }
 

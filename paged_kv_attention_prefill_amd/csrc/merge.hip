@@ -92,7 +92,93 @@ hipError_t launch_vt(const void* v, const float* s, int S, int64_t rows, int D, 
   return hipGetLastError();
 }
 
+// Merge of internal KV chunks (the same LSE formula): one group of D/4 lanes per
+// folded row (b, KV head g, row r < q_len*G); rows whose KV batch has a single
+// chunk were written directly by the attention kernel and are skipped here.
+__global__ __launch_bounds__(256) void chunk_merge_kernel(AttnParams p, int tpr) {
+  const int rpb = blockDim.x / tpr;
+  const int64_t rho = (int64_t)blockIdx.x * rpb + threadIdx.x / tpr;
+  const int li = threadIdx.x % tpr;
+  const int R = p.q_len * p.group;
+  const int64_t total = (int64_t)p.batch * p.num_kv_heads * 16;
+  if (threadIdx.x >= rpb * tpr || rho >= total) return;
+  const int r = (int)(rho % 16);
+  const int g = (int)((rho / 16) % p.num_kv_heads);
+  const int b = (int)(rho / (16 * p.num_kv_heads));
+  if (r >= R) return;
+  const int kb = p.broadcast ? 0 : b;
+  const int n = p.kv_indptr[kb + 1] - p.kv_indptr[kb];
+  const int L = n ? (n - 1) * p.page_size + p.kv_last[kb] : 0;
+  const int nch = num_chunks(L, p.chunk_tokens, p.max_chunks);
+  if (nch <= 1) return;
+  const int D = p.dvo;
+  const int64_t wrow0 = (int64_t)(b * p.num_kv_heads + g) * p.max_chunks * 16 + r;
+  const int d0 = li * 4;
+  // loads are issued in unrolled blocks of 8 chunks so their latencies overlap
+  constexpr int BLK = 8;
+  float M = -INFINITY, MX = -INFINITY;
+  for (int c0 = 0; c0 < nch; c0 += BLK) {
+    float ls[BLK], ms[BLK];
+#pragma unroll
+    for (int k = 0; k < BLK; ++k) {
+      const bool ok = c0 + k < nch;
+      ls[k] = ok ? p.ws_lse[wrow0 + (c0 + k) * 16] : -INFINITY;
+      ms[k] = ok ? p.ws_mx[wrow0 + (c0 + k) * 16] : -INFINITY;
+    }
+#pragma unroll
+    for (int k = 0; k < BLK; ++k) {
+      M = fmaxf(M, ls[k]);
+      MX = fmaxf(MX, ms[k]);
+    }
+  }
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (M != -INFINITY) {
+    for (int c0 = 0; c0 < nch; c0 += BLK) {
+      float ls[BLK];
+      float4 x[BLK];
+#pragma unroll
+      for (int k = 0; k < BLK; ++k) {
+        const bool ok = c0 + k < nch;
+        ls[k] = ok ? p.ws_lse[wrow0 + (c0 + k) * 16] : -INFINITY;
+        x[k] = ok ? *reinterpret_cast<const float4*>(p.ws_o + (wrow0 + (c0 + k) * 16) * D + d0)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int k = 0; k < BLK; ++k) {
+        const float w = ls[k] == -INFINITY ? 0.f : fast_exp2((ls[k] - M) * kLog2e);
+        wsum += w;
+        acc[0] = fmaf(w, x[k].x, acc[0]);
+        acc[1] = fmaf(w, x[k].y, acc[1]);
+        acc[2] = fmaf(w, x[k].z, acc[2]);
+        acc[3] = fmaf(w, x[k].w, acc[3]);
+      }
+    }
+    const float inv = 1.f / wsum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] *= inv;
+  }
+  const int qi = r / p.group, qh = r % p.group;
+  const int64_t rid = (int64_t)(b * p.q_len + qi) * p.num_qo_heads + (int64_t)g * p.group + qh;
+  if (p.o_dtype == F32) store4<F32>(p.o, rid * D + d0, acc);
+  else if (p.o_dtype == F16) store4<F16>(p.o, rid * D + d0, acc);
+  else store4<BF16>(p.o, rid * D + d0, acc);
+  if (li == 0) {
+    if (p.lse) p.lse[rid] = M == -INFINITY ? -INFINITY : M + fast_log2(wsum) * kLn2;
+    if (p.mx) p.mx[rid] = MX;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_chunk_merge(const AttnParams& p, hipStream_t stream) {
+  const int tpr = p.dvo / 4;
+  const int rpb = 256 / tpr;
+  const int64_t total = (int64_t)p.batch * p.num_kv_heads * 16;
+  const dim3 grid((unsigned)((total + rpb - 1) / rpb));
+  chunk_merge_kernel<<<grid, dim3(rpb * tpr), 0, stream>>>(p, tpr);
+  return hipGetLastError();
+}
 
 hipError_t launch_merge(const void* v, int v_dtype, const float* s, int num_states, int64_t rows,
                         int head_dim, int64_t v_state_stride, int64_t s_state_stride, void* out,

@@ -34,10 +34,27 @@ struct AttnParams {
   int32_t q_dtype, kv_dtype, o_dtype;
   int32_t max_kv_len;       // host hint (0 unknown)
   int32_t max_q_len;        // host hint: >= every q_b
+  // internal KV chunking (load balance): chunk_tokens > 0 cuts every KV batch into
+  // chunks of that many tokens (the last of max_chunks takes the rest); rows with
+  // more than one chunk leave partial states in the workspace for a merge launch
+  int32_t chunk_tokens;
+  int32_t max_chunks;
+  float* ws_o;              // [B][Hkv][max_chunks][16][dvo]
+  float* ws_lse;            // [B][Hkv][max_chunks][16]
+  float* ws_mx;             // [B][Hkv][max_chunks][16]
 };
+
+// Number of chunks of a KV batch of L tokens under internal chunking.
+__host__ __device__ inline int num_chunks(int L, int chunk_tokens, int max_chunks) {
+  const int n = L > 0 ? (L + chunk_tokens - 1) / chunk_tokens : 1;
+  return n < max_chunks ? n : max_chunks;
+}
 
 // Launchers (one per kernel family).  Return hipSuccess or the launch error.
 hipError_t launch_generic(const AttnParams& p, hipStream_t stream);
+bool gqa_decode_supported(const AttnParams& p);
+hipError_t launch_gqa_decode(const AttnParams& p, bool same_strides, hipStream_t stream);
+hipError_t launch_chunk_merge(const AttnParams& p, hipStream_t stream);
 hipError_t launch_merge(const void* v, int v_dtype, const float* s, int num_states, int64_t rows,
                         int head_dim, int64_t v_state_stride, int64_t s_state_stride, void* out,
                         int out_dtype, float* s_out, hipStream_t stream);

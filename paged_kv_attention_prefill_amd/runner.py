@@ -6,6 +6,7 @@ through ``binding``.
 """
 from __future__ import annotations
 
+import ctypes
 from dataclasses import dataclass
 from typing import Optional
 
@@ -145,20 +146,50 @@ class Step:
             self.merge()
 
     def time_attention_kernel(self, steps: int) -> float:
-        """Average ms of the attention launch alone, timed with HIP events on the
-        stream it runs on, over ``steps`` steps (each step runs in full)."""
+        """Average ms of the attention kernel alone over ``steps`` full steps: the
+        library records a HIP event pair around that launch on its stream (any
+        merge launch of the step falls outside the pair)."""
         import torch
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
+        hip = _hip()
+        pairs = []
+        for _ in range(steps):
+            e0, e1 = ctypes.c_void_p(), ctypes.c_void_p()
+            if hip.hipEventCreate(ctypes.byref(e0)) or hip.hipEventCreate(ctypes.byref(e1)):
+                raise RuntimeError("hipEventCreate failed")
+            pairs.append((e0, e1))
         torch.cuda.synchronize()
-        for e0, e1 in evs:
-            e0.record(self.stream)
-            self.attn()
-            e1.record(self.stream)
-            if self.merge is not None:
-                self.merge()
+        for e0, e1 in pairs:
+            self.attn.args.timing_events[0] = e0.value
+            self.attn.args.timing_events[1] = e1.value
+            self()
+        self.attn.args.timing_events[0] = None
+        self.attn.args.timing_events[1] = None
         torch.cuda.synchronize()
-        return sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
+        total = 0.0
+        for e0, e1 in pairs:
+            ms = ctypes.c_float()
+            if hip.hipEventElapsedTime(ctypes.byref(ms), e0, e1):
+                raise RuntimeError("hipEventElapsedTime failed")
+            total += ms.value
+            hip.hipEventDestroy(e0)
+            hip.hipEventDestroy(e1)
+        return total / steps
+
+
+_HIP = None
+
+
+def _hip():
+    """The HIP runtime, for event handles only."""
+    global _HIP
+    if _HIP is None:
+        lib = ctypes.CDLL("libamdhip64.so")
+        lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                            ctypes.c_void_p]
+        lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        _HIP = lib
+    return _HIP
 
 
 def prepare(d: DeviceWorkload, flags: int = 0, stream=None) -> Step:

@@ -1,0 +1,51 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the bench
+times: sampled rows (random rows, the first and last query of every batch and
+every head of the last query) are compared with the oracle row by row."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as OR
+from paged_kv_attention_prefill_amd import runner as R
+from paged_kv_attention_prefill_amd import workloads as W
+from gpu_check import check_rows, sample_rows, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def run_sampled(w, label, n=160, seed=0):
+    print(f"full-size case {label}: {w.manifest()}", flush=True)
+    d = R.upload(w)
+    step = R.prepare(d)
+    step()
+    torch.cuda.synchronize()
+    o = step.final_o if step.merge is not None else step.attn.outputs["o"]
+    lse = step.final_lse if step.merge is not None else step.attn.outputs["lse"]
+    rows = sample_rows(w, n, seed)
+    ro, rl, _ = OR.attention(w, rows=rows, num_kv_splits=1)
+    go = to64(o).reshape(-1, w.head_dim_vo)[rows]
+    gl = to64(lse).reshape(-1)[rows]
+    check_rows(w, go, gl, ro, rl, label=label)
+    # no row of the full output may be non-finite
+    assert torch.isfinite(o.float()).all()
+    del d, step
+    torch.cuda.empty_cache()
+
+
+def test_c2_llama_gqa_decode_full():
+    run_sampled(W.config2(), "c2 full")
+
+
+def test_c3_causal_prefill_full():
+    run_sampled(W.config3(), "c3 full")
+
+
+def test_c5_broadcast_split_decode_full():
+    run_sampled(W.config5(), "c5 full", n=96)
+
+
+@pytest.mark.parametrize("h,ql,dt", [(16, 1, W.DT_BF16), (128, 4, W.DT_FP8), (128, 1, W.DT_BF16),
+                                     (16, 4, W.DT_FP8)])
+def test_c4_mla_decode_full(h, ql, dt):
+    run_sampled(W.config4(num_heads=h, q_len=ql, kv_dtype=dt), f"c4 full h{h} q{ql} {W.DT_NAMES[dt]}",
+                n=96)

@@ -25,6 +25,23 @@ def small(name):
                                     v_layout="HND"),
         "c2_mixed": lambda: W.config2(batch=4, min_len=1, max_len=700, k_layout="NHD",
                                       v_layout="HND"),
+        "c2_kv2": lambda: W.config2(batch=5, min_len=1, max_len=900, num_qo_heads=16,
+                                    num_kv_heads=2),
+        "c2_g16": lambda: W.config2(batch=5, min_len=1, max_len=900, num_qo_heads=64,
+                                    num_kv_heads=4),
+        "c2_q2_causal": lambda: W.build(np.random.default_rng(21), 21, "gqa_q2", q_lens=[2] * 5,
+                                        kv_lens=[1, 2, 40, 333, 1000], num_qo_heads=32,
+                                        num_kv_heads=4, head_dim_qk=128, head_dim_vo=128,
+                                        page_size=16, q_dtype=W.DT_BF16, kv_dtype=W.DT_BF16,
+                                        causal=True),
+        "c2_d64_f16": lambda: W.build(np.random.default_rng(22), 22, "gqa_d64", q_lens=[1] * 6,
+                                      kv_lens=[3, 64, 65, 700, 1500, 2049], num_qo_heads=32,
+                                      num_kv_heads=8, head_dim_qk=64, head_dim_vo=64,
+                                      page_size=32, q_dtype=W.DT_F16, kv_dtype=W.DT_F16),
+        "c2_d256": lambda: W.build(np.random.default_rng(23), 23, "gqa_d256", q_lens=[1] * 4,
+                                   kv_lens=[5, 100, 1025, 1800], num_qo_heads=16,
+                                   num_kv_heads=4, head_dim_qk=256, head_dim_vo=256,
+                                   page_size=16, q_dtype=W.DT_BF16, kv_dtype=W.DT_BF16),
         "c3": lambda: W.config3(batch=3, min_q=1, max_q=300, max_prefix=400),
         "c3_fresh": lambda: W.config3(batch=2, min_q=100, max_q=260, max_prefix=0),
         "c5": lambda: W.config5(num_queries=8, kv_len=5000, num_kv_splits=16),
@@ -45,8 +62,9 @@ def run_and_check(w, label, flags=0, **kw):
                       None if res.get("mx") is None else to64(res["mx"]), mx, label=label), res
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c2_hnd", "c2_mixed", "c3", "c3_fresh", "c5",
-                                  "c5_long"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c2_hnd", "c2_mixed", "c2_kv2", "c2_g16",
+                                  "c2_q2_causal", "c2_d64_f16", "c2_d256", "c3", "c3_fresh",
+                                  "c5", "c5_long"])
 def test_parity_small(name):
     print(f"case {name}", flush=True)
     run_and_check(small(name), name)
@@ -178,3 +196,14 @@ def test_output_dtypes():
         torch.cuda.synchronize()
         assert res["o"].dtype == odt
         check_rows(w, to64(res["o"]), to64(res["lse"]), o, lse, label=f"out {odt}")
+
+
+def test_decode_takes_mfma_path_with_and_without_internal_chunks():
+    w = small("c2")
+    step = R.prepare(R.upload(w))
+    assert step.attention_kernel_name.startswith("gqa_decode_mfma"), step.attention_kernel_name
+    for flags in (0, B.FLAG_NO_INTERNAL_SPLIT, B.FLAG_FORCE_GENERAL_STRIDES,
+                  B.FLAG_NO_INTERNAL_SPLIT | B.FLAG_FORCE_GENERAL_STRIDES):
+        run_and_check(w, f"c2 flags={flags}", flags=flags)
+    # a length hint below the real maximum only changes the chunking, not the result
+    run_and_check(w, "c2 short hint", max_kv_len=300)

@@ -169,7 +169,7 @@ AttnParams params_prefill(const pa_prefill_args* a) {
 
 // The plan of one call: which kernels run and how much workspace they need.
 struct Plan {
-  enum Kind { GENERIC, GQA_DECODE } kind = GENERIC;
+  enum Kind { GENERIC, GQA_DECODE, FLASH } kind = GENERIC;
   bool same_strides = false;  // V offsets reuse K offsets (equal K/V strides)
   int chunk_tokens = 0;       // internal KV chunking (0: none)
   int max_chunks = 0;
@@ -203,7 +203,10 @@ Plan make_plan(const AttnParams& p, uint32_t flags) {
   Plan pl;
   const bool same = equal_kv_strides(p) && !(flags & PA_FLAG_FORCE_GENERAL_STRIDES);
   if (flags & PA_FLAG_FORCE_GENERIC) return pl;
-  if (pa::gqa_decode_supported(p)) {
+  // rows that read one KV head's data: q_len x G per query batch, or, under
+  // broadcast, those of every query batch together
+  const int64_t rows_per_kv = (int64_t)(p.broadcast ? p.total_q : p.max_q_len) * p.group;
+  if (pa::gqa_decode_supported(p) && (!p.broadcast || rows_per_kv <= 16)) {
     pl.kind = Plan::GQA_DECODE;
     pl.same_strides = same;
     pl.name = same ? "gqa_decode_mfma_same_strides" : "gqa_decode_mfma";
@@ -213,6 +216,12 @@ Plan make_plan(const AttnParams& p, uint32_t flags) {
       const size_t rows = (size_t)p.batch * p.num_kv_heads * pl.max_chunks * 16;
       pl.workspace = align256(rows * p.dvo * 4) + 2 * align256(rows * 4);
     }
+    return pl;
+  }
+  if (pa::flash_attn_supported(p)) {
+    pl.kind = Plan::FLASH;
+    pl.same_strides = same;
+    pl.name = same ? "flash_attn_mfma_same_strides" : "flash_attn_mfma";
     return pl;
   }
   return pl;
@@ -246,6 +255,9 @@ int run_plan(const Plan& pl, AttnParams p, void* ws, size_t ws_bytes, void* cons
       break;
     case Plan::GQA_DECODE:
       e = pa::launch_gqa_decode(p, pl.same_strides, stream);
+      break;
+    case Plan::FLASH:
+      e = pa::launch_flash_attn(p, pl.same_strides, stream);
       break;
   }
   if (e != hipSuccess) return PA_ERR_HIP;

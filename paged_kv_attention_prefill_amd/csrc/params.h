@@ -54,6 +54,8 @@ __host__ __device__ inline int num_chunks(int L, int chunk_tokens, int max_chunk
 hipError_t launch_generic(const AttnParams& p, hipStream_t stream);
 bool gqa_decode_supported(const AttnParams& p);
 hipError_t launch_gqa_decode(const AttnParams& p, bool same_strides, hipStream_t stream);
+bool flash_attn_supported(const AttnParams& p);
+hipError_t launch_flash_attn(const AttnParams& p, bool same_strides, hipStream_t stream);
 hipError_t launch_chunk_merge(const AttnParams& p, hipStream_t stream);
 hipError_t launch_merge(const void* v, int v_dtype, const float* s, int num_states, int64_t rows,
                         int head_dim, int64_t v_state_stride, int64_t s_state_stride, void* out,

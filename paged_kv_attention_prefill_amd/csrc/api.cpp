@@ -77,6 +77,9 @@ void fill_kv(AttnParams& p, const pa_paged_kv& kv) {
   p.ks0 = kv.k_stride[0]; p.ks1 = kv.k_stride[1]; p.ks2 = kv.k_stride[2];
   p.vs0 = kv.v_stride[0]; p.vs1 = kv.v_stride[1]; p.vs2 = kv.v_stride[2];
   p.page_size = kv.page_size;
+  p.page_shift = -1;
+  for (int sh = 0; sh < 31; ++sh)
+    if ((1 << sh) == kv.page_size) p.page_shift = sh;
   p.dqk = kv.head_dim_qk;
   p.dvo = kv.head_dim_vo;
   p.k_scale = kv.k_scale;
@@ -169,10 +172,11 @@ AttnParams params_prefill(const pa_prefill_args* a) {
 
 // The plan of one call: which kernels run and how much workspace they need.
 struct Plan {
-  enum Kind { GENERIC, GQA_DECODE, FLASH } kind = GENERIC;
+  enum Kind { GENERIC, GQA_DECODE, FLASH, MLA_DECODE } kind = GENERIC;
   bool same_strides = false;  // V offsets reuse K offsets (equal K/V strides)
   int chunk_tokens = 0;       // internal KV chunking (0: none)
   int max_chunks = 0;
+  int ws_rows = 16;           // workspace row slots per (batch, KV head, chunk)
   size_t workspace = 0;
   const char* name = "generic";
 };
@@ -199,6 +203,21 @@ int decode_chunk_tokens(const AttnParams& p, uint32_t flags) {
   return c;
 }
 
+// Chunk size for the MLA decode: the largest power of two (512..8192 tokens,
+// page aligned) that still gives about a thousand workgroups; bigger chunks
+// mean fewer partial states to write and merge.
+int mla_chunk_tokens(const AttnParams& p, uint32_t flags) {
+  if ((flags & PA_FLAG_NO_INTERNAL_SPLIT) || p.num_splits != 1 || p.max_kv_len <= 0) return 0;
+  const int R = p.q_len * p.group;
+  const int rt = R <= 16 ? 16 : R <= 32 ? 32 : 64;
+  const int64_t tiles = (int64_t)p.batch * p.num_kv_heads * ((R + rt - 1) / rt);
+  int c = 8192;
+  while (c > 512 && tiles * ((p.max_kv_len + c - 1) / c) < 1024) c /= 2;
+  c = (c + p.page_size - 1) / p.page_size * p.page_size;
+  if (p.max_kv_len <= c) return 0;
+  return c;
+}
+
 Plan make_plan(const AttnParams& p, uint32_t flags) {
   Plan pl;
   const bool same = equal_kv_strides(p) && !(flags & PA_FLAG_FORCE_GENERAL_STRIDES);
@@ -214,6 +233,18 @@ Plan make_plan(const AttnParams& p, uint32_t flags) {
     if (pl.chunk_tokens > 0) {
       pl.max_chunks = (p.max_kv_len + pl.chunk_tokens - 1) / pl.chunk_tokens;
       const size_t rows = (size_t)p.batch * p.num_kv_heads * pl.max_chunks * 16;
+      pl.workspace = align256(rows * p.dvo * 4) + 2 * align256(rows * 4);
+    }
+    return pl;
+  }
+  if (pa::mla_decode_supported(p)) {
+    pl.kind = Plan::MLA_DECODE;
+    pl.name = p.kv_dtype == PA_FP8_E4M3 ? "mla_decode_mfma_fp8" : "mla_decode_mfma";
+    pl.chunk_tokens = mla_chunk_tokens(p, flags);
+    if (pl.chunk_tokens > 0) {
+      pl.max_chunks = (p.max_kv_len + pl.chunk_tokens - 1) / pl.chunk_tokens;
+      pl.ws_rows = p.q_len * p.group;
+      const size_t rows = (size_t)p.batch * p.num_kv_heads * pl.max_chunks * pl.ws_rows;
       pl.workspace = align256(rows * p.dvo * 4) + 2 * align256(rows * 4);
     }
     return pl;
@@ -238,8 +269,9 @@ int run_plan(const Plan& pl, AttnParams p, void* ws, size_t ws_bytes, void* cons
                  pl.chunk_tokens, pl.max_chunks, pl.workspace);
   p.chunk_tokens = pl.chunk_tokens;
   p.max_chunks = pl.max_chunks;
+  p.ws_rows = pl.ws_rows;
   if (pl.chunk_tokens > 0) {
-    const size_t rows = (size_t)p.batch * p.num_kv_heads * pl.max_chunks * 16;
+    const size_t rows = (size_t)p.batch * p.num_kv_heads * pl.max_chunks * pl.ws_rows;
     char* w = static_cast<char*>(ws);
     p.ws_o = reinterpret_cast<float*>(w);
     p.ws_lse = reinterpret_cast<float*>(w + align256(rows * p.dvo * 4));
@@ -258,6 +290,9 @@ int run_plan(const Plan& pl, AttnParams p, void* ws, size_t ws_bytes, void* cons
       break;
     case Plan::FLASH:
       e = pa::launch_flash_attn(p, pl.same_strides, stream);
+      break;
+    case Plan::MLA_DECODE:
+      e = pa::launch_mla_decode(p, stream);
       break;
   }
   if (e != hipSuccess) return PA_ERR_HIP;

@@ -66,10 +66,25 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnParams p, int ti
   const int G = p.group;
   const int TQ = kRows / G;
 
-  // ---- which (row tile, KV head, split); late (heavy) row tiles first
-  const int g = blockIdx.y;
-  const int c = blockIdx.z;
-  const int tile_lin = num_row_tiles - 1 - (int)blockIdx.x;
+  // ---- which (row tile, KV head, split).  Workgroups are dealt round-robin to
+  // the 8 XCDs; when the (head, split) groups divide evenly, every group lives on
+  // one XCD (its KV stays in that XCD's L2) and each XCD walks its row tiles
+  // from the latest (heaviest under a causal mask) to the earliest.
+  const int HS = p.num_kv_heads * p.num_splits;
+  const int lam = blockIdx.x;
+  int rank, gc;
+  if (HS % 8 == 0) {
+    const int per = HS / 8;
+    const int xcd = lam % 8, k = lam / 8;
+    rank = k / per;
+    gc = xcd + 8 * (k % per);
+  } else {
+    rank = lam / HS;
+    gc = lam % HS;
+  }
+  const int g = gc % p.num_kv_heads;
+  const int c = gc / p.num_kv_heads;
+  const int tile_lin = num_row_tiles - 1 - rank;
   int b = 0, t_begin, t_end;  // query tokens [t_begin, t_end) of this tile
   if (p.broadcast) {
     t_begin = tile_lin * TQ;
@@ -115,6 +130,11 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnParams p, int ti
   if (lane == 0) s_red[w] = hi;
   __syncthreads();
   const int jhi = min(j1, max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3])));
+  // tiles ending at or before this wave's smallest row limit need no mask
+  int lo = ri.t >= 0 ? ri.lim : INT_MAX;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) lo = min(lo, __shfl_xor(lo, off, 64));
+  const int wave_lim_min = lo;
 
   // ---- Q^T B operand: 8 x 16 B per lane, kept in registers
   i16x8_t qreg[KK];
@@ -138,6 +158,8 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnParams p, int ti
   const uint16_t* kbase = static_cast<const uint16_t*>(p.k);
   const uint16_t* vbase = static_cast<const uint16_t*>(p.v);
   const int P = p.page_size;
+  const int pshift = p.page_shift;
+  float true_max = -INFINITY;  // running row max (the lazily updated m may lag it)
 
   // cooperative tile load: thread -> (chunk cc, tokens tk0 + 16u)
   const int cc = tid % Gm::CPR;
@@ -160,8 +182,9 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnParams p, int ti
         for (int u = 0; u < Gm::LPT; ++u) {
           const int j = jb + tk0 + TSTEP * u;
           const int jj = j < we ? j : we - 1;  // clamp: a valid token, never a poisoned slot
-          const int64_t page = s_pages[jj / P - wb];
-          const int slot = jj % P;
+          const int rel = jj - wb * P;
+          const int64_t page = s_pages[pshift >= 0 ? rel >> pshift : rel / P];
+          const int slot = pshift >= 0 ? (jj & (P - 1)) : jj % P;
           const int64_t koff = page * p.ks0 + slot * p.ks1 + (int64_t)g * p.ks2 + 8 * cc;
           const int64_t voff = SAME ? koff : page * p.vs0 + slot * p.vs1 + (int64_t)g * p.vs2 + 8 * cc;
           kreg[u] = *reinterpret_cast<const uint4*>(kbase + koff);
@@ -205,34 +228,50 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnParams p, int ti
             sacc[mb] = mfma32<DT>(as_i16x8(a), qreg[kk], sacc[mb]);
           }
 
-        // mask, scale, online softmax (lane: row l32, tokens 32mb + 8(i/4) + 4h2 + i%4)
+        // mask (boundary tiles only), online softmax (lane: row l32, tokens
+        // 32mb + 8(i/4) + 4h2 + i%4).  Scores stay unscaled; the scale is fused
+        // into the exponent's FMA.  The reference max m is re-based only when
+        // the tile max exceeds it by more than 8 (log2 units), so most tiles skip
+        // the O rescale; P <= 2^8 keeps 16-bit P and fp32 sums exact enough, and
+        // LSE = m + log2(l) holds for any reference m.
+        if (jb + kKT > wave_lim_min) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int j = jb + 32 * mb + 8 * (i >> 2) + 4 * h2 + (i & 3);
+              sacc[mb][i] = j < ri.lim ? sacc[mb][i] : -INFINITY;
+            }
+        }
         float tmax = -INFINITY;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int j = jb + 32 * mb + 8 * (i >> 2) + 4 * h2 + (i & 3);
-            const float v = j < ri.lim ? sacc[mb][i] * qk_scale : -INFINITY;
-            sacc[mb][i] = v;
-            tmax = fmaxf(tmax, v);
-          }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float mnew = fmaxf(m, tmax);
-        const float mref = mnew == -INFINITY ? 0.f : mnew;
-        const float alpha = fast_exp2(m - mref);
+          for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[mb][i]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * qk_scale;
+        true_max = fmaxf(true_max, tmax);
+        const bool grow = tmax > m + 8.f;
+        if (__ballot(grow)) {
+          const float mnew = grow ? tmax : m;
+          const float alpha = fast_exp2((m == -INFINITY ? -INFINITY : m) -
+                                        (mnew == -INFINITY ? 0.f : mnew));
+          const float a = grow ? alpha : 1.f;
+          lsum *= a;
+#pragma unroll
+          for (int t = 0; t < NDT; ++t) oacc[t] *= a;
+          m = mnew;
+        }
+        const float nmref = -(m == -INFINITY ? 0.f : m);
         float psum = 0.f;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float e = fast_exp2(sacc[mb][i] - mref);
+            const float e = fast_exp2(fmaf(sacc[mb][i], qk_scale, nmref));
             sacc[mb][i] = e;
             psum += e;
           }
-        lsum = fmaf(lsum, alpha, psum);
-        m = mnew;
-#pragma unroll
-        for (int t = 0; t < NDT; ++t) oacc[t] *= alpha;
+        lsum += psum;
 
         // P^T operands of the four 16-token PV steps
         i16x8_t pb[4];
@@ -293,7 +332,7 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnParams p, int ti
   if (h2 == 0) {
     const int64_t sidx = c * p.s_split_stride + rid;
     if (p.lse) p.lse[sidx] = empty ? -INFINITY : (m + fast_log2(ltot)) * kLn2;
-    if (p.mx) p.mx[sidx] = empty ? -INFINITY : m * kLn2;
+    if (p.mx) p.mx[sidx] = empty ? -INFINITY : true_max * kLn2;
   }
 }
 
@@ -308,7 +347,7 @@ hipError_t launch_fd(const AttnParams& p, bool same, hipStream_t stream) {
     num_row_tiles = p.batch * tiles_per_batch;
   }
   if (num_row_tiles == 0) return hipSuccess;
-  const dim3 grid(num_row_tiles, p.num_kv_heads, p.num_splits);
+  const dim3 grid(num_row_tiles * p.num_kv_heads * p.num_splits);
   if (same)
     flash_attn_kernel<DT, D, true><<<grid, 256, 0, stream>>>(p, tiles_per_batch, num_row_tiles);
   else

@@ -7,7 +7,8 @@
 //   s_out = m + ln(sum_c w_c); -inf states carry no weight; all -inf -> 0, -inf.
 //
 // HBM-bound: each row's S x D partials are read once (16-byte loads of four
-// fp32 elements per lane), the S LSEs once per lane from cache.
+// fp32 elements per lane, issued eight states at a time so their latencies
+// overlap), the S LSEs once per lane from cache.
 #include "device_common.h"
 
 namespace pa {
@@ -49,8 +50,16 @@ __global__ __launch_bounds__(256) void merge_kernel(const void* v, const float* 
   const int li = threadIdx.x % tpr;
   if (threadIdx.x >= rpb * tpr || row >= rows) return;
   const int d0 = li * 4;
+  // loads are issued in unrolled blocks of BLK states so their latencies overlap
+  constexpr int BLK = 8;
   float m = -INFINITY;
-  for (int c = 0; c < S; ++c) m = fmaxf(m, s[c * s_ss + row]);
+  for (int c0 = 0; c0 < S; c0 += BLK) {
+    float ls[BLK];
+#pragma unroll
+    for (int k = 0; k < BLK; ++k) ls[k] = c0 + k < S ? s[(c0 + k) * s_ss + row] : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < BLK; ++k) m = fmaxf(m, ls[k]);
+  }
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   if (m == -INFINITY) {
     store4<OT>(out, row * D + d0, acc);
@@ -58,15 +67,26 @@ __global__ __launch_bounds__(256) void merge_kernel(const void* v, const float* 
     return;
   }
   float wsum = 0.f;
-  for (int c = 0; c < S; ++c) {
-    const float lc = s[c * s_ss + row];
-    if (lc == -INFINITY) continue;
-    const float w = fast_exp2((lc - m) * kLog2e);
-    wsum += w;
-    float x[4];
-    load4<VT>(v, c * v_ss + row * D + d0, x);
+  for (int c0 = 0; c0 < S; c0 += BLK) {
+    float ls[BLK];
+    float x[BLK][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, x[i], acc[i]);
+    for (int k = 0; k < BLK; ++k) {
+      const bool ok = c0 + k < S;
+      ls[k] = ok ? s[(c0 + k) * s_ss + row] : -INFINITY;
+      if (ok) {
+        load4<VT>(v, (c0 + k) * v_ss + row * D + d0, x[k]);
+      } else {
+        x[k][0] = x[k][1] = x[k][2] = x[k][3] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < BLK; ++k) {
+      const float w = ls[k] == -INFINITY ? 0.f : fast_exp2((ls[k] - m) * kLog2e);
+      wsum += w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, x[k][i], acc[i]);
+    }
   }
   const float inv = 1.f / wsum;
 #pragma unroll
@@ -100,11 +120,12 @@ __global__ __launch_bounds__(256) void chunk_merge_kernel(AttnParams p, int tpr)
   const int64_t rho = (int64_t)blockIdx.x * rpb + threadIdx.x / tpr;
   const int li = threadIdx.x % tpr;
   const int R = p.q_len * p.group;
-  const int64_t total = (int64_t)p.batch * p.num_kv_heads * 16;
+  const int WR = p.ws_rows;
+  const int64_t total = (int64_t)p.batch * p.num_kv_heads * WR;
   if (threadIdx.x >= rpb * tpr || rho >= total) return;
-  const int r = (int)(rho % 16);
-  const int g = (int)((rho / 16) % p.num_kv_heads);
-  const int b = (int)(rho / (16 * p.num_kv_heads));
+  const int r = (int)(rho % WR);
+  const int g = (int)((rho / WR) % p.num_kv_heads);
+  const int b = (int)(rho / ((int64_t)WR * p.num_kv_heads));
   if (r >= R) return;
   const int kb = p.broadcast ? 0 : b;
   const int n = p.kv_indptr[kb + 1] - p.kv_indptr[kb];
@@ -112,7 +133,7 @@ __global__ __launch_bounds__(256) void chunk_merge_kernel(AttnParams p, int tpr)
   const int nch = num_chunks(L, p.chunk_tokens, p.max_chunks);
   if (nch <= 1) return;
   const int D = p.dvo;
-  const int64_t wrow0 = (int64_t)(b * p.num_kv_heads + g) * p.max_chunks * 16 + r;
+  const int64_t wrow0 = (int64_t)(b * p.num_kv_heads + g) * p.max_chunks * WR + r;
   const int d0 = li * 4;
   // loads are issued in unrolled blocks of 8 chunks so their latencies overlap
   constexpr int BLK = 8;
@@ -122,8 +143,8 @@ __global__ __launch_bounds__(256) void chunk_merge_kernel(AttnParams p, int tpr)
 #pragma unroll
     for (int k = 0; k < BLK; ++k) {
       const bool ok = c0 + k < nch;
-      ls[k] = ok ? p.ws_lse[wrow0 + (c0 + k) * 16] : -INFINITY;
-      ms[k] = ok ? p.ws_mx[wrow0 + (c0 + k) * 16] : -INFINITY;
+      ls[k] = ok ? p.ws_lse[wrow0 + (int64_t)(c0 + k) * WR] : -INFINITY;
+      ms[k] = ok ? p.ws_mx[wrow0 + (int64_t)(c0 + k) * WR] : -INFINITY;
     }
 #pragma unroll
     for (int k = 0; k < BLK; ++k) {
@@ -140,8 +161,8 @@ __global__ __launch_bounds__(256) void chunk_merge_kernel(AttnParams p, int tpr)
 #pragma unroll
       for (int k = 0; k < BLK; ++k) {
         const bool ok = c0 + k < nch;
-        ls[k] = ok ? p.ws_lse[wrow0 + (c0 + k) * 16] : -INFINITY;
-        x[k] = ok ? *reinterpret_cast<const float4*>(p.ws_o + (wrow0 + (c0 + k) * 16) * D + d0)
+        ls[k] = ok ? p.ws_lse[wrow0 + (int64_t)(c0 + k) * WR] : -INFINITY;
+        x[k] = ok ? *reinterpret_cast<const float4*>(p.ws_o + (wrow0 + (int64_t)(c0 + k) * WR) * D + d0)
                   : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
@@ -174,7 +195,7 @@ __global__ __launch_bounds__(256) void chunk_merge_kernel(AttnParams p, int tpr)
 hipError_t launch_chunk_merge(const AttnParams& p, hipStream_t stream) {
   const int tpr = p.dvo / 4;
   const int rpb = 256 / tpr;
-  const int64_t total = (int64_t)p.batch * p.num_kv_heads * 16;
+  const int64_t total = (int64_t)p.batch * p.num_kv_heads * p.ws_rows;
   const dim3 grid((unsigned)((total + rpb - 1) / rpb));
   chunk_merge_kernel<<<grid, dim3(rpb * tpr), 0, stream>>>(p, tpr);
   return hipGetLastError();

@@ -1,0 +1,401 @@
+// MLA paged decode: every query head and every query token of a request reads
+// one shared latent KV row per token (576 dims: K is the whole row, V its first
+// 512 dims) — the shared latent KV of the FlashInfer PR #3309 analysis (code
+// section 1), where q_len is folded into the head dimension because the KV is
+// shared by all heads and queries.  Here all q_len x H rows of a request form
+// row tiles of RT rows (r = token*H + head), so one KV tile feeds every row.
+//
+// A workgroup = (request, row tile, KV chunk) with 4 waves.  Per 64-token tile:
+//   the tile's rows (64 x 576, stored bf16; fp8 e4m3 codes are widened exactly
+//   to bf16 on the way into LDS) are double-buffered in LDS, the next tile's
+//   global loads overlapping this tile's math;
+//   S phase: the RT x 64 scores are cut into 16x16 blocks over the waves
+//     (v_mfma_f32_16x16x32_bf16: K from LDS as the A operand, Q^T held in
+//     registers as the B operand); row maxima across waves meet in LDS;
+//   softmax: lazily re-based running max (re-based only when a tile max exceeds
+//     it by more than 2^8), exp2 with the scale fused into its FMA; P (bf16)
+//     and the per-row rescale factors go to LDS;
+//   PV phase: wave w owns output dims [128w, 128w+128): O^T += V^T P^T with V^T
+//     read transposed from the same LDS rows (ds_read_b64_tr_b16) and P^T read
+//     row-major from LDS.
+// Chunks of long KV batches leave partial states (O normalised by the chunk's
+// own sum, LSE, max) in the workspace for the chunk-merge launch.
+#include "mfma_common.h"
+
+namespace pa {
+namespace {
+
+constexpr int kDqk = 576, kDvo = 512;
+constexpr int kTK = 64;                      // KV tokens per tile
+constexpr int kKP = kDqk * 2 + 16;           // LDS row pitch (bytes)
+constexpr int kStage = kTK * kKP;            // one KV tile in LDS
+constexpr int kPageWinM = 256;               // page ids staged in LDS at a time
+
+template <int RT>
+struct MGeo {
+  static constexpr int NRB = RT / 16;        // 16-row blocks
+  static constexpr int WPR = 4 / NRB;        // waves sharing a row block in the S phase
+  static constexpr int TBW = 4 / WPR;        // 16-token blocks per wave in the S phase
+  static constexpr int PP = kTK * 2 + 16;    // P row pitch (bytes)
+};
+
+template <bool FP8, int RT>
+__global__ __launch_bounds__(256, 1) void mla_decode_kernel(AttnParams p, int nrt, int ngroups) {
+  using Gm = MGeo<RT>;
+  constexpr int NRB = Gm::NRB, WPR = Gm::WPR, TBW = Gm::TBW;
+  constexpr int KK = kDqk / 32;             // 18 k-steps of Q.K
+  constexpr int CPR = FP8 ? kDqk / 16 : kDqk / 8;   // 16-byte global chunks per token row
+  constexpr int CPT = kTK * CPR / 256;      // chunks per thread per tile
+  __shared__ __align__(16) uint8_t s_kv[2 * kStage];
+  __shared__ __align__(16) uint8_t s_p[RT * Gm::PP];
+  __shared__ float s_pmax[WPR][RT];
+  __shared__ float s_alpha[RT];
+  __shared__ int s_pages[kPageWinM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+
+  // ---- work item: (request b, KV head g, row tile rt, chunk c); the row tiles
+  // of one (b, g, c) share an XCD so the KV chunk is read once into its L2
+  const int lam = blockIdx.x;
+  const int xcd = lam % 8, k8 = lam / 8;
+  const int rt = k8 % nrt;
+  const int gi = (k8 / nrt) * 8 + xcd;
+  if (gi >= ngroups) return;
+  const int groups_per_b = p.num_kv_heads * p.max_chunks;
+  const int b = gi / groups_per_b;
+  const int g = (gi / p.max_chunks) % p.num_kv_heads;
+  const int c = gi % p.max_chunks;
+  const int kb = p.broadcast ? 0 : b;
+  const int pbeg = p.kv_indptr[kb];
+  const int n = p.kv_indptr[kb + 1] - pbeg;
+  const int L = n ? (n - 1) * p.page_size + p.kv_last[kb] : 0;
+  int j0, j1;
+  bool to_ws = false;
+  if (p.chunk_tokens > 0) {
+    const int nch = num_chunks(L, p.chunk_tokens, p.max_chunks);
+    if (c >= nch) return;
+    j0 = c * p.chunk_tokens;
+    j1 = (c == nch - 1) ? L : j0 + p.chunk_tokens;
+    to_ws = nch > 1;
+  } else {
+    if (c >= p.num_splits) return;
+    j0 = (int)(((int64_t)c * n / p.num_splits) * p.page_size);
+    j1 = min((int)(((int64_t)(c + 1) * n / p.num_splits) * p.page_size), L);
+  }
+  const int R = p.q_len * p.group;  // folded rows of this (request, KV head)
+  const int row0 = rt * RT;
+
+  // ---- S-phase role: row block rb, token blocks tb = w % WPR + WPR*u
+  const int rb = w / WPR;
+  const int wp = w % WPR;
+  const int srow = row0 + 16 * rb + l16;  // this lane's S row
+  const bool srow_ok = srow < R;
+  int slim = j1;
+  if (srow_ok && p.causal) slim = min(slim, L - p.q_len + srow / p.group + 1);
+  if (!srow_ok) slim = INT_MIN;
+
+  i16x8_t qreg[KK];
+  {
+    const int qi = srow_ok ? srow / p.group : 0, qh = srow_ok ? srow % p.group : 0;
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) +
+                         ((int64_t)(b * p.q_len + qi) * p.num_qo_heads + (int64_t)g * p.group + qh) * kDqk +
+                         8 * lg;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const uint4 v = srow_ok ? *reinterpret_cast<const uint4*>(qp + 32 * kk) : make_uint4(0, 0, 0, 0);
+      qreg[kk] = as_i16x8(v);
+    }
+  }
+  // smallest visible limit over this wave's valid S rows (tiles below it need no mask)
+  int lo = srow_ok ? slim : INT_MAX;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) lo = min(lo, __shfl_xor(lo, off, 64));
+  const int wave_lim_min = lo;
+  // workgroup's last visible token
+  int jhi = j1;
+  if (p.causal) {
+    const int last_row = min(row0 + RT, R) - 1;
+    jhi = min(j1, L - p.q_len + last_row / p.group + 1);
+  }
+
+  float m = -INFINITY, lsum = 0.f, true_max = -INFINITY;  // S-phase row state (row srow)
+  f32x4_t oacc[NRB][8];                                     // PV: rows 16rt'+l16, dims 128w+16dt+4lg+i
+#pragma unroll
+  for (int a = 0; a < NRB; ++a)
+#pragma unroll
+    for (int d = 0; d < 8; ++d) oacc[a][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const float qk_scale = p.sm_scale * p.k_scale * kLog2e;
+  const int P = p.page_size;
+  const int pshift = p.page_shift;
+
+  if (jhi > j0) {
+    const int pfirst = j0 / P, plast = (jhi - 1) / P;
+    for (int wb = pfirst; wb <= plast; wb += kPageWinM) {
+      const int npw = min(kPageWinM, plast - wb + 1);
+      __syncthreads();
+      for (int i = tid; i < npw; i += 256) s_pages[i] = p.kv_indices[pbeg + wb + i];
+      __syncthreads();
+      const int ws = max(j0, wb * P), we = min(jhi, (wb + npw) * P);
+      const int nk = (we - ws + kTK - 1) / kTK;
+
+      // cooperative loads: linear 16-byte chunk q = u*256 + tid of the tile
+      // (row-major over 64 rows x CPR chunks), so each instruction reads ~1 KB
+      // contiguous within at most two token rows.  The next tile is fetched in
+      // two halves (chunks [0, CA) during the S phase, [CA, CPT) during the PV
+      // phase) to bound the staging registers.
+      constexpr int CA = CPT / 2;
+      uint4 ld[CPT - CA];
+      auto gload = [&](int jb, int u0, int u1) {
+#pragma unroll
+        for (int u = u0; u < u1; ++u) {
+          const int q = u * 256 + tid;
+          const int row = q / CPR, col = q % CPR;
+          const int j = jb + row;
+          const int jj = j < we ? j : we - 1;  // a valid token: never a poisoned slot
+          const int rel = jj - wb * P;
+          const int64_t page = s_pages[pshift >= 0 ? rel >> pshift : rel / P];
+          const int slot = pshift >= 0 ? (jj & (P - 1)) : jj % P;
+          const int64_t off = page * p.ks0 + slot * p.ks1 + (int64_t)g * p.ks2;
+          if constexpr (FP8)
+            ld[u - u0] = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(p.k) + off + 16 * col);
+          else
+            ld[u - u0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.k) + off + 8 * col);
+        }
+      };
+      auto lstore = [&](int jb, int stage, int u0, int u1) {
+        uint8_t* base = s_kv + stage * kStage;
+#pragma unroll
+        for (int u = u0; u < u1; ++u) {
+          const int q = u * 256 + tid;
+          const int row = q / CPR, col = q % CPR;
+          const bool ok = jb + row < we;  // rows past the end read as zeros
+          const uint4 x = ld[u - u0];
+          if constexpr (FP8) {
+            // 16 e4m3 codes -> 16 bf16 (exact: every e4m3 value is a bf16 value)
+            const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
+            uint32_t o[8];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              const auto lo2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[h], false);
+              const auto hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[h], true);
+              o[2 * h] = (__float_as_uint(lo2[0]) >> 16) | (__float_as_uint(lo2[1]) & 0xffff0000u);
+              o[2 * h + 1] = (__float_as_uint(hi2[0]) >> 16) | (__float_as_uint(hi2[1]) & 0xffff0000u);
+            }
+            uint4* dst = reinterpret_cast<uint4*>(base + row * kKP + col * 32);
+            dst[0] = ok ? make_uint4(o[0], o[1], o[2], o[3]) : make_uint4(0, 0, 0, 0);
+            dst[1] = ok ? make_uint4(o[4], o[5], o[6], o[7]) : make_uint4(0, 0, 0, 0);
+          } else {
+            *reinterpret_cast<uint4*>(base + row * kKP + col * 16) = ok ? x : make_uint4(0, 0, 0, 0);
+          }
+        }
+      };
+
+      gload(ws, 0, CA);
+      lstore(ws, 0, 0, CA);
+      gload(ws, CA, CPT);
+      lstore(ws, 0, CA, CPT);
+      __syncthreads();
+      for (int kt = 0; kt < nk; ++kt) {
+        const int jb = ws + kt * kTK;
+        const int stage = kt & 1;
+        const bool more = kt + 1 < nk;
+        if (more) gload(jb + kTK, 0, CA);
+        const uint8_t* kv = s_kv + stage * kStage;
+
+        // ---- S phase: blocks (rb, tb) of 16 rows x 16 tokens
+        f32x4_t sacc[TBW];
+#pragma unroll
+        for (int u = 0; u < TBW; ++u) sacc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+          for (int u = 0; u < TBW; ++u) {
+            const int tb = wp + WPR * u;
+            const uint4 a = *reinterpret_cast<const uint4*>(kv + (16 * tb + l16) * kKP + (32 * kk + 8 * lg) * 2);
+            sacc[u] = mfma16<BF16>(as_i16x8(a), qreg[kk], sacc[u]);
+          }
+        // C layout: lane row srow, tokens 16tb + 4lg + i
+        if (jb + kTK > wave_lim_min) {
+#pragma unroll
+          for (int u = 0; u < TBW; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int j = jb + 16 * (wp + WPR * u) + 4 * lg + i;
+              sacc[u][i] = j < slim ? sacc[u][i] : -INFINITY;
+            }
+        }
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < TBW; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sacc[u][i]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        if (lg == 0) s_pmax[wp][16 * rb + l16] = tmax;
+        __syncthreads();
+        float rmax = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < WPR; ++k) rmax = fmaxf(rmax, s_pmax[k][16 * rb + l16]);
+        rmax *= qk_scale;
+        true_max = fmaxf(true_max, rmax);
+        const bool grow = rmax > m + 8.f;
+        float alpha = 1.f;
+        if (grow) {
+          alpha = fast_exp2((m == -INFINITY ? -INFINITY : m) - rmax);
+          lsum *= alpha;
+          m = rmax;
+        }
+        const float nmref = -(m == -INFINITY ? 0.f : m);
+        float psum = 0.f;
+        uint8_t* prow = s_p + (16 * rb + l16) * Gm::PP;
+#pragma unroll
+        for (int u = 0; u < TBW; ++u) {
+          float e[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            e[i] = fast_exp2(fmaf(sacc[u][i], qk_scale, nmref));
+            psum += e[i];
+          }
+          *reinterpret_cast<uint2*>(prow + (16 * (wp + WPR * u) + 4 * lg) * 2) =
+              make_uint2(pack2<BF16>(e[0], e[1]), pack2<BF16>(e[2], e[3]));
+        }
+        lsum += psum;
+        if (wp == 0 && lg == 0) s_alpha[16 * rb + l16] = alpha;
+        if (more) {
+          lstore(jb + kTK, stage ^ 1, 0, CA);
+          gload(jb + kTK, CA, CPT);
+        }
+        __syncthreads();
+
+        // ---- PV phase: this wave's 128 output dims, all RT rows
+#pragma unroll
+        for (int a = 0; a < NRB; ++a) {
+          const float al = s_alpha[16 * a + l16];
+          if (__ballot(al != 1.f)) {
+#pragma unroll
+            for (int d = 0; d < 8; ++d) oacc[a][d] *= al;
+          }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          i16x8_t pb[NRB];
+#pragma unroll
+          for (int a = 0; a < NRB; ++a)
+            pb[a] = as_i16x8(*reinterpret_cast<const uint4*>(s_p + (16 * a + l16) * Gm::PP +
+                                                            (32 * ks + 8 * lg) * 2));
+          const uint16_t* vr = reinterpret_cast<const uint16_t*>(kv + (32 * ks + 8 * lg + (l16 >> 2)) * kKP) +
+                               128 * w + 4 * (l16 & 3);
+#pragma unroll
+          for (int d = 0; d < 8; ++d) {
+            const i16x4_t lo4 = lds_read_tr(vr + 16 * d);
+            const i16x4_t hi4 = lds_read_tr(vr + 4 * (kKP / 2) + 16 * d);
+            const i16x8_t va = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+#pragma unroll
+            for (int a = 0; a < NRB; ++a) oacc[a][d] = mfma16<BF16>(va, pb[a], oacc[a][d]);
+          }
+        }
+        if (more) lstore(jb + kTK, stage ^ 1, CA, CPT);
+        __syncthreads();
+      }
+    }
+  }
+
+  // ---- epilogue: total row sums meet in LDS (s_pmax reused), then each wave
+  // writes its 128 dims of every row; LSE / max by the S-phase owners
+  float lpart = lsum + __shfl_xor(lsum, 16, 64);
+  lpart += __shfl_xor(lpart, 32, 64);
+  __syncthreads();
+  if (lg == 0) s_pmax[wp][16 * rb + l16] = lpart;
+  __syncthreads();
+  float ltot_s = 0.f;
+#pragma unroll
+  for (int k = 0; k < WPR; ++k) ltot_s += s_pmax[k][16 * rb + l16];
+  if (wp == 0 && lg == 0 && srow_ok) {
+    const bool empty = !(ltot_s > 0.f);
+    const int64_t rid = (int64_t)(b * p.q_len + srow / p.group) * p.num_qo_heads + (int64_t)g * p.group +
+                        srow % p.group;
+    const float lse = empty ? -INFINITY : (m + fast_log2(ltot_s)) * kLn2;
+    const float mx = empty ? -INFINITY : true_max * kLn2;
+    if (to_ws) {
+      const int64_t wrow = ((int64_t)(b * p.num_kv_heads + g) * p.max_chunks + c) * p.ws_rows + srow;
+      p.ws_lse[wrow] = lse;
+      p.ws_mx[wrow] = mx;
+    } else {
+      const int64_t sidx = c * p.s_split_stride + rid;
+      if (p.lse) p.lse[sidx] = lse;
+      if (p.mx) p.mx[sidx] = mx;
+    }
+  }
+#pragma unroll
+  for (int a = 0; a < NRB; ++a) {
+    const int r = row0 + 16 * a + l16;
+    if (r >= R) continue;
+    float lt = 0.f;
+#pragma unroll
+    for (int k = 0; k < WPR; ++k) lt += s_pmax[k][16 * a + l16];
+    const float scale = lt > 0.f ? p.v_scale / lt : 0.f;
+    const int64_t rid = (int64_t)(b * p.q_len + r / p.group) * p.num_qo_heads + (int64_t)g * p.group +
+                        r % p.group;
+    const int64_t wrow = ((int64_t)(b * p.num_kv_heads + g) * p.max_chunks + c) * p.ws_rows + r;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const int dim = 128 * w + 16 * d + 4 * lg;
+      const float x0 = oacc[a][d][0] * scale, x1 = oacc[a][d][1] * scale;
+      const float x2 = oacc[a][d][2] * scale, x3 = oacc[a][d][3] * scale;
+      if (to_ws) {
+        *reinterpret_cast<float4*>(p.ws_o + wrow * kDvo + dim) = make_float4(x0, x1, x2, x3);
+      } else if (p.o_dtype == F32) {
+        *reinterpret_cast<float4*>(static_cast<float*>(p.o) + c * p.o_split_stride + rid * kDvo + dim) =
+            make_float4(x0, x1, x2, x3);
+      } else {
+        const uint2 v = p.o_dtype == F16 ? make_uint2(pack2<F16>(x0, x1), pack2<F16>(x2, x3))
+                                         : make_uint2(pack2<BF16>(x0, x1), pack2<BF16>(x2, x3));
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + c * p.o_split_stride + rid * kDvo + dim) = v;
+      }
+    }
+  }
+}
+
+template <bool FP8, int RT>
+hipError_t launch_rt(const AttnParams& p, hipStream_t stream) {
+  const int R = p.q_len * p.group;
+  const int nrt = (R + RT - 1) / RT;
+  const int items = p.chunk_tokens > 0 ? p.max_chunks : p.num_splits;
+  // mla kernel indexes groups with max_chunks; explicit splits use num_splits chunks
+  AttnParams q = p;
+  if (p.chunk_tokens <= 0) q.max_chunks = items;
+  const int ngroups = p.batch * p.num_kv_heads * items;
+  const int blocks = nrt * 8 * ((ngroups + 7) / 8);
+  mla_decode_kernel<FP8, RT><<<blocks, 256, 0, stream>>>(q, nrt, ngroups);
+  return hipGetLastError();
+}
+
+template <bool FP8>
+hipError_t launch_f(const AttnParams& p, hipStream_t stream) {
+  const int R = p.q_len * p.group;
+  if (R <= 16) return launch_rt<FP8, 16>(p, stream);
+  if (R <= 32) return launch_rt<FP8, 32>(p, stream);
+  return launch_rt<FP8, 64>(p, stream);
+}
+
+}  // namespace
+
+bool mla_decode_supported(const AttnParams& p) {
+  return p.qo_indptr == nullptr && p.q_dtype == BF16 && (p.kv_dtype == BF16 || p.kv_dtype == FP8) &&
+         p.dqk == kDqk && p.dvo == kDvo && p.ks0 == p.vs0 && p.ks1 == p.vs1 && p.ks2 == p.vs2 &&
+         p.k == p.v;
+}
+
+int mla_rows_per_tile(const AttnParams& p) {
+  const int R = p.q_len * p.group;
+  return R <= 16 ? 16 : R <= 32 ? 32 : 64;
+}
+
+hipError_t launch_mla_decode(const AttnParams& p, hipStream_t stream) {
+  return p.kv_dtype == FP8 ? launch_f<true>(p, stream) : launch_f<false>(p, stream);
+}
+
+}  // namespace pa

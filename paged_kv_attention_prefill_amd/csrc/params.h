@@ -19,6 +19,7 @@ struct AttnParams {
   const void* v;
   int64_t ks0, ks1, ks2, vs0, vs1, vs2;
   int32_t page_size, dqk, dvo;
+  int32_t page_shift;       // log2(page_size) if a power of two, else -1
   float k_scale, v_scale, sm_scale;
   const int32_t* kv_indptr;
   const int32_t* kv_indices;
@@ -39,9 +40,10 @@ struct AttnParams {
   // more than one chunk leave partial states in the workspace for a merge launch
   int32_t chunk_tokens;
   int32_t max_chunks;
-  float* ws_o;              // [B][Hkv][max_chunks][16][dvo]
-  float* ws_lse;            // [B][Hkv][max_chunks][16]
-  float* ws_mx;             // [B][Hkv][max_chunks][16]
+  int32_t ws_rows;          // row slots per (batch, KV head, chunk) in the workspace
+  float* ws_o;              // [B][Hkv][max_chunks][ws_rows][dvo]
+  float* ws_lse;            // [B][Hkv][max_chunks][ws_rows]
+  float* ws_mx;             // [B][Hkv][max_chunks][ws_rows]
 };
 
 // Number of chunks of a KV batch of L tokens under internal chunking.
@@ -54,6 +56,8 @@ __host__ __device__ inline int num_chunks(int L, int chunk_tokens, int max_chunk
 hipError_t launch_generic(const AttnParams& p, hipStream_t stream);
 bool gqa_decode_supported(const AttnParams& p);
 hipError_t launch_gqa_decode(const AttnParams& p, bool same_strides, hipStream_t stream);
+bool mla_decode_supported(const AttnParams& p);
+hipError_t launch_mla_decode(const AttnParams& p, hipStream_t stream);
 bool flash_attn_supported(const AttnParams& p);
 hipError_t launch_flash_attn(const AttnParams& p, bool same_strides, hipStream_t stream);
 hipError_t launch_chunk_merge(const AttnParams& p, hipStream_t stream);

@@ -44,6 +44,27 @@ def small(name):
                                    page_size=16, q_dtype=W.DT_BF16, kv_dtype=W.DT_BF16),
         "c3": lambda: W.config3(batch=3, min_q=1, max_q=300, max_prefix=400),
         "c3_fresh": lambda: W.config3(batch=2, min_q=100, max_q=260, max_prefix=0),
+        "c3_p24_g8": lambda: W.build(np.random.default_rng(31), 31, "prefill_p24", q_lens=[1, 70, 200],
+                                     kv_lens=[1, 300, 200], num_qo_heads=32, num_kv_heads=4,
+                                     head_dim_qk=128, head_dim_vo=128, page_size=24,
+                                     q_dtype=W.DT_BF16, kv_dtype=W.DT_BF16, causal=True,
+                                     uniform_q_len=False),
+        "c3_mha_d64_f16": lambda: W.build(np.random.default_rng(32), 32, "prefill_mha", q_lens=[130, 5],
+                                          kv_lens=[900, 5], num_qo_heads=4, num_kv_heads=4,
+                                          head_dim_qk=64, head_dim_vo=64, page_size=16,
+                                          q_dtype=W.DT_F16, kv_dtype=W.DT_F16, causal=True,
+                                          uniform_q_len=False),
+        "c3_noncausal_g3": lambda: W.build(np.random.default_rng(33), 33, "prefill_g3", q_lens=[50, 100],
+                                           kv_lens=[80, 3000], num_qo_heads=6, num_kv_heads=2,
+                                           head_dim_qk=128, head_dim_vo=128, page_size=16,
+                                           q_dtype=W.DT_BF16, kv_dtype=W.DT_BF16, causal=False,
+                                           uniform_q_len=False),
+        "c5_causal_prefill_bcast": lambda: W.build(np.random.default_rng(34), 34, "bcast_prefill",
+                                                   q_lens=[3, 40, 1], kv_lens=[500],
+                                                   num_qo_heads=32, num_kv_heads=8, head_dim_qk=128,
+                                                   head_dim_vo=128, page_size=128, q_dtype=W.DT_F16,
+                                                   kv_dtype=W.DT_F16, kv_broadcast=True,
+                                                   causal=True, uniform_q_len=False),
         "c5": lambda: W.config5(num_queries=8, kv_len=5000, num_kv_splits=16),
         "c5_long": lambda: W.config5(num_queries=3, kv_len=131072, num_kv_splits=16),
     }[name]()
@@ -64,7 +85,8 @@ def run_and_check(w, label, flags=0, **kw):
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c2_hnd", "c2_mixed", "c2_kv2", "c2_g16",
                                   "c2_q2_causal", "c2_d64_f16", "c2_d256", "c3", "c3_fresh",
-                                  "c5", "c5_long"])
+                                  "c3_p24_g8", "c3_mha_d64_f16", "c3_noncausal_g3",
+                                  "c5_causal_prefill_bcast", "c5", "c5_long"])
 def test_parity_small(name):
     print(f"case {name}", flush=True)
     run_and_check(small(name), name)
@@ -207,3 +229,10 @@ def test_decode_takes_mfma_path_with_and_without_internal_chunks():
         run_and_check(w, f"c2 flags={flags}", flags=flags)
     # a length hint below the real maximum only changes the chunking, not the result
     run_and_check(w, "c2 short hint", max_kv_len=300)
+
+
+@pytest.mark.parametrize("name,prefix", [("c3", "flash_attn_mfma"), ("c5", "flash_attn_mfma"),
+                                         ("c2", "gqa_decode_mfma"), ("c1", "generic")])
+def test_plan_names(name, prefix):
+    step = R.prepare(R.upload(small(name)))
+    assert step.attention_kernel_name.startswith(prefix), step.attention_kernel_name

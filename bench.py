@@ -111,12 +111,45 @@ def cpu_baseline(w, target_s: float = 15.0):
         chosen.append(int(b))
         acc += per_batch[b]
     rows = np.concatenate([rows_of(b) for b in chosen])
-    t0 = time.perf_counter()
-    OR.attention(w, rows=rows, num_kv_splits=1)
-    elapsed = time.perf_counter() - t0
+    # repeat a sample that finishes quickly so the timing covers ~min(10 s, target)
+    reps, elapsed = 0, 0.0
+    while reps == 0 or (elapsed < min(10.0, target_s) and reps < 20):
+        t0 = time.perf_counter()
+        OR.attention(w, rows=rows, num_kv_splits=1)
+        elapsed += time.perf_counter() - t0
+        reps += 1
     frac = acc / per_batch.sum()
-    return elapsed / frac, dict(batches=len(chosen), rows=int(rows.size), seconds=elapsed,
-                                fraction=frac, threads=OR.num_threads())
+    return elapsed / reps / frac, dict(batches=len(chosen), rows=int(rows.size),
+                                       seconds=elapsed, reps=reps, fraction=frac,
+                                       threads=OR.num_threads())
+
+
+COPY_BYTES = 1 << 30  # calibration copy: reads and writes this many bytes per launch
+
+
+def copy_calibration(steps: int) -> int:
+    """A plain streaming kernel of known size (elementwise negate of a 1 GiB fp32
+    tensor: 1 GiB read, 1 GiB written per launch) for scaling HBM byte counters."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "launches": steps}))
+    return 0
+
+
+def recorded_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from profiles/traffic.json if it was measured for this
+    workload and kernel with the current kernel sources, else None."""
+    from paged_kv_attention_prefill_amd import profiling
+    if not os.path.exists(profiling.TRAFFIC_JSON):
+        return None
+    rec = json.load(open(profiling.TRAFFIC_JSON)).get(workload)
+    if not rec or rec.get("source_hash") != profiling.kernel_source_hash():
+        return None
+    return int(rec["traffic_bytes"])
 
 
 def main(argv=None):
@@ -127,11 +160,16 @@ def main(argv=None):
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only the HBM-counter calibration copy kernel")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {a.gpus}); run with --gpus 1", file=sys.stderr)
         return 2
+
+    if a.copy_calibration:
+        return copy_calibration(a.steps)
 
     import torch
     from paged_kv_attention_prefill_amd import binding as B
@@ -172,6 +210,7 @@ def main(argv=None):
         ach = flops / (attn_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    roof["traffic"] = recorded_traffic(a.workload, call.attention_kernel_name)
     roof["kernel"] = call.attention_kernel_name
     roof["kernel_ms"] = round(attn_ms, 5)
     roof["bytes_per_launch"] = attn_bytes
@@ -211,8 +250,8 @@ def main(argv=None):
                                 "cores": info["threads"], "kind": "oracle",
                                 "sample": (f"{info['batches']} whole query batches "
                                            f"({info['rows']} rows, {info['fraction']:.3f} of the "
-                                           f"work) in {info['seconds']:.1f} s, scaled to the "
-                                           "full workload"),
+                                           f"work), {info['reps']} run(s) in "
+                                           f"{info['seconds']:.1f} s, scaled to the full workload"),
                                 "seconds_full_workload": round(full_s, 2)}
     print(json.dumps(line), flush=True)
     return 0

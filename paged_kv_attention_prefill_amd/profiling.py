@@ -1,0 +1,150 @@
+"""Summaries of rocprofv3 output for the profiles/ directory.
+
+    python -m paged_kv_attention_prefill_amd.profiling kernels <trace_dir> [--match NAME]
+    python -m paged_kv_attention_prefill_amd.profiling counters <pmc_dir> [--match NAME]
+    python -m paged_kv_attention_prefill_amd.profiling traffic --workload W --kernel K \
+        --fetch <pmc_dir> --write <pmc_dir> --copy-fetch <pmc_dir> --copy-write <pmc_dir> \
+        --copy-bytes N
+
+``kernels`` prints per-kernel dispatch counts and durations from a
+``--kernel-trace`` run (CSV output, ``-f csv``); ``counters`` prints per-kernel
+averages of the counters of a ``--pmc`` run; ``traffic`` turns FETCH_SIZE and
+WRITE_SIZE (KiB per dispatch) into HBM bytes per launch, each scaled by what the
+same counter reads for a plain copy kernel of known size, and records them in
+profiles/traffic.json together with a hash of the kernel sources (the bench
+reports the record only while the sources are unchanged).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the library's kernel and host sources."""
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(PKG, "csrc", "*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _csv(dirname: str, suffix: str):
+    files = sorted(glob.glob(os.path.join(dirname, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {dirname}")
+    rows = []
+    for fn in files:
+        with open(fn, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def short(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "")
+    return name if len(name) < 110 else name[:107] + "..."
+
+
+def kernel_stats(trace_dir: str, match: str = ""):
+    rows = _csv(trace_dir, "kernel_trace.csv")
+    agg = defaultdict(list)
+    for r in rows:
+        n = r.get("Kernel_Name", "")
+        if match and match not in n:
+            continue
+        agg[n].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = []
+    for n, ds in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        out.append(dict(kernel=short(n), calls=len(ds), avg_us=statistics.mean(ds),
+                        median_us=statistics.median(ds), min_us=min(ds), max_us=max(ds),
+                        total_us=sum(ds)))
+    return out
+
+
+def counter_stats(pmc_dir: str, match: str = ""):
+    rows = _csv(pmc_dir, "counter_collection.csv")
+    agg = defaultdict(lambda: defaultdict(list))
+    for r in rows:
+        n = r.get("Kernel_Name", "")
+        if match and match not in n:
+            continue
+        agg[n][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = []
+    for n, ctrs in agg.items():
+        out.append(dict(kernel=short(n), dispatches=max(len(v) for v in ctrs.values()),
+                        **{k: statistics.mean(v) for k, v in ctrs.items()}))
+    return out
+
+
+def _one(stats, counter):
+    vals = [s[counter] for s in stats if counter in s]
+    if not vals:
+        raise SystemExit(f"counter {counter} not found")
+    return max(vals)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    k = sub.add_parser("kernels")
+    k.add_argument("dir")
+    k.add_argument("--match", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--match", default="")
+    t = sub.add_parser("traffic")
+    for a in ("--workload", "--kernel", "--fetch", "--write", "--copy-fetch", "--copy-write"):
+        t.add_argument(a, required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--algorithmic-bytes", type=int, default=0)
+    a = ap.parse_args(argv)
+    if a.cmd == "kernels":
+        print("| kernel | calls | avg us | median us | min us | max us |")
+        print("|---|---|---|---|---|---|")
+        for s in kernel_stats(a.dir, a.match):
+            print(f"| {s['kernel']} | {s['calls']} | {s['avg_us']:.2f} | {s['median_us']:.2f} | "
+                  f"{s['min_us']:.2f} | {s['max_us']:.2f} |")
+        return 0
+    if a.cmd == "counters":
+        for s in counter_stats(a.dir, a.match):
+            print(json.dumps(s))
+        return 0
+    fetch = _one(counter_stats(a.fetch, a.kernel), "FETCH_SIZE")
+    write = _one(counter_stats(a.write, a.kernel), "WRITE_SIZE")
+    cf = _one(counter_stats(a.copy_fetch, "neg_kernel"), "FETCH_SIZE")
+    cw = _one(counter_stats(a.copy_write, "neg_kernel"), "WRITE_SIZE")
+    f_scale = a.copy_bytes / (cf * 1024.0)
+    w_scale = a.copy_bytes / (cw * 1024.0)
+    rec = dict(workload=a.workload, kernel=a.kernel, source_hash=kernel_source_hash(),
+               fetch_kib=fetch, write_kib=write, copy_fetch_kib=cf, copy_write_kib=cw,
+               copy_bytes=a.copy_bytes, fetch_scale=f_scale, write_scale=w_scale,
+               fetch_bytes=fetch * 1024.0 * f_scale, write_bytes=write * 1024.0 * w_scale)
+    rec["traffic_bytes"] = rec["fetch_bytes"] + rec["write_bytes"]
+    if a.algorithmic_bytes:
+        rec["algorithmic_bytes"] = a.algorithmic_bytes
+        rec["traffic_over_algorithmic"] = rec["traffic_bytes"] / a.algorithmic_bytes
+    data = {}
+    if os.path.exists(TRAFFIC_JSON):
+        data = json.load(open(TRAFFIC_JSON))
+    data[a.workload] = rec
+    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+    print(json.dumps(rec, indent=1))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -6,58 +6,215 @@
 // per tile instead of once per query batch.
 //
 // Rows: a row is (query token t, query head h) with h in KV group g; a row tile
-// holds TQ = 128/G tokens x G heads (r = token_offset*G + head_in_group).
+// holds TQ = 256/G tokens x G heads (r = token_offset*G + head_in_group).
 // Without broadcast a tile's tokens come from one query batch; with broadcast
 // they run over all query tokens of all batches.
 //
-// A workgroup = (row tile, KV head g, explicit KV split) with 4 waves of 32
-// rows.  Per 64-token KV tile (double-buffered in LDS, loaded cooperatively
-// with the page ids of the range staged in LDS):
+// A workgroup = (row tile, KV head g, explicit KV split) with 8 waves of 32
+// rows (256 rows share each KV tile).  Per 64-token KV tile (double-buffered in
+// LDS and fetched two tiles ahead into registers, cooperatively, with the page
+// ids of the range staged in LDS):
 //   S^T = K Q^T on v_mfma_f32_32x32x16 (K from LDS as the A operand, Q^T from
-//   registers as the B operand); causal/length mask; online softmax (running
-//   max and sum per row, one lane-pair shuffle per reduction);
+//   registers as the B operand); causal/length mask on boundary tiles only;
+//   online softmax (running max and sum per row, one lane-pair shuffle per
+//   reduction; the reference max is re-based lazily);
 //   O^T += V^T P^T with V^T read from LDS by ds_read_b64_tr_b16 and P^T taken
 //   straight from the score registers.
-// Tiles past a tile's last visible position (causal) are skipped, and tiles of
-// late query positions — the heaviest under a causal mask — are dispatched first.
+// Tiles past a tile's last visible position (causal) are skipped; workgroups
+// are ordered so that every (KV head, split) group lives on one XCD (its KV
+// stays in that XCD's L2) and each XCD starts with its heaviest row tiles.
 #include "mfma_common.h"
 
 namespace pa {
 namespace {
 
-constexpr int kRows = 128;      // rows per workgroup
-constexpr int kKT = 64;         // KV tokens per tile
-constexpr int kPageWin = 1024;  // page ids staged in LDS at a time
+constexpr int kNW = 8;           // waves per workgroup
+constexpr int kRows = 32 * kNW;  // rows per workgroup (32 per wave)
+constexpr int kThreads = 64 * kNW;
+constexpr int kKT = 64;          // KV tokens per tile
+constexpr int kPageWin = 1024;   // page ids staged in LDS at a time
 
 template <int D>
 struct FGeo {
   static constexpr int KK = D / 16;            // 16-dim k-steps of Q.K
   static constexpr int NDT = D / 32;           // 32-dim tiles of O
   static constexpr int KP = D * 2 + 16;        // K row pitch (bytes): conflict-free b128 reads
-  static constexpr int VP = D * 2 + 32;        // V row pitch (bytes): spread transposed reads
+  static constexpr int VP = D * 2 + 64;        // V row pitch (bytes): a 32-lane transposed read
+                                               // pass (4 rows x 64 B) covers 64 distinct banks
   static constexpr int KBYTES = kKT * KP;
   static constexpr int VBYTES = kKT * VP;
   static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int CPR = D / 8;            // 16-byte chunks per row
-  static constexpr int LPT = kKT * CPR / 256;  // chunks per thread per tile (each of K, V)
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  static constexpr int LPT = kKT * CPR / kThreads;  // chunks per thread per tile (each of K, V)
+  static constexpr int TSTEP = kThreads / CPR;      // token stride between a thread's chunks
 };
 
-struct RowInfo {
-  int64_t t;  // query token (global), -1 if the row is padding
-  int h;      // query head
-  int lim;    // visible KV tokens are j < lim (causal position + 1, or L)
+// Per-thread view of the cooperative tile fetch over one page-id window.
+struct Fetch {
+  const uint16_t* kbase;
+  const uint16_t* vbase;
+  const int* s_pages;
+  int64_t ks0, ks1, kc, vs0, vs1, vc;  // kc / vc: KV-head plus 16-byte-chunk offsets
+  int tk0, P, pshift;
+  int wb, ws, we, nk;  // window's first page; its token range [ws, we); tiles in it
 };
 
-__device__ __forceinline__ int batch_of(const AttnParams& p, int t) { return batch_of_token(p, t); }
+// One tile's worth of this thread's K and V chunks (at most two of each: a
+// tile is 64 rows x D/8 chunks over 512 threads, D <= 128).  Named members, not
+// arrays, so the sets stay in VGPRs across the pipelined loop.
+struct TileRegs {
+  i16x8_t k0, k1, v0, v1;
+};
+
+template <int D, bool SAME>
+__device__ __forceinline__ void fetch_chunk(const Fetch& f, int jb, int u, i16x8_t& kr,
+                                            i16x8_t& vr) {
+  using Gm = FGeo<D>;
+  const int j = jb + f.tk0 + Gm::TSTEP * u;
+  const int jj = j < f.we ? j : f.we - 1;  // a valid token, never a poisoned slot
+  const int rel = jj - f.wb * f.P;
+  const int64_t page = f.s_pages[f.pshift >= 0 ? rel >> f.pshift : rel / f.P];
+  const int slot = f.pshift >= 0 ? (jj & (f.P - 1)) : jj % f.P;
+  const int64_t koff = page * f.ks0 + slot * f.ks1 + f.kc;
+  const int64_t voff = SAME ? koff : page * f.vs0 + slot * f.vs1 + f.vc;
+  kr = *reinterpret_cast<const i16x8_t*>(f.kbase + koff);
+  vr = *reinterpret_cast<const i16x8_t*>(f.vbase + voff);
+}
+
+template <int D, bool SAME>
+__device__ __forceinline__ void fetch_tile(const Fetch& f, int t, TileRegs& r) {
+  static_assert(FGeo<D>::LPT == 1 || FGeo<D>::LPT == 2, "tile fetch covers one or two chunks");
+  const int jb = f.ws + min(t, f.nk - 1) * kKT;  // clamped: fetches are unconditional
+  fetch_chunk<D, SAME>(f, jb, 0, r.k0, r.v0);
+  if constexpr (FGeo<D>::LPT == 2) fetch_chunk<D, SAME>(f, jb, 1, r.k1, r.v1);
+}
+
+// Rows past the range end hold a clamped valid token: finite, and their P is 0.
+template <int D>
+__device__ __forceinline__ void store_tile(uint8_t* stage, int tk0, int cc, const TileRegs& r) {
+  using Gm = FGeo<D>;
+  uint8_t* kl = stage + tk0 * Gm::KP + cc * 16;
+  uint8_t* vl = stage + Gm::KBYTES + tk0 * Gm::VP + cc * 16;
+  *reinterpret_cast<i16x8_t*>(kl) = r.k0;
+  *reinterpret_cast<i16x8_t*>(vl) = r.v0;
+  if constexpr (Gm::LPT == 2) {
+    *reinterpret_cast<i16x8_t*>(kl + Gm::TSTEP * Gm::KP) = r.k1;
+    *reinterpret_cast<i16x8_t*>(vl + Gm::TSTEP * Gm::VP) = r.v1;
+  }
+}
+
+struct RowState {
+  float m;         // reference max (log2 units, scaled); re-based lazily
+  float lsum;      // this lane's partial sum of exp2(s - m)
+  float true_max;  // running row max (m may lag it)
+};
+
+// One 64-token KV tile of math for this wave's 32 rows (lane: row l32, half h2).
+template <int DT, int D>
+__device__ __forceinline__ void tile_math(const uint8_t* stage, int jb, int lim, bool need_mask,
+                                          const i16x8_t (&qreg)[FGeo<D>::KK], float qk_scale,
+                                          RowState& st, f32x16_t (&oacc)[FGeo<D>::NDT],
+                                          int lane) {
+  using Gm = FGeo<D>;
+  constexpr int KK = Gm::KK, NDT = Gm::NDT;
+  const int l32 = lane & 31, h2 = lane >> 5;
+  const uint8_t* kl = stage;
+  const uint8_t* vl = stage + Gm::KBYTES;
+
+  // S^T[token][row] = K Q^T as two 32-token blocks
+  f32x16_t sacc[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[mb][i] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const uint4 a =
+          *reinterpret_cast<const uint4*>(kl + (32 * mb + l32) * Gm::KP + (16 * kk + 8 * h2) * 2);
+      sacc[mb] = mfma32<DT>(as_i16x8(a), qreg[kk], sacc[mb]);
+    }
+
+  // Lane holds row l32 for tokens jb + 32mb + 8(i/4) + 4h2 + i%4.  Scores stay
+  // unscaled; the scale is fused into the exponent's FMA.  The reference max is
+  // re-based only when the tile max exceeds it by more than 8 (log2 units):
+  // most tiles skip the O rescale, P <= 2^8 keeps 16-bit P and fp32 sums well
+  // in range, and LSE = m + log2(l) holds for any reference m.
+  if (need_mask) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = jb + 32 * mb + 8 * (i >> 2) + 4 * h2 + (i & 3);
+        sacc[mb][i] = j < lim ? sacc[mb][i] : -INFINITY;
+      }
+  }
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[mb][i]);
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * qk_scale;
+  st.true_max = fmaxf(st.true_max, tmax);
+  const bool grow = tmax > st.m + 8.f;
+  if (__ballot(grow)) {
+    const float mnew = grow ? tmax : st.m;
+    const float alpha =
+        fast_exp2((st.m == -INFINITY ? -INFINITY : st.m) - (mnew == -INFINITY ? 0.f : mnew));
+    const float a = grow ? alpha : 1.f;
+    st.lsum *= a;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) oacc[t] *= a;
+    st.m = mnew;
+  }
+  const float nmref = -(st.m == -INFINITY ? 0.f : st.m);
+  float psum = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float e = fast_exp2(fmaf(sacc[mb][i], qk_scale, nmref));
+      sacc[mb][i] = e;
+      psum += e;
+    }
+  st.lsum += psum;
+
+  // P^T B operands of the four 16-token PV steps
+  i16x8_t pb[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int mb = t >> 1, i0 = 8 * (t & 1);
+    const uint4 bits = make_uint4(pack2<DT>(sacc[mb][i0 + 0], sacc[mb][i0 + 1]),
+                                  pack2<DT>(sacc[mb][i0 + 2], sacc[mb][i0 + 3]),
+                                  pack2<DT>(sacc[mb][i0 + 4], sacc[mb][i0 + 5]),
+                                  pack2<DT>(sacc[mb][i0 + 6], sacc[mb][i0 + 7]));
+    pb[t] = as_i16x8(bits);
+  }
+  // O^T += V^T P^T, V^T by transposed LDS reads
+  const int l16 = lane & 15;
+  const uint16_t* vrow = reinterpret_cast<const uint16_t*>(vl + (4 * h2 + (l16 >> 2)) * Gm::VP) +
+                         16 * ((lane >> 4) & 1) + 4 * (l16 & 3);
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const uint16_t* ra = vrow + (16 * t) * (Gm::VP / 2) + 32 * dt;
+      const i16x4_t lo = lds_read_tr(ra);
+      const i16x4_t hi4 = lds_read_tr(ra + 8 * (Gm::VP / 2));
+      const i16x8_t va = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      oacc[dt] = mfma32<DT>(va, pb[t], oacc[dt]);
+    }
+}
 
 template <int DT, int D, bool SAME>
-__global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnParams p, int tiles_per_batch,
-                                                           int num_row_tiles) {
+__global__ __launch_bounds__(kThreads, 1) void flash_attn_kernel(AttnParams p, int tiles_per_batch,
+                                                                int num_row_tiles) {
   using Gm = FGeo<D>;
   constexpr int KK = Gm::KK, NDT = Gm::NDT;
   __shared__ __align__(16) uint8_t smem[2 * Gm::STAGE];
   __shared__ int s_pages[kPageWin];
-  __shared__ int s_red[8];
+  __shared__ int s_red[kNW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -68,8 +225,8 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnParams p, int ti
 
   // ---- which (row tile, KV head, split).  Workgroups are dealt round-robin to
   // the 8 XCDs; when the (head, split) groups divide evenly, every group lives on
-  // one XCD (its KV stays in that XCD's L2) and each XCD walks its row tiles
-  // from the latest (heaviest under a causal mask) to the earliest.
+  // one XCD and each XCD walks its row tiles from the latest (heaviest under a
+  // causal mask) to the earliest.
   const int HS = p.num_kv_heads * p.num_splits;
   const int lam = blockIdx.x;
   int rank, gc;
@@ -107,210 +264,129 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnParams p, int ti
   const int j1 = min((int)(((int64_t)(c + 1) * n / S) * p.page_size), L);
 
   // ---- this lane's row (B-operand column / C column): wave w rows 32w..32w+31
-  RowInfo ri;
+  int64_t row_t;  // query token (global), -1 for a padding row
+  int row_h;      // query head
+  int lim;        // visible KV tokens are j < lim
   {
     const int r = 32 * w + l32;
     const int64_t t = t_begin + r / G;
     const bool ok = (r / G) < TQ && t < t_end;
-    ri.t = ok ? t : -1;
-    ri.h = g * G + r % G;
-    int lim = j1;
+    row_t = ok ? t : -1;
+    row_h = g * G + r % G;
+    int l = j1;
     if (ok && p.causal) {
-      const int bb = p.broadcast ? batch_of(p, (int)t) : b;
+      const int bb = p.broadcast ? batch_of_token(p, (int)t) : b;
       const int q0 = p.qo_indptr ? p.qo_indptr[bb] : bb * p.q_len;
       const int qb = p.qo_indptr ? p.qo_indptr[bb + 1] - q0 : p.q_len;
-      lim = min(lim, L - qb + ((int)t - q0) + 1);
+      l = min(l, L - qb + ((int)t - q0) + 1);
     }
-    ri.lim = ok ? lim : INT_MIN;
+    lim = ok ? l : INT_MIN;
   }
   // workgroup-wide last visible token (tiles past it are skipped)
-  int hi = ri.lim;
+  int hi = lim;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) hi = max(hi, __shfl_xor(hi, off, 64));
   if (lane == 0) s_red[w] = hi;
   __syncthreads();
-  const int jhi = min(j1, max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3])));
+  int jmax = s_red[0];
+#pragma unroll
+  for (int i = 1; i < kNW; ++i) jmax = max(jmax, s_red[i]);
+  const int jhi = min(j1, jmax);
   // tiles ending at or before this wave's smallest row limit need no mask
-  int lo = ri.t >= 0 ? ri.lim : INT_MAX;
+  int lo = row_t >= 0 ? lim : INT_MAX;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) lo = min(lo, __shfl_xor(lo, off, 64));
   const int wave_lim_min = lo;
 
-  // ---- Q^T B operand: 8 x 16 B per lane, kept in registers
+  // ---- Q^T B operand: KK x 16 B per lane, kept in registers
   i16x8_t qreg[KK];
   {
     const uint16_t* qp = static_cast<const uint16_t*>(p.q) +
-                         ((ri.t < 0 ? 0 : ri.t) * p.num_qo_heads + ri.h) * (int64_t)D + 8 * h2;
+                         ((row_t < 0 ? 0 : row_t) * p.num_qo_heads + row_h) * (int64_t)D + 8 * h2;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const uint4 v = ri.t >= 0 ? *reinterpret_cast<const uint4*>(qp + 16 * kk) : make_uint4(0, 0, 0, 0);
+      const uint4 v =
+          row_t >= 0 ? *reinterpret_cast<const uint4*>(qp + 16 * kk) : make_uint4(0, 0, 0, 0);
       qreg[kk] = as_i16x8(v);
     }
   }
 
-  float m = -INFINITY, lsum = 0.f;
+  RowState st{-INFINITY, 0.f, -INFINITY};
   f32x16_t oacc[NDT];
 #pragma unroll
   for (int t = 0; t < NDT; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[t][i] = 0.f;
   const float qk_scale = p.sm_scale * p.k_scale * kLog2e;
-  const uint16_t* kbase = static_cast<const uint16_t*>(p.k);
-  const uint16_t* vbase = static_cast<const uint16_t*>(p.v);
-  const int P = p.page_size;
-  const int pshift = p.page_shift;
-  float true_max = -INFINITY;  // running row max (the lazily updated m may lag it)
 
-  // cooperative tile load: thread -> (chunk cc, tokens tk0 + 16u)
+  // cooperative fetch: thread -> (16-byte chunk cc, tokens tk0 + TSTEP*u)
   const int cc = tid % Gm::CPR;
-  const int tk0 = tid / Gm::CPR;
-  constexpr int TSTEP = 256 / Gm::CPR;
+  Fetch f;
+  f.kbase = static_cast<const uint16_t*>(p.k);
+  f.vbase = static_cast<const uint16_t*>(p.v);
+  f.s_pages = s_pages;
+  f.ks0 = p.ks0;
+  f.ks1 = p.ks1;
+  f.kc = (int64_t)g * p.ks2 + 8 * cc;
+  f.vs0 = p.vs0;
+  f.vs1 = p.vs1;
+  f.vc = (int64_t)g * p.vs2 + 8 * cc;
+  f.tk0 = tid / Gm::CPR;
+  f.P = p.page_size;
+  f.pshift = p.page_shift;
 
   if (jhi > j0) {
+    const int P = p.page_size;
     const int pfirst = j0 / P, plast = (jhi - 1) / P;
     for (int wb = pfirst; wb <= plast; wb += kPageWin) {
       const int npw = min(kPageWin, plast - wb + 1);
       __syncthreads();  // previous window's readers are done
-      for (int i = tid; i < npw; i += 256) s_pages[i] = p.kv_indices[pbeg + wb + i];
+      for (int i = tid; i < npw; i += kThreads) s_pages[i] = p.kv_indices[pbeg + wb + i];
       __syncthreads();
-      const int ws = max(j0, wb * P), we = min(jhi, (wb + npw) * P);
-      const int nk = (we - ws + kKT - 1) / kKT;
+      f.wb = wb;
+      f.ws = max(j0, wb * P);
+      f.we = min(jhi, (wb + npw) * P);
+      f.nk = (f.we - f.ws + kKT - 1) / kKT;
+      const int nk = f.nk;
 
-      uint4 kreg[Gm::LPT], vreg[Gm::LPT];
-      auto gload = [&](int jb) {
-#pragma unroll
-        for (int u = 0; u < Gm::LPT; ++u) {
-          const int j = jb + tk0 + TSTEP * u;
-          const int jj = j < we ? j : we - 1;  // clamp: a valid token, never a poisoned slot
-          const int rel = jj - wb * P;
-          const int64_t page = s_pages[pshift >= 0 ? rel >> pshift : rel / P];
-          const int slot = pshift >= 0 ? (jj & (P - 1)) : jj % P;
-          const int64_t koff = page * p.ks0 + slot * p.ks1 + (int64_t)g * p.ks2 + 8 * cc;
-          const int64_t voff = SAME ? koff : page * p.vs0 + slot * p.vs1 + (int64_t)g * p.vs2 + 8 * cc;
-          kreg[u] = *reinterpret_cast<const uint4*>(kbase + koff);
-          vreg[u] = *reinterpret_cast<const uint4*>(vbase + voff);
-        }
-      };
-      auto lstore = [&](int jb, int stage) {
-        uint8_t* kl = smem + stage * Gm::STAGE;
-        uint8_t* vl = kl + Gm::KBYTES;
-#pragma unroll
-        for (int u = 0; u < Gm::LPT; ++u) {
-          const int row = tk0 + TSTEP * u;
-          *reinterpret_cast<uint4*>(kl + row * Gm::KP + cc * 16) = kreg[u];
-          *reinterpret_cast<uint4*>(vl + row * Gm::VP + cc * 16) =
-              jb + row < we ? vreg[u] : make_uint4(0, 0, 0, 0);  // V rows past the end read as 0
-        }
-      };
-
-      gload(ws);
-      lstore(ws, 0);
+      // Two register sets carry tiles ahead of the math: tile t is fetched at the
+      // end of iteration t-3 and written to LDS stage t%2 at the end of iteration
+      // t-1.  Fetches are unconditional (tile index clamped to the last tile) so
+      // every path has the same loads in flight.  The loop is unrolled by two so
+      // each set is a fixed register set.
+      TileRegs rA, rB;
+      fetch_tile<D, SAME>(f, 0, rA);
+      fetch_tile<D, SAME>(f, 1, rB);
+      store_tile<D>(smem, f.tk0, cc, rA);
       __syncthreads();
-      for (int k = 0; k < nk; ++k) {
-        const int jb = ws + k * kKT;
-        const int stage = k & 1;
-        if (k + 1 < nk) gload(jb + kKT);
-        const uint8_t* kl = smem + stage * Gm::STAGE;
-        const uint8_t* vl = kl + Gm::KBYTES;
-
-        // S^T[token][row] = K Q^T: two 32-token blocks
-        f32x16_t sacc[2];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[mb][i] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            const uint4 a = *reinterpret_cast<const uint4*>(kl + (32 * mb + l32) * Gm::KP +
-                                                            (16 * kk + 8 * h2) * 2);
-            sacc[mb] = mfma32<DT>(as_i16x8(a), qreg[kk], sacc[mb]);
-          }
-
-        // mask (boundary tiles only), online softmax (lane: row l32, tokens
-        // 32mb + 8(i/4) + 4h2 + i%4).  Scores stay unscaled; the scale is fused
-        // into the exponent's FMA.  The reference max m is re-based only when
-        // the tile max exceeds it by more than 8 (log2 units), so most tiles skip
-        // the O rescale; P <= 2^8 keeps 16-bit P and fp32 sums exact enough, and
-        // LSE = m + log2(l) holds for any reference m.
-        if (jb + kKT > wave_lim_min) {
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int j = jb + 32 * mb + 8 * (i >> 2) + 4 * h2 + (i & 3);
-              sacc[mb][i] = j < ri.lim ? sacc[mb][i] : -INFINITY;
-            }
+      fetch_tile<D, SAME>(f, 2, rA);
+      for (int k = 0; k < nk; k += 2) {
+        {
+          const int jb = f.ws + k * kKT;
+          tile_math<DT, D>(smem, jb, lim, jb + kKT > wave_lim_min, qreg, qk_scale, st, oacc, lane);
         }
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[mb][i]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * qk_scale;
-        true_max = fmaxf(true_max, tmax);
-        const bool grow = tmax > m + 8.f;
-        if (__ballot(grow)) {
-          const float mnew = grow ? tmax : m;
-          const float alpha = fast_exp2((m == -INFINITY ? -INFINITY : m) -
-                                        (mnew == -INFINITY ? 0.f : mnew));
-          const float a = grow ? alpha : 1.f;
-          lsum *= a;
-#pragma unroll
-          for (int t = 0; t < NDT; ++t) oacc[t] *= a;
-          m = mnew;
-        }
-        const float nmref = -(m == -INFINITY ? 0.f : m);
-        float psum = 0.f;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float e = fast_exp2(fmaf(sacc[mb][i], qk_scale, nmref));
-            sacc[mb][i] = e;
-            psum += e;
-          }
-        lsum += psum;
-
-        // P^T operands of the four 16-token PV steps
-        i16x8_t pb[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int mb = t >> 1, i0 = 8 * (t & 1);
-          const uint4 bits = make_uint4(pack2<DT>(sacc[mb][i0 + 0], sacc[mb][i0 + 1]),
-                                        pack2<DT>(sacc[mb][i0 + 2], sacc[mb][i0 + 3]),
-                                        pack2<DT>(sacc[mb][i0 + 4], sacc[mb][i0 + 5]),
-                                        pack2<DT>(sacc[mb][i0 + 6], sacc[mb][i0 + 7]));
-          pb[t] = as_i16x8(bits);
-        }
-        // O^T += V^T P^T; V^T via transposed LDS reads
-        const int l16 = lane & 15;
-        const uint16_t* vrow = reinterpret_cast<const uint16_t*>(vl + (4 * h2 + (l16 >> 2)) * Gm::VP) +
-                               16 * ((lane >> 4) & 1) + 4 * (l16 & 3);
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const uint16_t* ra = vrow + (16 * t) * (Gm::VP / 2) + 32 * dt;
-            const i16x4_t lo = lds_read_tr(ra);
-            const i16x4_t hi4 = lds_read_tr(ra + 8 * (Gm::VP / 2));
-            const i16x8_t va = {lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-            oacc[dt] = mfma32<DT>(va, pb[t], oacc[dt]);
-          }
-
-        if (k + 1 < nk) lstore(jb + kKT, stage ^ 1);
+        if (k + 1 < nk) store_tile<D>(smem + Gm::STAGE, f.tk0, cc, rB);
         __syncthreads();
+        fetch_tile<D, SAME>(f, k + 3, rB);
+        if (k + 1 >= nk) break;
+        {
+          const int jb = f.ws + (k + 1) * kKT;
+          tile_math<DT, D>(smem + Gm::STAGE, jb, lim, jb + kKT > wave_lim_min, qreg, qk_scale, st,
+                           oacc, lane);
+        }
+        if (k + 2 < nk) store_tile<D>(smem, f.tk0, cc, rA);
+        __syncthreads();
+        fetch_tile<D, SAME>(f, k + 4, rA);
       }
     }
   }
 
   // ---- epilogue: lane (row l32, half h2) holds dims 32dt + 8q + 4h2 + (0..3)
-  const float ltot = lsum + __shfl_xor(lsum, 32, 64);
-  if (ri.t < 0) return;
+  const float ltot = st.lsum + __shfl_xor(st.lsum, 32, 64);
+  if (row_t < 0) return;
   const bool empty = !(ltot > 0.f);
   const float scale = empty ? 0.f : p.v_scale / ltot;
-  const int64_t rid = ri.t * p.num_qo_heads + ri.h;
+  const int64_t rid = row_t * p.num_qo_heads + row_h;
   const int64_t obase = c * p.o_split_stride + rid * D;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
@@ -331,8 +407,8 @@ __global__ __launch_bounds__(256, 2) void flash_attn_kernel(AttnParams p, int ti
     }
   if (h2 == 0) {
     const int64_t sidx = c * p.s_split_stride + rid;
-    if (p.lse) p.lse[sidx] = empty ? -INFINITY : (m + fast_log2(ltot)) * kLn2;
-    if (p.mx) p.mx[sidx] = empty ? -INFINITY : true_max * kLn2;
+    if (p.lse) p.lse[sidx] = empty ? -INFINITY : (st.m + fast_log2(ltot)) * kLn2;
+    if (p.mx) p.mx[sidx] = empty ? -INFINITY : st.true_max * kLn2;
   }
 }
 
@@ -349,9 +425,9 @@ hipError_t launch_fd(const AttnParams& p, bool same, hipStream_t stream) {
   if (num_row_tiles == 0) return hipSuccess;
   const dim3 grid(num_row_tiles * p.num_kv_heads * p.num_splits);
   if (same)
-    flash_attn_kernel<DT, D, true><<<grid, 256, 0, stream>>>(p, tiles_per_batch, num_row_tiles);
+    flash_attn_kernel<DT, D, true><<<grid, kThreads, 0, stream>>>(p, tiles_per_batch, num_row_tiles);
   else
-    flash_attn_kernel<DT, D, false><<<grid, 256, 0, stream>>>(p, tiles_per_batch, num_row_tiles);
+    flash_attn_kernel<DT, D, false><<<grid, kThreads, 0, stream>>>(p, tiles_per_batch, num_row_tiles);
   return hipGetLastError();
 }
 

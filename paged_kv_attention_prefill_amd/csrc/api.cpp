@@ -80,6 +80,9 @@ void fill_kv(AttnParams& p, const pa_paged_kv& kv) {
   p.page_shift = -1;
   for (int sh = 0; sh < 31; ++sh)
     if ((1 << sh) == kv.page_size) p.page_shift = sh;
+  p.page_magic = kv.page_size == 1
+                     ? 0u
+                     : (uint32_t)(((uint64_t(1) << 32) + kv.page_size - 1) / kv.page_size);
   p.dqk = kv.head_dim_qk;
   p.dvo = kv.head_dim_vo;
   p.k_scale = kv.k_scale;

@@ -54,9 +54,10 @@ struct Fetch {
   const uint16_t* kbase;
   const uint16_t* vbase;
   const int* s_pages;
-  int64_t ks0, ks1, kc, vs0, vs1, vc;  // kc / vc: KV-head plus 16-byte-chunk offsets
-  int tk0, P, pshift;
-  int wb, ws, we, nk;  // window's first page; its token range [ws, we); tiles in it
+  uint32_t ks0, ks1, kc, vs0, vs1, vc;  // kc / vc: KV-head plus 16-byte-chunk offsets
+  int tk0, P;
+  uint32_t pmagic;         // ceil(2^32 / P), or 0 for P == 1
+  int wbP, ws, we, nk;  // window's first token (page-aligned); its range [ws, we); tiles in it
 };
 
 // One tile's worth of this thread's K and V chunks (at most two of each: a
@@ -72,11 +73,15 @@ __device__ __forceinline__ void fetch_chunk(const Fetch& f, int jb, int u, i16x8
   using Gm = FGeo<D>;
   const int j = jb + f.tk0 + Gm::TSTEP * u;
   const int jj = j < f.we ? j : f.we - 1;  // a valid token, never a poisoned slot
-  const int rel = jj - f.wb * f.P;
-  const int64_t page = f.s_pages[f.pshift >= 0 ? rel >> f.pshift : rel / f.P];
-  const int slot = f.pshift >= 0 ? (jj & (f.P - 1)) : jj % f.P;
-  const int64_t koff = page * f.ks0 + slot * f.ks1 + f.kc;
-  const int64_t voff = SAME ? koff : page * f.vs0 + slot * f.vs1 + f.vc;
+  // page within the window and slot within the page, division-free: rel < 1024 P
+  // and P <= 2048 keep rel * P < 2^32, where the rounded-up reciprocal is exact
+  const uint32_t rel = jj - f.wbP;
+  const uint32_t pw = f.pmagic ? __umulhi(rel, f.pmagic) : rel;
+  const int slot = rel - pw * f.P;
+  const uint32_t page = f.s_pages[pw];
+  // 32x32->64-bit page offset plus a 32-bit offset within the page
+  const uint64_t koff = (uint64_t)page * f.ks0 + (slot * f.ks1 + f.kc);
+  const uint64_t voff = SAME ? koff : (uint64_t)page * f.vs0 + (slot * f.vs1 + f.vc);
   kr = *reinterpret_cast<const i16x8_t*>(f.kbase + koff);
   vr = *reinterpret_cast<const i16x8_t*>(f.vbase + voff);
 }
@@ -109,53 +114,64 @@ struct RowState {
   float true_max;  // running row max (m may lag it)
 };
 
-// One 64-token KV tile of math for this wave's 32 rows (lane: row l32, half h2).
-template <int DT, int D>
-__device__ __forceinline__ void tile_math(const uint8_t* stage, int jb, int lim, bool need_mask,
-                                          const i16x8_t (&qreg)[FGeo<D>::KK], float qk_scale,
-                                          RowState& st, f32x16_t (&oacc)[FGeo<D>::NDT],
-                                          int lane) {
-  using Gm = FGeo<D>;
-  constexpr int KK = Gm::KK, NDT = Gm::NDT;
-  const int l32 = lane & 31, h2 = lane >> 5;
-  const uint8_t* kl = stage;
-  const uint8_t* vl = stage + Gm::KBYTES;
+// max or sum of a lane's value and its partner's in the other 32-lane half
+__device__ __forceinline__ float half_swap_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
-  // S^T[token][row] = K Q^T as two 32-token blocks
-  f32x16_t sacc[2];
+// S^T[token][row] = K Q^T for one 64-token tile, as two 32-token blocks.  Lane
+// (row l32, half h2) holds tokens 32mb + 8(i/4) + 4h2 + i%4 of its row.
+template <int DT, int D>
+__device__ __forceinline__ void tile_qk(const uint8_t* stage, const i16x8_t (&qreg)[FGeo<D>::KK],
+                                        f32x16_t (&s)[2], int lane) {
+  using Gm = FGeo<D>;
+  const int l32 = lane & 31, h2 = lane >> 5;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sacc[mb][i] = 0.f;
+    for (int i = 0; i < 16; ++i) s[mb][i] = 0.f;
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk)
+  for (int kk = 0; kk < Gm::KK; ++kk)
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const uint4 a =
-          *reinterpret_cast<const uint4*>(kl + (32 * mb + l32) * Gm::KP + (16 * kk + 8 * h2) * 2);
-      sacc[mb] = mfma32<DT>(as_i16x8(a), qreg[kk], sacc[mb]);
+      const i16x8_t a = *reinterpret_cast<const i16x8_t*>(stage + (32 * mb + l32) * Gm::KP +
+                                                          (16 * kk + 8 * h2) * 2);
+      s[mb] = mfma32<DT>(a, qreg[kk], s[mb]);
     }
+}
 
-  // Lane holds row l32 for tokens jb + 32mb + 8(i/4) + 4h2 + i%4.  Scores stay
-  // unscaled; the scale is fused into the exponent's FMA.  The reference max is
-  // re-based only when the tile max exceeds it by more than 8 (log2 units):
-  // most tiles skip the O rescale, P <= 2^8 keeps 16-bit P and fp32 sums well
-  // in range, and LSE = m + log2(l) holds for any reference m.
-  if (need_mask) {
+// Tokens j >= lim of this lane's row get -inf (boundary tiles only).
+__device__ __forceinline__ void tile_mask(f32x16_t (&s)[2], int jb, int lim, int lane) {
+  const int h2 = lane >> 5;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = jb + 32 * mb + 8 * (i >> 2) + 4 * h2 + (i & 3);
-        sacc[mb][i] = j < lim ? sacc[mb][i] : -INFINITY;
-      }
-  }
+    for (int i = 0; i < 16; ++i) {
+      const int j = jb + 32 * mb + 8 * (i >> 2) + 4 * h2 + (i & 3);
+      s[mb][i] = j < lim ? s[mb][i] : -INFINITY;
+    }
+}
+
+// Running max over the tile.  Scores stay unscaled; the scale is fused into the
+// exponent's FMA.  The reference max is re-based only when the tile max exceeds
+// it by more than 8 (log2 units): most tiles skip the O rescale, P <= 2^8 keeps
+// 16-bit P and fp32 sums well in range, and LSE = m + log2(l) holds for any
+// reference m.
+// A tile that is not `valid` (past the range) leaves the state as it is.
+template <int NDT>
+__device__ __forceinline__ void tile_max(const f32x16_t (&s)[2], float qk_scale, RowState& st,
+                                         f32x16_t (&oacc)[NDT], bool valid) {
   float tmax = -INFINITY;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[mb][i]);
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * qk_scale;
+    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[mb][i]);
+  tmax = valid ? half_swap_max(tmax) * qk_scale : -INFINITY;
   st.true_max = fmaxf(st.true_max, tmax);
   const bool grow = tmax > st.m + 8.f;
   if (__ballot(grow)) {
@@ -168,37 +184,80 @@ __device__ __forceinline__ void tile_math(const uint8_t* stage, int jb, int lim,
     for (int t = 0; t < NDT; ++t) oacc[t] *= a;
     st.m = mnew;
   }
+}
+
+// S^T of the next tile (sn = K Q^T, as tile_qk) and, interleaved with its MFMAs,
+// P of the current tile: exp2(sc * scale - m) packed to 16-bit as the B operands
+// of the four 16-token PV steps (pb), the row sum accumulating in fp32.  Each
+// k-step issues the K reads of the next k-step, its two MFMAs and a share of the
+// exponentials, so the VALU work runs while the MFMAs execute.
+template <int DT, int D>
+__device__ __forceinline__ void tile_qk_exp(const uint8_t* stage,
+                                            const i16x8_t (&qreg)[FGeo<D>::KK],
+                                            f32x16_t (&sn)[2], const f32x16_t (&sc)[2],
+                                            float qk_scale, RowState& st, i16x8_t (&pb)[4],
+                                            int lane) {
+  using Gm = FGeo<D>;
+  constexpr int KK = Gm::KK;
+  constexpr int EPK = 32 / KK;  // exponentials per k-step
+  static_assert(EPK * KK == 32 && (EPK % 4) == 0, "k-steps split the 32 scores evenly");
+  const int l32 = lane & 31, h2 = lane >> 5;
+  const uint8_t* krow = stage + l32 * Gm::KP + 16 * h2;
   const float nmref = -(st.m == -INFINITY ? 0.f : st.m);
-  float psum = 0.f;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float e = fast_exp2(fmaf(sacc[mb][i], qk_scale, nmref));
-      sacc[mb][i] = e;
-      psum += e;
-    }
-  st.lsum += psum;
-
-  // P^T B operands of the four 16-token PV steps
-  i16x8_t pb[4];
+    for (int i = 0; i < 16; ++i) sn[mb][i] = 0.f;
+  float e[32];
+  float psum = 0.f;
+  i16x8_t a0 = *reinterpret_cast<const i16x8_t*>(krow);
+  i16x8_t a1 = *reinterpret_cast<const i16x8_t*>(krow + 32 * Gm::KP);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int mb = t >> 1, i0 = 8 * (t & 1);
-    const uint4 bits = make_uint4(pack2<DT>(sacc[mb][i0 + 0], sacc[mb][i0 + 1]),
-                                  pack2<DT>(sacc[mb][i0 + 2], sacc[mb][i0 + 3]),
-                                  pack2<DT>(sacc[mb][i0 + 4], sacc[mb][i0 + 5]),
-                                  pack2<DT>(sacc[mb][i0 + 6], sacc[mb][i0 + 7]));
-    pb[t] = as_i16x8(bits);
+  for (int kk = 0; kk < KK; ++kk) {
+    i16x8_t n0 = a0, n1 = a1;
+    if (kk + 1 < KK) {
+      n0 = *reinterpret_cast<const i16x8_t*>(krow + 32 * (kk + 1));
+      n1 = *reinterpret_cast<const i16x8_t*>(krow + 32 * Gm::KP + 32 * (kk + 1));
+    }
+    sn[0] = mfma32<DT>(a0, qreg[kk], sn[0]);
+    sn[1] = mfma32<DT>(a1, qreg[kk], sn[1]);
+#pragma unroll
+    for (int i = 0; i < EPK; ++i) {
+      const int idx = kk * EPK + i;
+      e[idx] = fast_exp2(fmaf(sc[idx >> 4][idx & 15], qk_scale, nmref));
+    }
+    if (((kk + 1) * EPK) % 8 == 0) {
+      const int t = (kk + 1) * EPK / 8 - 1;
+      const uint4 bits = make_uint4(pack2<DT>(e[8 * t + 0], e[8 * t + 1]),
+                                    pack2<DT>(e[8 * t + 2], e[8 * t + 3]),
+                                    pack2<DT>(e[8 * t + 4], e[8 * t + 5]),
+                                    pack2<DT>(e[8 * t + 6], e[8 * t + 7]));
+      pb[t] = as_i16x8(bits);
+      asm volatile("" : "+v"(pb[t]));  // computed here, not sunk past the mask branch
+      // the row sum is taken over the rounded P that the PV step multiplies
+      psum = sum2<DT>(bits.x, sum2<DT>(bits.y, sum2<DT>(bits.z, sum2<DT>(bits.w, psum))));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    a0 = n0;
+    a1 = n1;
   }
-  // O^T += V^T P^T, V^T by transposed LDS reads
-  const int l16 = lane & 15;
-  const uint16_t* vrow = reinterpret_cast<const uint16_t*>(vl + (4 * h2 + (l16 >> 2)) * Gm::VP) +
-                         16 * ((lane >> 4) & 1) + 4 * (l16 & 3);
+  asm volatile("" : "+v"(psum));
+  st.lsum += psum;
+}
+
+// O^T += V^T P^T, V^T by transposed LDS reads.
+template <int DT, int D>
+__device__ __forceinline__ void tile_pv(const uint8_t* stage, const i16x8_t (&pb)[4],
+                                        f32x16_t (&oacc)[FGeo<D>::NDT], int lane) {
+  using Gm = FGeo<D>;
+  const int l16 = lane & 15, h2 = lane >> 5;
+  const uint16_t* vrow =
+      reinterpret_cast<const uint16_t*>(stage + Gm::KBYTES + (4 * h2 + (l16 >> 2)) * Gm::VP) +
+      16 * ((lane >> 4) & 1) + 4 * (l16 & 3);
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
+    for (int dt = 0; dt < Gm::NDT; ++dt) {
       const uint16_t* ra = vrow + (16 * t) * (Gm::VP / 2) + 32 * dt;
       const i16x4_t lo = lds_read_tr(ra);
       const i16x4_t hi4 = lds_read_tr(ra + 8 * (Gm::VP / 2));
@@ -212,7 +271,7 @@ __global__ __launch_bounds__(kThreads, 1) void flash_attn_kernel(AttnParams p, i
                                                                 int num_row_tiles) {
   using Gm = FGeo<D>;
   constexpr int KK = Gm::KK, NDT = Gm::NDT;
-  __shared__ __align__(16) uint8_t smem[2 * Gm::STAGE];
+  __shared__ __align__(16) uint8_t smem[3 * Gm::STAGE];
   __shared__ int s_pages[kPageWin];
   __shared__ int s_red[kNW];
 
@@ -296,7 +355,7 @@ __global__ __launch_bounds__(kThreads, 1) void flash_attn_kernel(AttnParams p, i
   int lo = row_t >= 0 ? lim : INT_MAX;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) lo = min(lo, __shfl_xor(lo, off, 64));
-  const int wave_lim_min = lo;
+  const int wave_lim_min = __builtin_amdgcn_readfirstlane(lo);
 
   // ---- Q^T B operand: KK x 16 B per lane, kept in registers
   i16x8_t qreg[KK];
@@ -325,16 +384,17 @@ __global__ __launch_bounds__(kThreads, 1) void flash_attn_kernel(AttnParams p, i
   f.kbase = static_cast<const uint16_t*>(p.k);
   f.vbase = static_cast<const uint16_t*>(p.v);
   f.s_pages = s_pages;
-  f.ks0 = p.ks0;
-  f.ks1 = p.ks1;
-  f.kc = (int64_t)g * p.ks2 + 8 * cc;
-  f.vs0 = p.vs0;
-  f.vs1 = p.vs1;
-  f.vc = (int64_t)g * p.vs2 + 8 * cc;
+  f.ks0 = (uint32_t)p.ks0;
+  f.ks1 = (uint32_t)p.ks1;
+  f.kc = (uint32_t)(g * p.ks2 + 8 * cc);
+  f.vs0 = (uint32_t)p.vs0;
+  f.vs1 = (uint32_t)p.vs1;
+  f.vc = (uint32_t)(g * p.vs2 + 8 * cc);
   f.tk0 = tid / Gm::CPR;
   f.P = p.page_size;
-  f.pshift = p.page_shift;
+  f.pmagic = p.page_magic;
 
+  TileRegs rg;  // the tile in flight from HBM to LDS
   if (jhi > j0) {
     const int P = p.page_size;
     const int pfirst = j0 / P, plast = (jhi - 1) / P;
@@ -343,40 +403,52 @@ __global__ __launch_bounds__(kThreads, 1) void flash_attn_kernel(AttnParams p, i
       __syncthreads();  // previous window's readers are done
       for (int i = tid; i < npw; i += kThreads) s_pages[i] = p.kv_indices[pbeg + wb + i];
       __syncthreads();
-      f.wb = wb;
+      f.wbP = wb * P;
       f.ws = max(j0, wb * P);
       f.we = min(jhi, (wb + npw) * P);
       f.nk = (f.we - f.ws + kKT - 1) / kKT;
       const int nk = f.nk;
 
-      // Two register sets carry tiles ahead of the math: tile t is fetched at the
-      // end of iteration t-3 and written to LDS stage t%2 at the end of iteration
-      // t-1.  Fetches are unconditional (tile index clamped to the last tile) so
-      // every path has the same loads in flight.  The loop is unrolled by two so
-      // each set is a fixed register set.
-      TileRegs rA, rB;
-      fetch_tile<D, SAME>(f, 0, rA);
-      fetch_tile<D, SAME>(f, 1, rB);
-      store_tile<D>(smem, f.tk0, cc, rA);
+      // Software pipeline over three LDS stages (tile t in stage t % 3), one
+      // barrier per tile.  Iteration k issues the QK MFMAs of tile k+1 next to the
+      // exponentials of tile k, then the PV MFMAs of tile k next to the store of
+      // tile k+2 (fetched into registers one iteration earlier), the fetch of tile
+      // k+3 and the mask/max of tile k+1.  Fetches are unconditional (tile index
+      // clamped) so every path has the same loads in flight.
+      {
+        TileRegs r1;
+        fetch_tile<D, SAME>(f, 0, rg);
+        fetch_tile<D, SAME>(f, 1, r1);
+        store_tile<D>(smem, f.tk0, cc, rg);
+        store_tile<D>(smem + Gm::STAGE, f.tk0, cc, r1);
+      }
+      fetch_tile<D, SAME>(f, 2, rg);
       __syncthreads();
-      fetch_tile<D, SAME>(f, 2, rA);
+      f32x16_t sa[2], sb[2];
+      tile_qk<DT, D>(smem, qreg, sa, lane);
+      if (f.ws + kKT > wave_lim_min) tile_mask(sa, f.ws, lim, lane);
+      tile_max(sa, qk_scale, st, oacc, true);
+      int cur = 0, nxt = Gm::STAGE, nn = 2 * Gm::STAGE;  // stage offsets of tiles k, k+1, k+2
+      auto step = [&](int k, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) __attribute__((always_inline)) {
+        const bool more = k + 1 < nk;  // sn past the last tile is computed but unused
+        i16x8_t pb[4];
+        tile_qk_exp<DT, D>(smem + nxt, qreg, sn, sc, qk_scale, st, pb, lane);
+        const int jn = f.ws + (k + 1) * kKT;
+        if (more && jn + kKT > wave_lim_min) tile_mask(sn, jn, lim, lane);
+        tile_pv<DT, D>(smem + cur, pb, oacc, lane);
+        store_tile<D>(smem + nn, f.tk0, cc, rg);  // past the last tile: a stage nobody reads
+        fetch_tile<D, SAME>(f, k + 3, rg);
+        tile_max(sn, qk_scale, st, oacc, more);
+        __syncthreads();
+        const int t = cur;
+        cur = nxt;
+        nxt = nn;
+        nn = t;
+      };
       for (int k = 0; k < nk; k += 2) {
-        {
-          const int jb = f.ws + k * kKT;
-          tile_math<DT, D>(smem, jb, lim, jb + kKT > wave_lim_min, qreg, qk_scale, st, oacc, lane);
-        }
-        if (k + 1 < nk) store_tile<D>(smem + Gm::STAGE, f.tk0, cc, rB);
-        __syncthreads();
-        fetch_tile<D, SAME>(f, k + 3, rB);
+        step(k, sa, sb);
         if (k + 1 >= nk) break;
-        {
-          const int jb = f.ws + (k + 1) * kKT;
-          tile_math<DT, D>(smem + Gm::STAGE, jb, lim, jb + kKT > wave_lim_min, qreg, qk_scale, st,
-                           oacc, lane);
-        }
-        if (k + 2 < nk) store_tile<D>(smem, f.tk0, cc, rA);
-        __syncthreads();
-        fetch_tile<D, SAME>(f, k + 4, rA);
+        step(k + 1, sb, sa);
       }
     }
   }
@@ -434,8 +506,14 @@ hipError_t launch_fd(const AttnParams& p, bool same, hipStream_t stream) {
 }  // namespace
 
 bool flash_attn_supported(const AttnParams& p) {
+  // element offsets: page strides fit 32 bits and so does every offset within a page
+  const int64_t lim = int64_t(1) << 31;
+  const bool offsets32 =
+      p.ks0 < lim && p.vs0 < lim &&
+      (p.page_size - 1) * p.ks1 + (p.num_kv_heads - 1) * p.ks2 + p.dqk < lim &&
+      (p.page_size - 1) * p.vs1 + (p.num_kv_heads - 1) * p.vs2 + p.dvo < lim;
   return p.q_dtype == p.kv_dtype && (p.q_dtype == BF16 || p.q_dtype == F16) && p.dqk == p.dvo &&
-         (p.dqk == 64 || p.dqk == 128) && p.group <= kRows;
+         (p.dqk == 64 || p.dqk == 128) && p.group <= kRows && p.page_size <= 2048 && offsets32;
 }
 
 hipError_t launch_flash_attn(const AttnParams& p, bool same_strides, hipStream_t stream) {

@@ -62,9 +62,32 @@ __device__ __forceinline__ uint32_t to_bits16(float x) {
   }
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed 16-bit bits of DT (RNE), a in the low half: one
+// v_cvt_pk_{bf16,f16}_f32
 template <int DT>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return to_bits16<DT>(a) | (to_bits16<DT>(b) << 16);
+  const f32x2_t v = {a, b};
+  if constexpr (DT == BF16) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+  }
+}
+
+// acc + the two 16-bit values of DT packed in `bits` (v_dot2 against ones, fp32 sum)
+template <int DT>
+__device__ __forceinline__ float sum2(uint32_t bits, float acc) {
+  if constexpr (DT == BF16) {
+    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, bits), one, acc, false);
+  } else {
+    const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, bits), one, acc, false);
+  }
 }
 
 __device__ __forceinline__ i16x8_t as_i16x8(const uint4& u) { return __builtin_bit_cast(i16x8_t, u); }

@@ -20,6 +20,8 @@ struct AttnParams {
   int64_t ks0, ks1, ks2, vs0, vs1, vs2;
   int32_t page_size, dqk, dvo;
   int32_t page_shift;       // log2(page_size) if a power of two, else -1
+  uint32_t page_magic;      // ceil(2^32 / page_size) (page_size >= 2): n / page_size ==
+                            // umulhi(n, page_magic) for n * page_size < 2^32; 0 if page_size == 1
   float k_scale, v_scale, sm_scale;
   const int32_t* kv_indptr;
   const int32_t* kv_indices;

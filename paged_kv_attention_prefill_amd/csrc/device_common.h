@@ -79,6 +79,13 @@ __device__ __forceinline__ float wave_allreduce_max(float v) {
   return v;
 }
 
+// n / d given magic = ceil(2^32 / d) for d >= 2 (exact while n * d < 2^32), or
+// magic = 0 for d == 1; branch-free
+__device__ __forceinline__ uint32_t div_by_magic(uint32_t n, uint32_t magic) {
+  const uint32_t one = magic == 0 ? 0xFFFFFFFFu : 0u;
+  return __umulhi(n, magic) + (n & one);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

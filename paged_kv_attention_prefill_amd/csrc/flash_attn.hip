@@ -76,7 +76,7 @@ __device__ __forceinline__ void fetch_chunk(const Fetch& f, int jb, int u, i16x8
   // page within the window and slot within the page, division-free: rel < 1024 P
   // and P <= 2048 keep rel * P < 2^32, where the rounded-up reciprocal is exact
   const uint32_t rel = jj - f.wbP;
-  const uint32_t pw = f.pmagic ? __umulhi(rel, f.pmagic) : rel;
+  const uint32_t pw = div_by_magic(rel, f.pmagic);
   const int slot = rel - pw * f.P;
   const uint32_t page = f.s_pages[pw];
   // 32x32->64-bit page offset plus a 32-bit offset within the page
@@ -113,16 +113,6 @@ struct RowState {
   float lsum;      // this lane's partial sum of exp2(s - m)
   float true_max;  // running row max (m may lag it)
 };
-
-// max or sum of a lane's value and its partner's in the other 32-lane half
-__device__ __forceinline__ float half_swap_max(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float half_swap_sum(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // S^T[token][row] = K Q^T for one 64-token tile, as two 32-token blocks.  Lane
 // (row l32, half h2) holds tokens 32mb + 8(i/4) + 4h2 + i%4 of its row.
@@ -171,7 +161,7 @@ __device__ __forceinline__ void tile_max(const f32x16_t (&s)[2], float qk_scale,
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[mb][i]);
-  tmax = valid ? half_swap_max(tmax) * qk_scale : -INFINITY;
+  tmax = valid ? xor32_max(tmax) * qk_scale : -INFINITY;
   st.true_max = fmaxf(st.true_max, tmax);
   const bool grow = tmax > st.m + 8.f;
   if (__ballot(grow)) {
@@ -454,7 +444,7 @@ __global__ __launch_bounds__(kThreads, 1) void flash_attn_kernel(AttnParams p, i
   }
 
   // ---- epilogue: lane (row l32, half h2) holds dims 32dt + 8q + 4h2 + (0..3)
-  const float ltot = st.lsum + __shfl_xor(st.lsum, 32, 64);
+  const float ltot = xor32_sum(st.lsum);
   if (row_t < 0) return;
   const bool empty = !(ltot > 0.f);
   const float scale = empty ? 0.f : p.v_scale / ltot;

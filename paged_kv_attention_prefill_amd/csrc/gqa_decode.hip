@@ -4,27 +4,27 @@
 // one KV load to every row of the group).
 //
 // Per wave and 32-token tile (the streaming core, stream_range):
-//   page ids of a 64-page window sit in registers (lane i: page wbase+i) and
-//   are fetched per token with a lane shuffle, so no dependent table load sits
-//   between tiles;
-//   K: each lane loads 16 B (8 elements) of two token rows straight into the
-//   MFMA A-operand layout (token = lane%16 [+16], dims 32kk + 8*(lane/16));
-//   with equal K/V strides the V offset is the K offset (the SAME_KV_STRIDES
+//   K and V rows are fetched whole: 16-byte lanes cover consecutive 16-byte
+//   pieces of a token's head row, so one load instruction reads 64/(D/8) full
+//   rows (four 256-byte rows at D = 128).  On MI355X this shape streams HBM
+//   about 30% faster than loads laid out straight in the MFMA operand order
+//   (16 rows x 64 bytes per instruction).  The page of each lane's token comes
+//   from the range's page ids staged in LDS, and with equal K/V strides the V offset is the K offset (the SAME_KV_STRIDES
 //   specialisation of the FlashInfer PR #4736 analysis, code section 2);
-//   S^T[token][row] = K Q^T (Q^T is the B operand, loaded once); mask (KV end,
-//   causal position, rows beyond the group), scale, online softmax (running
-//   max m, running sum l, rescale by exp2(m_old - m_new)) with wavefront
-//   reductions across the four 16-lane groups;
-//   V rows go to the wave's LDS tile (invalid tokens as zeros) and come back
-//   transposed (ds_read_b64_tr_b16) as the A operand of O^T += V^T P^T; P^T is
-//   exactly the score registers converted to 16-bit (no shuffles).
+//   the rows pass through the wave's LDS tile: K comes back in the MFMA A
+//   layout for S^T[token][row] = K Q^T (Q^T is the B operand, loaded once), V
+//   comes back transposed (ds_read_b64_tr_b16) as the A operand of
+//   O^T += V^T P^T, P^T being the score registers converted to 16-bit;
+//   the wave's next tile's loads are issued as soon as this tile is in LDS, so
+//   they are in flight during this tile's math;
+//   mask (KV end, causal position, rows beyond the group), online softmax
+//   (running max m, running sum l, rescale by exp2(m_old - m_new)) with
+//   cross-lane reductions over the four 16-lane groups.
 //
 // A workgroup = (KV head, query batch, KV chunk or explicit split) with four
 // waves that take the range's tiles round-robin and merge their states in LDS
-// at the end — the in-workgroup split-and-merge of the SM110 XQA split kernel
-// (kernel-design section).  (Measured on MI355X: one wave per KV head with the
-// waves of a workgroup reading the same pages, and two tiles in flight per
-// wave, were both slower for the Llama-70B-like decode.)
+// at the end — the in-workgroup split-and-merge of the SM110 XQA
+// split kernel (kernel-design section).
 // Internal chunking cuts long KV batches into fixed-size chunks whose partial
 // states (O normalised by the chunk's own sum, LSE, max) go to the workspace for
 // the chunk-merge launch; explicit splits write the caller's partial states.
@@ -39,8 +39,12 @@ template <int D>
 struct Geo {
   static constexpr int KK = D / 32;          // 32-dim k-steps of Q.K
   static constexpr int NDT = D / 16;         // 16-dim tiles of O
-  static constexpr int ROWB = D * 2 + 32;    // LDS pitch of a V row (pad: conflict-free tr reads)
-  static constexpr int VBUF = kTile * ROWB;  // bytes of one wave's V tile
+  static constexpr int CPR = D / 8;          // 16-byte pieces per head row
+  static constexpr int RPI = 64 / CPR;       // rows per load instruction
+  static constexpr int NI = kTile / RPI;     // load instructions per tile (each of K, V)
+  static constexpr int KP = D * 2 + 16;      // LDS pitch of a K row (conflict-free operand reads)
+  static constexpr int VP = D * 2 + 32;      // LDS pitch of a V row (conflict-free tr reads)
+  static constexpr int VBUF = kTile * VP;    // bytes of one wave's tile buffer (K, then V)
 };
 
 // Token range of work item c of a KV batch with n pages / L tokens.
@@ -80,74 +84,101 @@ __device__ __forceinline__ void load_q(const AttnParams& p, int b, int g, int ro
   }
 }
 
-// Stream tiles k = tfirst, tfirst + tstep, ... of [j0, j1) for KV head g.  Each
-// wave has one 16 KB tile in flight; latency is hidden across the resident waves.
+constexpr int kPageWin = 1024;  // page ids staged in LDS at a time
+
+// Streams [j0, j1) of KV head g: the range's page ids go to LDS (s_pages) a
+// window at a time, and the window's 32-token tiles are dealt round-robin to the
+// nw waves, so the waves of a workgroup (and the workgroups of the other heads,
+// launched next to it) read neighbouring pages together.  Each wave's next tile
+// is in flight while its current one is computed; the tile buffer `buf` (LDS,
+// per wave) holds K, then V.  Called by every thread of the workgroup (barriers).
 template <int DT, int D, bool SAME>
 __device__ __forceinline__ void stream_range(const AttnParams& p, int g, int pbeg, int j0, int j1,
                                              int row_lim, const i16x8_t (&qreg)[Geo<D>::KK],
-                                             int tfirst, int tstep, uint8_t* vbuf, float& m,
+                                             int w, int nw, uint8_t* buf, int* s_pages, float& m,
                                              float& lsum, f32x4_t (&oacc)[Geo<D>::NDT]) {
-  constexpr int KK = Geo<D>::KK, NDT = Geo<D>::NDT, ROWB = Geo<D>::ROWB;
+  using Gm = Geo<D>;
+  constexpr int KK = Gm::KK, NDT = Gm::NDT, NI = Gm::NI, RPI = Gm::RPI;
   const int lane = threadIdx.x & 63;
   const int l16 = lane & 15, lg = lane >> 4;
+  const int rsub = lane / Gm::CPR;  // row of this lane within a load instruction
+  const int cch = lane % Gm::CPR;   // its 16-byte piece of the row
+  if (j1 <= j0) return;
   const int P = p.page_size;
+  const uint32_t pmagic = p.page_magic;
   const float qk_scale = p.sm_scale * p.k_scale * kLog2e;
   const uint16_t* kbase = static_cast<const uint16_t*>(p.k);
   const uint16_t* vbase = static_cast<const uint16_t*>(p.v);
-  if (j1 <= j0) return;
+  const uint32_t ks0 = (uint32_t)p.ks0, ks1 = (uint32_t)p.ks1;
+  const uint32_t vs0 = (uint32_t)p.vs0, vs1 = (uint32_t)p.vs1;
+  const uint32_t kc = (uint32_t)(g * p.ks2) + 8 * cch;
+  const uint32_t vc = (uint32_t)(g * p.vs2) + 8 * cch;
   const int pfirst = j0 / P, plast = (j1 - 1) / P;
-  for (int wbase = pfirst; wbase <= plast; wbase += 64) {
-    const int pid = wbase + lane <= plast ? p.kv_indices[pbeg + wbase + lane] : 0;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the window is in registers
-    const int ws_tok = max(j0, wbase * P);
-    const int we_tok = min(j1, (wbase + 64) * P);
-    const int kbeg = (ws_tok - j0 + kTile - 1) / kTile;
-    const int kend = (we_tok - j0 + kTile - 1) / kTile;
-    int tile = tfirst;
-    if (tile < kbeg) tile += (kbeg - tile + tstep - 1) / tstep * tstep;
-    for (; tile < kend; tile += tstep) {
-      const int jb = j0 + tile * kTile;
-      uint4 kr[2][KK], vr[2][KK];
+
+  for (int wb = pfirst; wb <= plast; wb += kPageWin) {
+    const int npw = min(kPageWin, plast - wb + 1);
+    __syncthreads();  // the previous window's readers are done
+    for (int i = threadIdx.x; i < npw; i += 64 * nw) s_pages[i] = p.kv_indices[pbeg + wb + i];
+    __syncthreads();
+    const int ws = max(j0, wb * P), we = min(j1, (wb + npw) * P);
+    const int nk = (we - ws + kTile - 1) / kTile;
+    const int lim = min(row_lim, we);
+    i16x8_t kr[NI], vr[NI];
+    // loads of window tile k (clamped to the last tile: every path issues them)
+    auto issue = [&](int k) __attribute__((always_inline)) {
+      const int jb = ws + min(k, nk - 1) * kTile;
+      uint64_t koff[NI], voff[NI];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int j = jb + 16 * st + l16;
-        const int jj = j < j1 ? j : j1 - 1;  // a valid token of this batch: no stray reads
-        const int64_t page = __shfl(pid, jj / P - wbase, 64);
-        const int slot = jj % P;
-        const int64_t koff = page * p.ks0 + slot * p.ks1 + (int64_t)g * p.ks2 + 8 * lg;
-        const int64_t voff = SAME ? koff : page * p.vs0 + slot * p.vs1 + (int64_t)g * p.vs2 + 8 * lg;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          kr[st][kk] = *reinterpret_cast<const uint4*>(kbase + koff + 32 * kk);
-          vr[st][kk] = *reinterpret_cast<const uint4*>(vbase + voff + 32 * kk);
-        }
+      for (int s = 0; s < NI; ++s) {
+        const int j = jb + s * RPI + rsub;
+        const uint32_t jj = (j < we ? j : we - 1) - wb * P;  // a valid token, window-relative
+        // page and slot, division-free (jj * P < 1024 P^2 <= 2^32)
+        const uint32_t pi = div_by_magic(jj, pmagic);
+        const uint32_t slot = jj - pi * P;
+        const uint32_t page = s_pages[pi];
+        koff[s] = (uint64_t)page * ks0 + (slot * ks1 + kc);
+        voff[s] = SAME ? koff[s] : (uint64_t)page * vs0 + (slot * vs1 + vc);
       }
+      // all K rows of the tile, then all V rows
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const bool ok = jb + 16 * st + l16 < j1;
+      for (int s = 0; s < NI; ++s) kr[s] = *reinterpret_cast<const i16x8_t*>(kbase + koff[s]);
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          *reinterpret_cast<uint4*>(vbuf + (16 * st + l16) * ROWB + (32 * kk + 8 * lg) * 2) =
-              ok ? vr[st][kk] : make_uint4(0, 0, 0, 0);
-      }
+      for (int s = 0; s < NI; ++s) vr[s] = *reinterpret_cast<const i16x8_t*>(vbase + voff[s]);
+    };
+    if (w < nk) issue(w);
+    for (int k = w; k < nk; k += nw) {
+      const int jb = ws + k * kTile;
+      // K rows -> LDS, back in the MFMA A layout (token l16 [+16], dims 32kk + 8lg)
+#pragma unroll
+      for (int s = 0; s < NI; ++s)
+        *reinterpret_cast<i16x8_t*>(buf + (s * RPI + rsub) * Gm::KP + cch * 16) = kr[s];
       f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-        for (int st = 0; st < 2; ++st) sacc[st] = mfma16<DT>(as_i16x8(kr[st][kk]), qreg[kk], sacc[st]);
+        for (int st = 0; st < 2; ++st) {
+          const i16x8_t a = *reinterpret_cast<const i16x8_t*>(buf + (16 * st + l16) * Gm::KP +
+                                                              (32 * kk + 8 * lg) * 2);
+          sacc[st] = mfma16<DT>(a, qreg[kk], sacc[st]);
+        }
+      // V rows -> the same buffer (the K reads above come first: one wave's LDS
+      // operations complete in order)
+#pragma unroll
+      for (int s = 0; s < NI; ++s)
+        *reinterpret_cast<i16x8_t*>(buf + (s * RPI + rsub) * Gm::VP + cch * 16) = vr[s];
+      issue(k + nw);  // registers are free: the next tile is in flight during the math
 
-      float s[2][4];
+      float sv[2][4];
       float tmax = -INFINITY;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = jb + 16 * st + 4 * lg + i;
-          s[st][i] = j < row_lim ? sacc[st][i] * qk_scale : -INFINITY;
-          tmax = fmaxf(tmax, s[st][i]);
+          sv[st][i] = j < lim ? sacc[st][i] * qk_scale : -INFINITY;
+          tmax = fmaxf(tmax, sv[st][i]);
         }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      tmax = xor32_max(xor16_max(tmax));
       const float mnew = fmaxf(m, tmax);
       const float mref = mnew == -INFINITY ? 0.f : mnew;
       const float alpha = fast_exp2(m - mref);
@@ -157,27 +188,26 @@ __device__ __forceinline__ void stream_range(const AttnParams& p, int g, int pbe
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pr[st][i] = fast_exp2(s[st][i] - mref);
+          pr[st][i] = fast_exp2(sv[st][i] - mref);
           psum += pr[st][i];
         }
       lsum = fmaf(lsum, alpha, psum);
       m = mnew;
 #pragma unroll
-      for (int t = 0; t < NDT; ++t) oacc[t] *= alpha;
+      for (int d = 0; d < NDT; ++d) oacc[d] *= alpha;
 
       const uint4 pbits = make_uint4(pack2<DT>(pr[0][0], pr[0][1]), pack2<DT>(pr[0][2], pr[0][3]),
                                      pack2<DT>(pr[1][0], pr[1][1]), pack2<DT>(pr[1][2], pr[1][3]));
       const i16x8_t pb = as_i16x8(pbits);
-      lds_wait();
-      const uint16_t* r0 = reinterpret_cast<const uint16_t*>(vbuf + (4 * lg + (l16 >> 2)) * ROWB) +
-                           4 * (l16 & 3);
-      const uint16_t* r1 = r0 + 16 * (ROWB / 2);
+      const uint16_t* r0 =
+          reinterpret_cast<const uint16_t*>(buf + (4 * lg + (l16 >> 2)) * Gm::VP) + 4 * (l16 & 3);
+      const uint16_t* r1 = r0 + 16 * (Gm::VP / 2);
 #pragma unroll
-      for (int t = 0; t < NDT; ++t) {
-        const i16x4_t lo = lds_read_tr(r0 + 16 * t);
-        const i16x4_t hi = lds_read_tr(r1 + 16 * t);
+      for (int d = 0; d < NDT; ++d) {
+        const i16x4_t lo = lds_read_tr(r0 + 16 * d);
+        const i16x4_t hi = lds_read_tr(r1 + 16 * d);
         const i16x8_t va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        oacc[t] = mfma16<DT>(va, pb, oacc[t]);
+        oacc[d] = mfma16<DT>(va, pb, oacc[d]);
       }
     }
   }
@@ -218,11 +248,12 @@ __device__ __forceinline__ void store_stats(const AttnParams& p, bool to_ws, int
 
 // ---------------------------------------------------------------- split kernel
 template <int DT, int D, bool SAME, int NW>
-__global__ __launch_bounds__(64 * NW) void gqa_decode_split_kernel(AttnParams p) {
+__global__ __launch_bounds__(64 * NW, (D > 128 ? 1 : 3)) void gqa_decode_split_kernel(AttnParams p) {
   constexpr int NDT = Geo<D>::NDT;
   constexpr int MERGE_BYTES = NW * 16 * D * 4 + NW * 16 * 2 * 4;
   constexpr int SMEM = (NW * Geo<D>::VBUF > MERGE_BYTES) ? NW * Geo<D>::VBUF : MERGE_BYTES;
   __shared__ __align__(16) uint8_t smem[SMEM];
+  __shared__ int s_pages[kPageWin];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
@@ -248,12 +279,11 @@ __global__ __launch_bounds__(64 * NW) void gqa_decode_split_kernel(AttnParams p)
   f32x4_t oacc[NDT];
 #pragma unroll
   for (int t = 0; t < NDT; ++t) oacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  stream_range<DT, D, SAME>(p, g, pbeg, j0, j1, row_lim, qreg, w, NW, smem + w * Geo<D>::VBUF, m,
-                            lsum, oacc);
+  stream_range<DT, D, SAME>(p, g, pbeg, j0, j1, row_lim, qreg, w, NW, smem + w * Geo<D>::VBUF,
+                            s_pages, m, lsum, oacc);
 
   // merge the waves' states in LDS
-  float ltot = lsum + __shfl_xor(lsum, 16, 64);
-  ltot += __shfl_xor(ltot, 32, 64);
+  const float ltot = xor32_sum(xor16_sum(lsum));
   __syncthreads();
   float* obuf = reinterpret_cast<float*>(smem);  // [NW][16][D]
   float* stat = obuf + NW * 16 * D;              // [NW][16][2]
@@ -318,9 +348,18 @@ hipError_t launch_dt(const AttnParams& p, bool same, hipStream_t stream) {
 }  // namespace
 
 bool gqa_decode_supported(const AttnParams& p) {
+  // element offsets: page strides fit 32 bits and so does every offset within a
+  // page; window-relative token indices (< 1024 pages) times the page size stay
+  // below 2^32 (division by the page size as a multiply with its rounded-up
+  // reciprocal)
+  const int64_t lim = int64_t(1) << 31;
+  const bool offsets32 =
+      p.ks0 < lim && p.vs0 < lim &&
+      (p.page_size - 1) * p.ks1 + (p.num_kv_heads - 1) * p.ks2 + p.dqk < lim &&
+      (p.page_size - 1) * p.vs1 + (p.num_kv_heads - 1) * p.vs2 + p.dvo < lim;
   return p.qo_indptr == nullptr && p.q_dtype == p.kv_dtype && (p.q_dtype == BF16 || p.q_dtype == F16) &&
          p.dqk == p.dvo && (p.dqk == 64 || p.dqk == 128 || p.dqk == 256) &&
-         p.q_len * p.group <= 16;
+         p.q_len * p.group <= 16 && offsets32 && p.page_size <= 2048;
 }
 
 hipError_t launch_gqa_decode(const AttnParams& p, bool same_strides, hipStream_t stream) {

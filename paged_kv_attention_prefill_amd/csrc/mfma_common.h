@@ -92,6 +92,28 @@ __device__ __forceinline__ float sum2(uint32_t bits, float acc) {
 
 __device__ __forceinline__ i16x8_t as_i16x8(const uint4& u) { return __builtin_bit_cast(i16x8_t, u); }
 
+// Reductions of a lane's value with that of lane l ^ 16 or l ^ 32 through the
+// gfx950 permlane swaps (VALU, no LDS): v_permlane16_swap exchanges the odd
+// 16-lane rows of its first operand with the even rows of its second, so with
+// both operands equal to v one result holds rows (0,0,2,2) and the other
+// (1,1,3,3); v_permlane32_swap does the same with the two 32-lane halves.
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ void lds_wait() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 }  // namespace pa

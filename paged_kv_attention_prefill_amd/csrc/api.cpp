@@ -212,7 +212,7 @@ int decode_chunk_tokens(const AttnParams& p, uint32_t flags) {
 int mla_chunk_tokens(const AttnParams& p, uint32_t flags) {
   if ((flags & PA_FLAG_NO_INTERNAL_SPLIT) || p.num_splits != 1 || p.max_kv_len <= 0) return 0;
   const int R = p.q_len * p.group;
-  const int rt = R <= 16 ? 16 : R <= 32 ? 32 : 64;
+  const int rt = pa::mla_rows_per_tile(p);
   const int64_t tiles = (int64_t)p.batch * p.num_kv_heads * ((R + rt - 1) / rt);
   int c = 8192;
   while (c > 512 && tiles * ((p.max_kv_len + c - 1) / c) < 1024) c /= 2;

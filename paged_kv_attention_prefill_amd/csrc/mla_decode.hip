@@ -359,6 +359,349 @@ __global__ __launch_bounds__(256, 1) void mla_decode_kernel(AttnParams p, int nr
   }
 }
 
+// ---------------------------------------------------------------------------
+// Many rows per request (q_len x H > 64, bf16 KV): the flash-attention shape.
+// A workgroup = (request, 128-row tile, KV chunk) with 8 waves of 16 rows each;
+// every wave keeps its rows' Q^T (16 x 576) in registers and its rows' whole
+// O^T (512 x 16, fp32) in accumulation registers, so a KV tile in LDS feeds all
+// 128 rows with no exchange between waves.  Per 32-token tile:
+//   the tile's rows go HBM -> LDS by direct-to-LDS loads (global_load_lds, 16
+//   bytes per lane, a wave instruction filling 1 KB of LDS), double-buffered so
+//   the next tile streams in during this tile's math;
+//   S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K from LDS as the A operand);
+//   online softmax with a lazily re-based running max (as in the prefill kernel);
+//   O^T += V^T P^T with V^T read transposed (ds_read_b64_tr_b16) from the same
+//   LDS rows (V is the first 512 dims of a row) and P^T straight from the
+//   score registers.
+constexpr int kNW2 = 8;                  // waves per workgroup
+constexpr int kRW = 16;                  // rows per wave
+constexpr int kRT2 = kNW2 * kRW;         // rows per workgroup
+constexpr int kTK2 = 32;                 // KV tokens per tile
+constexpr int kPieces = kDqk / 8;       // 16-byte pieces per latent row (72)
+constexpr int kKP2 = kPieces * 16;       // LDS row pitch (bytes), unpadded
+constexpr int kDma = kTK2 * kPieces / 64;  // 1-KB direct-load instructions per tile (36)
+constexpr int kStage2 = kDma * 1024;     // one tile in LDS
+static_assert(kTK2 * kPieces % 64 == 0, "a tile is a whole number of 1-KB wave loads");
+
+// LDS swizzle: piece p of row r sits at slot p ^ swz(r) of the row (the XOR stays
+// within p's aligned group of 8 pieces).  With the 1152-byte pitch, even rows
+// start at bank 0 and odd rows at bank 32; swz(r) = g(r/2 mod 8) with
+// g(x) = 2 (x mod 4) + x / 4 makes the 16-lane K operand reads (16 rows, one
+// piece) and the 32-lane transposed V reads (8 rows, a pair of pieces) hit 64
+// distinct banks.
+__device__ __forceinline__ int mla_swz(int r) {
+  const int x = (r >> 1) & 7;
+  return 2 * (x & 3) + (x >> 2);
+}
+
+// Direct HBM -> LDS load of tile rows [jb, jb + kTK2) (clamped into [.., we)):
+// instruction i of the tile fills LDS bytes [1024 i, 1024 i + 1024); lane l
+// fills slot 64 i + l = (row, slot q) with piece q ^ swz(row) of that row.
+__device__ __forceinline__ void dma_tile(const AttnParams& p, const int* s_pages, uint8_t* stage,
+                                         int jb, int we, int wbP, int g, int w, int lane) {
+  const uint16_t* kbase = static_cast<const uint16_t*>(p.k);
+  const uint32_t ks0 = (uint32_t)p.ks0, ks1 = (uint32_t)p.ks1;
+  const uint32_t kc = (uint32_t)(g * p.ks2);
+  // recomputed per call (cheap) rather than hoisted and held across the loop
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+#pragma unroll
+  for (int i0 = 0; i0 < kDma; i0 += kNW2) {
+    const int i = i0 + w;
+    const int slot = 64 * i + ln;
+    const int row = slot / kPieces, q = slot - row * kPieces;
+    const int piece = q ^ mla_swz(row);
+    const int j = jb + row;
+    const uint32_t jj = (j < we ? j : we - 1) - wbP;  // a valid token, window-relative
+    const uint32_t pi = div_by_magic(jj, p.page_magic);
+    const uint32_t pslot = jj - pi * (uint32_t)p.page_size;
+    const uint32_t page = s_pages[pi];
+    const uint64_t off = (uint64_t)page * ks0 + (pslot * ks1 + kc + 8 * piece);
+    if (i < kDma)
+      __builtin_amdgcn_global_load_lds(kbase + off, (PA_LDS void*)(stage + 1024 * i), 16, 0, 0);
+  }
+}
+
+struct MlaRow {
+  float m;         // reference max (log2 units, scaled); re-based lazily
+  float lsum;      // this lane's partial sum
+  float true_max;  // running row max
+};
+
+// One 32-token tile of math for this wave's 16 rows (lane: row l16, group lg).
+__device__ __forceinline__ void mla_rows_tile(const uint8_t* kv, int jb, int lim, bool need_mask,
+                                              const i16x8_t (&qreg)[kDqk / 32], float qk_scale,
+                                              MlaRow& st, f32x4_t (&oacc)[kDvo / 16], int lane) {
+  constexpr int KK = kDqk / 32, NDT = kDvo / 16;
+  int ln = lane;  // per-lane offsets recomputed per tile, not held across the loop
+  asm volatile("" : "+v"(ln));
+  const int l16 = ln & 15, lg = ln >> 4;
+  // S^T[token][row] = K Q^T: two 16-token blocks.  The 36 K operands (k-step
+  // kk, block st: f = 2 kk + st) are read kPF ahead of their MFMAs from a ring
+  // of registers; the scheduling barriers keep that order.
+  constexpr int kPF = 2;
+  f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  // K operand of k-step kk, block st: row 16 st + l16, piece 4 kk + lg, whose
+  // low three bits are 4 (kk % 2) + lg; swz(row) is the same for both blocks
+  const int sw = mla_swz(l16);
+  const int kq0 = l16 * kKP2 + 16 * (lg ^ sw);        // even k-steps (byte offsets)
+  const int kq1 = l16 * kKP2 + 16 * ((lg + 4) ^ sw);  // odd k-steps
+  auto kfrag = [&](int f) __attribute__((always_inline)) {
+    const int kk = f >> 1;
+    return *reinterpret_cast<const i16x8_t*>(kv + (kk & 1 ? kq1 : kq0) + 16 * (f & 1) * kKP2 +
+                                             128 * (kk >> 1));
+  };
+  i16x8_t ring[kPF];
+#pragma unroll
+  for (int f = 0; f < kPF; ++f) ring[f] = kfrag(f);
+#pragma unroll
+  for (int f = 0; f < 2 * KK; ++f) {
+    const i16x8_t a = ring[f % kPF];
+    if (f + kPF < 2 * KK) ring[f % kPF] = kfrag(f + kPF);
+    sacc[f & 1] = mfma16<BF16>(a, qreg[f >> 1], sacc[f & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // lane holds row l16, tokens jb + 16st + 4lg + i
+  float sv[2][4];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = jb + 16 * st2 + 4 * lg + i;
+      sv[st2][i] = (!need_mask || j < lim) ? sacc[st2][i] : -INFINITY;
+      tmax = fmaxf(tmax, sv[st2][i]);
+    }
+  tmax = xor32_max(xor16_max(tmax)) * qk_scale;
+  st.true_max = fmaxf(st.true_max, tmax);
+  // lazily re-based reference max: O is rescaled only when a row max grows by
+  // more than 2^8 (P <= 2^8 stays well inside bf16 and fp32 sums)
+  const bool grow = tmax > st.m + 8.f;
+  if (__ballot(grow)) {
+    const float mnew = grow ? tmax : st.m;
+    const float alpha =
+        fast_exp2((st.m == -INFINITY ? -INFINITY : st.m) - (mnew == -INFINITY ? 0.f : mnew));
+    const float a = grow ? alpha : 1.f;
+    st.lsum *= a;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) oacc[t] *= a;
+    st.m = mnew;
+  }
+  const float nmref = -(st.m == -INFINITY ? 0.f : st.m);
+  float e[8];
+#pragma unroll
+  for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e[4 * st2 + i] = fast_exp2(fmaf(sv[st2][i], qk_scale, nmref));
+  const uint4 bits = make_uint4(pack2<BF16>(e[0], e[1]), pack2<BF16>(e[2], e[3]),
+                                pack2<BF16>(e[4], e[5]), pack2<BF16>(e[6], e[7]));
+  const i16x8_t pb = as_i16x8(bits);
+  st.lsum = sum2<BF16>(bits.x, sum2<BF16>(bits.y, sum2<BF16>(bits.z, sum2<BF16>(bits.w, st.lsum))));
+  // O^T += V^T P^T: V^T 16 dims x (tokens 4lg..4lg+3, 16+4lg..16+4lg+3) by two
+  // transposed 4x16 reads, matching the token order of P^T above
+  // lane reads 4 dims (8 bytes) of row rr = 4 lg + l16/4 (and rr + 16, same
+  // swizzle): dims 16 d + 4 (l16 % 4) = piece 2 d + (l16 % 4) / 2, half l16 % 2;
+  // the piece's low three bits are 2 (d % 4) + (l16 % 4) / 2
+  const int rr = 4 * lg + (l16 >> 2);
+  const int vsw = mla_swz(rr);
+  const int vb = rr * kKP2 + 8 * (l16 & 1);
+  const int hp = (l16 & 3) >> 1;
+  const int vq[4] = {vb + 16 * ((0 + hp) ^ vsw), vb + 16 * ((2 + hp) ^ vsw),
+                     vb + 16 * ((4 + hp) ^ vsw), vb + 16 * ((6 + hp) ^ vsw)};
+  constexpr int kPV = 2;  // V^T operands in flight
+  i16x8_t vring[kPV];
+  auto vfrag = [&](int d) __attribute__((always_inline)) {
+    const uint16_t* a0 = reinterpret_cast<const uint16_t*>(kv + vq[d & 3] + 128 * (d >> 2));
+    const i16x4_t lo4 = lds_read_tr(a0);
+    const i16x4_t hi4 = lds_read_tr(a0 + 16 * (kKP2 / 2));
+    return i16x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+  };
+#pragma unroll
+  for (int d = 0; d < kPV; ++d) vring[d] = vfrag(d);
+#pragma unroll
+  for (int d = 0; d < NDT; ++d) {
+    const i16x8_t va = vring[d % kPV];
+    if (d + kPV < NDT) vring[d % kPV] = vfrag(d + kPV);
+    oacc[d] = mfma16<BF16>(va, pb, oacc[d]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+__global__ __launch_bounds__(64 * kNW2, 1) void mla_rows_kernel(AttnParams p, int nrt, int ngroups) {
+  constexpr int KK = kDqk / 32;   // 18 k-steps of Q.K (16x16x32)
+  constexpr int NDT = kDvo / 16;  // 32 16-dim tiles of O
+  // four stages (distinct LDS objects, so the compiler's wait counting tells
+  // the direct loads into one stage from the reads of another)
+  __shared__ __align__(16) uint8_t s_kv0[kStage2];
+  __shared__ __align__(16) uint8_t s_kv1[kStage2];
+  __shared__ __align__(16) uint8_t s_kv2[kStage2];
+  __shared__ __align__(16) uint8_t s_kv3[kStage2];
+  __shared__ int s_pages[kPageWinM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
+  const int l16 = lane & 15, lg = lane >> 4;
+
+  // ---- work item: (request b, KV head g, row tile rt, chunk c); the row tiles
+  // of one (b, g, c) share an XCD so the KV chunk is read once into its L2
+  const int lam = blockIdx.x;
+  const int xcd = lam % 8, k8 = lam / 8;
+  const int rt = k8 % nrt;
+  const int gi = (k8 / nrt) * 8 + xcd;
+  if (gi >= ngroups) return;
+  const int b = gi / (p.num_kv_heads * p.max_chunks);
+  const int g = (gi / p.max_chunks) % p.num_kv_heads;
+  const int c = gi % p.max_chunks;
+  const int kb = p.broadcast ? 0 : b;
+  const int pbeg = p.kv_indptr[kb];
+  const int n = p.kv_indptr[kb + 1] - pbeg;
+  const int L = n ? (n - 1) * p.page_size + p.kv_last[kb] : 0;
+  int j0, j1;
+  bool to_ws = false;
+  if (p.chunk_tokens > 0) {
+    const int nch = num_chunks(L, p.chunk_tokens, p.max_chunks);
+    if (c >= nch) return;
+    j0 = c * p.chunk_tokens;
+    j1 = (c == nch - 1) ? L : j0 + p.chunk_tokens;
+    to_ws = nch > 1;
+  } else {
+    if (c >= p.num_splits) return;
+    j0 = (int)(((int64_t)c * n / p.num_splits) * p.page_size);
+    j1 = min((int)(((int64_t)(c + 1) * n / p.num_splits) * p.page_size), L);
+  }
+  const int R = p.q_len * p.group;
+  const int row0 = rt * kRT2;
+
+  // ---- this lane's row (B-operand column / C column): wave w rows 16w..16w+15
+  const int row = row0 + kRW * w + l16;
+  const bool row_ok = row < R;
+  int lim = j1;
+  if (row_ok && p.causal) lim = min(lim, L - p.q_len + row / p.group + 1);
+  if (!row_ok) lim = INT_MIN;
+  int lo = row_ok ? lim : INT_MAX;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) lo = min(lo, __shfl_xor(lo, off, 64));
+  const int wave_lim_min = __builtin_amdgcn_readfirstlane(lo);
+  const bool wave_live = wave_lim_min != INT_MAX;  // the wave has a valid row
+  int jhi = j1;  // workgroup's last visible token
+  if (p.causal) jhi = min(j1, L - p.q_len + (min(row0 + kRT2, R) - 1) / p.group + 1);
+
+  i16x8_t qreg[KK];
+  {
+    const int qi = row_ok ? row / p.group : 0, qh = row_ok ? row % p.group : 0;
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) +
+                         ((int64_t)(b * p.q_len + qi) * p.num_qo_heads + (int64_t)g * p.group + qh) * kDqk +
+                         8 * lg;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qreg[kk] = row_ok ? *reinterpret_cast<const i16x8_t*>(qp + 32 * kk) : i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+
+  MlaRow st{-INFINITY, 0.f, -INFINITY};
+  f32x4_t oacc[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) oacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const float qk_scale = p.sm_scale * p.k_scale * kLog2e;
+  const int P = p.page_size;
+
+  if (jhi > j0) {
+    const int pfirst = j0 / P, plast = (jhi - 1) / P;
+    for (int wb = pfirst; wb <= plast; wb += kPageWinM) {
+      const int npw = min(kPageWinM, plast - wb + 1);
+      __syncthreads();  // the previous window's readers are done
+      for (int i = tid; i < npw; i += 64 * kNW2) s_pages[i] = p.kv_indices[pbeg + wb + i];
+      __syncthreads();
+      const int ws = max(j0, wb * P), we = min(jhi, (wb + npw) * P);
+      const int nk = (we - ws + kTK2 - 1) / kTK2;
+      // tile k lives in stage k % 4; tiles k+1..k+3 are in flight during the
+      // math of tile k.  A wave issues at least kMinDma direct loads per tile, so
+      // vmcnt(2 kMinDma) after issuing tile k+2 means tile k's loads are done;
+      // the barrier then covers every wave's loads, and every wave is done with
+      // tile k-1, whose stage takes tile k+3.
+      constexpr int kMinDma = kDma / kNW2;  // direct loads per wave per tile, at least
+      constexpr int kWait = 2 * kMinDma;     // vmcnt that leaves only tiles k+1, k+2 in flight
+      static_assert(kWait < 64, "vmcnt field");
+      constexpr int kWaitImm = (kWait & 0xF) | ((kWait >> 4) << 14) | 0x70 | 0xF00;
+      const int wbP = wb * P;
+      auto tile_at = [&](int k) { return ws + min(k, nk - 1) * kTK2; };
+      dma_tile(p, s_pages, s_kv0, tile_at(0), we, wbP, g, w, lane);
+      dma_tile(p, s_pages, s_kv1, tile_at(1), we, wbP, g, w, lane);
+      dma_tile(p, s_pages, s_kv2, tile_at(2), we, wbP, g, w, lane);
+#define PA_MLA_STEP(K, CUR, NEXT3)                                                            \
+  {                                                                                         \
+    __builtin_amdgcn_s_waitcnt(kWaitImm); /* tile K's direct loads are done */              \
+    __syncthreads();                                                                        \
+    dma_tile(p, s_pages, NEXT3, tile_at((K) + 3), we, wbP, g, w, lane);                     \
+    const int jb = ws + (K) * kTK2;                                                         \
+    if (wave_live)                                                                          \
+      mla_rows_tile(CUR, jb, lim, jb + kTK2 > wave_lim_min, qreg, qk_scale, st, oacc, lane); \
+  }
+      for (int k = 0; k < nk; k += 4) {
+        PA_MLA_STEP(k, s_kv0, s_kv3);
+        if (k + 1 >= nk) break;
+        PA_MLA_STEP(k + 1, s_kv1, s_kv0);
+        if (k + 2 >= nk) break;
+        PA_MLA_STEP(k + 2, s_kv2, s_kv1);
+        if (k + 3 >= nk) break;
+        PA_MLA_STEP(k + 3, s_kv3, s_kv2);
+      }
+#undef PA_MLA_STEP
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no loads in flight into the stages
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: lane (row l16, group lg) holds dims 16d + 4lg + (0..3)
+  const float ltot = xor32_sum(xor16_sum(st.lsum));
+  if (!row_ok) return;
+  const bool empty = !(ltot > 0.f);
+  const float scale = empty ? 0.f : p.v_scale / ltot;
+  const int64_t rid = (int64_t)(b * p.q_len + row / p.group) * p.num_qo_heads + (int64_t)g * p.group +
+                      row % p.group;
+  const int64_t wrow = ((int64_t)(b * p.num_kv_heads + g) * p.max_chunks + c) * p.ws_rows + row;
+#pragma unroll
+  for (int d = 0; d < NDT; ++d) {
+    const int dim = 16 * d + 4 * lg;
+    const float x0 = oacc[d][0] * scale, x1 = oacc[d][1] * scale;
+    const float x2 = oacc[d][2] * scale, x3 = oacc[d][3] * scale;
+    if (to_ws) {
+      *reinterpret_cast<float4*>(p.ws_o + wrow * kDvo + dim) = make_float4(x0, x1, x2, x3);
+    } else if (p.o_dtype == F32) {
+      *reinterpret_cast<float4*>(static_cast<float*>(p.o) + c * p.o_split_stride + rid * kDvo + dim) =
+          make_float4(x0, x1, x2, x3);
+    } else {
+      const uint2 v = p.o_dtype == F16 ? make_uint2(pack2<F16>(x0, x1), pack2<F16>(x2, x3))
+                                       : make_uint2(pack2<BF16>(x0, x1), pack2<BF16>(x2, x3));
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + c * p.o_split_stride + rid * kDvo + dim) = v;
+    }
+  }
+  if (lg == 0) {
+    const float lse = empty ? -INFINITY : (st.m + fast_log2(ltot)) * kLn2;
+    const float mx = empty ? -INFINITY : st.true_max * kLn2;
+    if (to_ws) {
+      p.ws_lse[wrow] = lse;
+      p.ws_mx[wrow] = mx;
+    } else {
+      const int64_t sidx = c * p.s_split_stride + rid;
+      if (p.lse) p.lse[sidx] = lse;
+      if (p.mx) p.mx[sidx] = mx;
+    }
+  }
+}
+
+hipError_t launch_rows(const AttnParams& p, hipStream_t stream) {
+  const int R = p.q_len * p.group;
+  const int nrt = (R + kRT2 - 1) / kRT2;
+  const int items = p.chunk_tokens > 0 ? p.max_chunks : p.num_splits;
+  AttnParams q = p;
+  if (p.chunk_tokens <= 0) q.max_chunks = items;
+  const int ngroups = p.batch * p.num_kv_heads * items;
+  const int blocks = nrt * 8 * ((ngroups + 7) / 8);
+  mla_rows_kernel<<<blocks, 64 * kNW2, 0, stream>>>(q, nrt, ngroups);
+  return hipGetLastError();
+}
+
 template <bool FP8, int RT>
 hipError_t launch_rt(const AttnParams& p, hipStream_t stream) {
   const int R = p.q_len * p.group;
@@ -376,12 +719,22 @@ hipError_t launch_rt(const AttnParams& p, hipStream_t stream) {
 template <bool FP8>
 hipError_t launch_f(const AttnParams& p, hipStream_t stream) {
   const int R = p.q_len * p.group;
+  if (!FP8 && mla_rows_path(p)) return launch_rows(p, stream);
   if (R <= 16) return launch_rt<FP8, 16>(p, stream);
   if (R <= 32) return launch_rt<FP8, 32>(p, stream);
   return launch_rt<FP8, 64>(p, stream);
 }
 
 }  // namespace
+
+bool mla_rows_path(const AttnParams& p) {
+  // the 128-row kernel divides tokens within a page-id window by the page size
+  // with a 32-bit reciprocal: window-relative tokens (< 256 pages) times the page
+  // size below 2^32
+  return p.kv_dtype == BF16 && p.q_len * p.group > 64 && p.page_size <= 4096 &&
+         p.ks0 < (int64_t(1) << 31) &&
+         (p.page_size - 1) * p.ks1 + (p.num_kv_heads - 1) * p.ks2 + kDqk < (int64_t(1) << 31);
+}
 
 bool mla_decode_supported(const AttnParams& p) {
   return p.qo_indptr == nullptr && p.q_dtype == BF16 && (p.kv_dtype == BF16 || p.kv_dtype == FP8) &&
@@ -391,6 +744,7 @@ bool mla_decode_supported(const AttnParams& p) {
 
 int mla_rows_per_tile(const AttnParams& p) {
   const int R = p.q_len * p.group;
+  if (mla_rows_path(p)) return kRT2;
   return R <= 16 ? 16 : R <= 32 ? 32 : 64;
 }
 

@@ -59,6 +59,8 @@ hipError_t launch_generic(const AttnParams& p, hipStream_t stream);
 bool gqa_decode_supported(const AttnParams& p);
 hipError_t launch_gqa_decode(const AttnParams& p, bool same_strides, hipStream_t stream);
 bool mla_decode_supported(const AttnParams& p);
+bool mla_rows_path(const AttnParams& p);
+int mla_rows_per_tile(const AttnParams& p);
 hipError_t launch_mla_decode(const AttnParams& p, hipStream_t stream);
 bool flash_attn_supported(const AttnParams& p);
 hipError_t launch_flash_attn(const AttnParams& p, bool same_strides, hipStream_t stream);

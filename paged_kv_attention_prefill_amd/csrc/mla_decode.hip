@@ -731,7 +731,7 @@ bool mla_rows_path(const AttnParams& p) {
   // the 128-row kernel divides tokens within a page-id window by the page size
   // with a 32-bit reciprocal: window-relative tokens (< 256 pages) times the page
   // size below 2^32
-  return p.kv_dtype == BF16 && p.q_len * p.group > 64 && p.page_size <= 4096 &&
+  return p.kv_dtype == BF16 && p.page_size <= 4096 &&
          p.ks0 < (int64_t(1) << 31) &&
          (p.page_size - 1) * p.ks1 + (p.num_kv_heads - 1) * p.ks2 + kDqk < (int64_t(1) << 31);
 }

@@ -209,6 +209,38 @@ def test_causal_rows_that_see_nothing():
     run_and_check(w2, "MLA fp8 empty causal rows")
 
 
+def mla_build(seed, heads, q_len, kv_lens, page_size, dt=W.DT_BF16, **kw):
+    rng = np.random.default_rng(seed)
+    return W.build(rng, seed, f"mla h{heads} q{q_len} p{page_size}", q_lens=[q_len] * len(kv_lens),
+                   kv_lens=kv_lens, num_qo_heads=heads, num_kv_heads=1, head_dim_qk=576,
+                   head_dim_vo=512, page_size=page_size, q_dtype=W.DT_BF16, kv_dtype=dt,
+                   shared_kv=True, causal=True, sm_scale=1.0 / np.sqrt(192.0), **kw)
+
+
+@pytest.mark.parametrize("heads,q_len,page_size", [(48, 3, 24), (16, 1, 1), (128, 2, 64), (40, 4, 7)])
+def test_mla_row_tiles_and_page_sizes(heads, q_len, page_size):
+    # q_len x H rows that fill row tiles partly (144 = 128 + 16, 160 = 128 + 32) or
+    # cross two tiles, page sizes that are not powers of two, one-token pages
+    label = f"MLA h{heads} q{q_len} page {page_size}"
+    print(label, flush=True)
+    w = mla_build(900 + heads + page_size, heads, q_len, [1, 45, 700, 1333, 64 * 5], page_size)
+    run_and_check(w, label)
+
+
+def test_mla_explicit_splits():
+    w = mla_build(991, 128, 1, [0, 5, 640, 999], 64)
+    d = R.upload(w)
+    S = 4
+    res = R.run(d, num_kv_splits=S)
+    torch.cuda.synchronize()
+    po, pl, pm = OR.attention(w, num_kv_splits=S)
+    for c in range(S):
+        check_rows(w, to64(res["po"][c]), to64(res["plse"][c]), po[c], pl[c],
+                   to64(res["pmx"][c]), pm[c], label=f"MLA partial {c}")
+    o, lse, _ = OR.attention(w, num_kv_splits=1)
+    check_rows(w, to64(res["o"]), to64(res["lse"]), o, lse, label="MLA merged")
+
+
 def test_output_dtypes():
     w = small("c2")
     d = R.upload(w)

@@ -180,6 +180,8 @@ struct Plan {
   int chunk_tokens = 0;       // internal KV chunking (0: none)
   int max_chunks = 0;
   int ws_rows = 16;           // workspace row slots per (batch, KV head, chunk)
+  int bal_blocks = 0;         // balanced split over this many workgroups (0: none)
+  int bal_unit = 0;           // its unit of work in KV tokens
   size_t workspace = 0;
   const char* name = "generic";
 };
@@ -204,6 +206,33 @@ int decode_chunk_tokens(const AttnParams& p, uint32_t flags) {
   c = (c + p.page_size - 1) / p.page_size * p.page_size;
   if (p.max_kv_len <= c) return 0;
   return c;
+}
+
+// Compute units of the current device (MI355X: 256), cached per device.
+int device_cus() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (cache[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// Workspace of a balanced split: partial states in slots item + workgroup, then
+// the first/last workgroup of every item.
+size_t balanced_workspace(const AttnParams& p, int blocks, int ws_rows) {
+  const int64_t items = (int64_t)p.batch * p.num_kv_heads;
+  const size_t rows = (size_t)pa::bal_slots(items, blocks) * ws_rows;
+  return align256(rows * p.dvo * 4) + 2 * align256(rows * 4) + align256((size_t)items * 8);
 }
 
 // Chunk size for the MLA decode: the largest power of two (512..8192 tokens,
@@ -232,18 +261,35 @@ Plan make_plan(const AttnParams& p, uint32_t flags) {
     pl.kind = Plan::GQA_DECODE;
     pl.same_strides = same;
     pl.name = same ? "gqa_decode_mfma_same_strides" : "gqa_decode_mfma";
-    pl.chunk_tokens = decode_chunk_tokens(p, flags);
-    if (pl.chunk_tokens > 0) {
-      pl.max_chunks = (p.max_kv_len + pl.chunk_tokens - 1) / pl.chunk_tokens;
-      const size_t rows = (size_t)p.batch * p.num_kv_heads * pl.max_chunks * 16;
-      pl.workspace = align256(rows * p.dvo * 4) + 2 * align256(rows * 4);
+    // KV long enough to be worth splitting: a balanced split over one wave of
+    // co-resident workgroups (every workgroup streams the same number of
+    // 32-token tiles, so none idles at the end)
+    if (decode_chunk_tokens(p, flags) > 0) {
+      static int occ[2][3][2] = {};
+      int& o = occ[p.q_dtype == PA_BF16][p.dqk == 64 ? 0 : p.dqk == 128 ? 1 : 2][same];
+      if (o <= 0) o = pa::gqa_decode_blocks_per_cu(p, same);
+      pl.bal_unit = 32;
+      pl.bal_blocks = o * device_cus();
+      pl.workspace = balanced_workspace(p, pl.bal_blocks, 16);
     }
     return pl;
   }
   if (pa::mla_decode_supported(p)) {
     pl.kind = Plan::MLA_DECODE;
     pl.name = p.kv_dtype == PA_FP8_E4M3 ? "mla_decode_mfma_fp8" : "mla_decode_mfma";
-    pl.chunk_tokens = mla_chunk_tokens(p, flags);
+    const int ct = mla_chunk_tokens(p, flags);
+    if (ct > 0 && pa::mla_balanced_ok(p)) {
+      // one row tile per request: balanced split over one wave of workgroups
+      static int occ[2][2] = {};
+      int& o = occ[p.kv_dtype == PA_FP8_E4M3][p.q_len * p.group <= 16];
+      if (o <= 0) o = pa::mla_blocks_per_cu(p);
+      pl.bal_unit = 32;
+      pl.bal_blocks = o * device_cus();
+      pl.ws_rows = p.q_len * p.group;
+      pl.workspace = balanced_workspace(p, pl.bal_blocks, pl.ws_rows);
+      return pl;
+    }
+    pl.chunk_tokens = ct;
     if (pl.chunk_tokens > 0) {
       pl.max_chunks = (p.max_kv_len + pl.chunk_tokens - 1) / pl.chunk_tokens;
       pl.ws_rows = p.q_len * p.group;
@@ -267,13 +313,23 @@ int run_plan(const Plan& pl, AttnParams p, void* ws, size_t ws_bytes, void* cons
   if (log_enabled())
     std::fprintf(stderr,
                  "[paged_attn] kernel=%s total_q=%d Hq=%d Hkv=%d dqk=%d dvo=%d splits=%d "
-                 "chunk=%d x%d ws=%zu\n",
+                 "chunk=%d x%d balanced=%d x%d ws=%zu\n",
                  pl.name, p.total_q, p.num_qo_heads, p.num_kv_heads, p.dqk, p.dvo, p.num_splits,
-                 pl.chunk_tokens, pl.max_chunks, pl.workspace);
+                 pl.chunk_tokens, pl.max_chunks, pl.bal_blocks, pl.bal_unit, pl.workspace);
   p.chunk_tokens = pl.chunk_tokens;
   p.max_chunks = pl.max_chunks;
   p.ws_rows = pl.ws_rows;
-  if (pl.chunk_tokens > 0) {
+  p.bal_blocks = pl.bal_blocks;
+  p.bal_unit = pl.bal_unit;
+  if (pl.bal_blocks > 0) {
+    const int64_t items = (int64_t)p.batch * p.num_kv_heads;
+    const size_t rows = (size_t)pa::bal_slots(items, pl.bal_blocks) * pl.ws_rows;
+    char* w = static_cast<char*>(ws);
+    p.ws_o = reinterpret_cast<float*>(w);
+    p.ws_lse = reinterpret_cast<float*>(w + align256(rows * p.dvo * 4));
+    p.ws_mx = reinterpret_cast<float*>(w + align256(rows * p.dvo * 4) + align256(rows * 4));
+    p.ws_seg = reinterpret_cast<int32_t*>(w + align256(rows * p.dvo * 4) + 2 * align256(rows * 4));
+  } else if (pl.chunk_tokens > 0) {
     const size_t rows = (size_t)p.batch * p.num_kv_heads * pl.max_chunks * pl.ws_rows;
     char* w = static_cast<char*>(ws);
     p.ws_o = reinterpret_cast<float*>(w);
@@ -301,7 +357,7 @@ int run_plan(const Plan& pl, AttnParams p, void* ws, size_t ws_bytes, void* cons
   if (e != hipSuccess) return PA_ERR_HIP;
   if (timed && hipEventRecord(static_cast<hipEvent_t>(events[1]), stream) != hipSuccess)
     return PA_ERR_HIP;
-  if (pl.chunk_tokens > 0) e = pa::launch_chunk_merge(p, stream);
+  if (pl.chunk_tokens > 0 || pl.bal_blocks > 0) e = pa::launch_chunk_merge(p, stream);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

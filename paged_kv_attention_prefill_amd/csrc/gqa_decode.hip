@@ -28,6 +28,7 @@
 // Internal chunking cuts long KV batches into fixed-size chunks whose partial
 // states (O normalised by the chunk's own sum, LSE, max) go to the workspace for
 // the chunk-merge launch; explicit splits write the caller's partial states.
+#include "balance.h"
 #include "mfma_common.h"
 
 namespace pa {
@@ -247,26 +248,20 @@ __device__ __forceinline__ void store_stats(const AttnParams& p, bool to_ws, int
 }
 
 // ---------------------------------------------------------------- split kernel
+// One (query batch b, KV head g) token range [j0, j1): the waves stream it and
+// merge their states in LDS; the result goes to the final O / LSE (split index
+// c_out) or, for a partial range, to workspace slot wslot.  Called by every
+// thread of the workgroup.
 template <int DT, int D, bool SAME, int NW>
-__global__ __launch_bounds__(64 * NW, (D > 128 ? 1 : 3)) void gqa_decode_split_kernel(AttnParams p) {
+__device__ __forceinline__ void decode_range(const AttnParams& p, int b, int g, int L, int j0, int j1,
+                                             bool to_ws, int64_t wslot, int c_out, uint8_t* smem,
+                                             int* s_pages) {
   constexpr int NDT = Geo<D>::NDT;
-  constexpr int MERGE_BYTES = NW * 16 * D * 4 + NW * 16 * 2 * 4;
-  constexpr int SMEM = (NW * Geo<D>::VBUF > MERGE_BYTES) ? NW * Geo<D>::VBUF : MERGE_BYTES;
-  __shared__ __align__(16) uint8_t smem[SMEM];
-  __shared__ int s_pages[kPageWin];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int g = blockIdx.x;
-  const int b = blockIdx.y;
-  const int c = blockIdx.z;
   const int kb = p.broadcast ? 0 : b;
   const int pbeg = p.kv_indptr[kb];
-  const int n = p.kv_indptr[kb + 1] - pbeg;
-  const int L = n ? (n - 1) * p.page_size + p.kv_last[kb] : 0;
-  int j0, j1;
-  bool to_ws;
-  if (!item_range(p, c, n, L, j0, j1, to_ws)) return;
 
   const int R = p.q_len * p.group;
   i16x8_t qreg[Geo<D>::KK];
@@ -302,34 +297,68 @@ __global__ __launch_bounds__(64 * NW, (D > 128 ? 1 : 3)) void gqa_decode_split_k
   static_assert(EPT >= 4 && (EPT % 4) == 0, "merge mapping");
   const int orow = threadIdx.x / TPR;
   const int d0 = (threadIdx.x % TPR) * EPT;
-  if (orow >= R) return;
-  float M = -INFINITY;
+  if (orow < R) {
+    float M = -INFINITY;
 #pragma unroll
-  for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, stat[(ww * 16 + orow) * 2]);
-  const float Mref = M == -INFINITY ? 0.f : M;
-  float Lt = 0.f;
-  float acc[EPT];
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, stat[(ww * 16 + orow) * 2]);
+    const float Mref = M == -INFINITY ? 0.f : M;
+    float Lt = 0.f;
+    float acc[EPT];
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
+    for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
 #pragma unroll
-  for (int ww = 0; ww < NW; ++ww) {
-    const float cw = fast_exp2(stat[(ww * 16 + orow) * 2] - Mref);
-    Lt = fmaf(cw, stat[(ww * 16 + orow) * 2 + 1], Lt);
+    for (int ww = 0; ww < NW; ++ww) {
+      const float cw = fast_exp2(stat[(ww * 16 + orow) * 2] - Mref);
+      Lt = fmaf(cw, stat[(ww * 16 + orow) * 2 + 1], Lt);
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) acc[e] = fmaf(cw, obuf[(ww * 16 + orow) * D + d0 + e], acc[e]);
+      for (int e = 0; e < EPT; ++e) acc[e] = fmaf(cw, obuf[(ww * 16 + orow) * D + d0 + e], acc[e]);
+    }
+    const float scale = Lt > 0.f ? p.v_scale / Lt : 0.f;
+    const int oi = orow / p.group, oh = orow % p.group;
+    const int64_t rid = (int64_t)(b * p.q_len + oi) * p.num_qo_heads + (int64_t)g * p.group + oh;
+    const int64_t ws_row = wslot * 16 + orow;
+    store_row<EPT>(p, to_ws, (to_ws ? ws_row * D : c_out * p.o_split_stride + rid * D) + d0, acc, scale);
+    if (d0 == 0) store_stats(p, to_ws, ws_row, c_out * p.s_split_stride + rid, M, Lt);
   }
-  const float scale = Lt > 0.f ? p.v_scale / Lt : 0.f;
-  const int oi = orow / p.group, oh = orow % p.group;
-  const int64_t rid = (int64_t)(b * p.q_len + oi) * p.num_qo_heads + (int64_t)g * p.group + oh;
-  const int64_t ws_row = ((int64_t)(b * p.num_kv_heads + g) * p.max_chunks + c) * 16 + orow;
-  store_row<EPT>(p, to_ws, (to_ws ? ws_row * D : c * p.o_split_stride + rid * D) + d0, acc, scale);
-  if (d0 == 0) store_stats(p, to_ws, ws_row, c * p.s_split_stride + rid, M, Lt);
+}
+
+// Workgroups: (KV head, query batch, chunk or explicit split) on a 3-D grid, or,
+// under the balanced split, a 1-D grid whose workgroups walk their share of the
+// (batch, KV head, 32-token unit) sequence.
+template <int DT, int D, bool SAME, int NW>
+__global__ __launch_bounds__(64 * NW, (D > 128 ? 1 : 3)) void gqa_decode_split_kernel(AttnParams p) {
+  constexpr int MERGE_BYTES = NW * 16 * D * 4 + NW * 16 * 2 * 4;
+  constexpr int SMEM = (NW * Geo<D>::VBUF > MERGE_BYTES) ? NW * Geo<D>::VBUF : MERGE_BYTES;
+  __shared__ __align__(16) uint8_t smem[SMEM];
+  __shared__ int s_pages[kPageWin];
+  if (p.bal_blocks > 0) {
+    BalCursor cur;
+    if (!cur.start(p, blockIdx.x)) return;
+    do {
+      decode_range<DT, D, SAME, NW>(p, cur.b, cur.g, cur.L, cur.j0(p), cur.j1(p), !cur.whole(),
+                                    cur.slot(p), 0, smem, s_pages);
+    } while (cur.next(p));
+    return;
+  }
+  const int g = blockIdx.x;
+  const int b = blockIdx.y;
+  const int c = blockIdx.z;
+  const int kb = p.broadcast ? 0 : b;
+  const int n = p.kv_indptr[kb + 1] - p.kv_indptr[kb];
+  const int L = n ? (n - 1) * p.page_size + p.kv_last[kb] : 0;
+  int j0, j1;
+  bool to_ws;
+  if (!item_range(p, c, n, L, j0, j1, to_ws)) return;
+  decode_range<DT, D, SAME, NW>(p, b, g, L, j0, j1, to_ws,
+                                (int64_t)(b * p.num_kv_heads + g) * p.max_chunks + c, c, smem, s_pages);
 }
 
 template <int DT, int D>
 hipError_t launch_d(const AttnParams& p, bool same, hipStream_t stream) {
   constexpr int NW = 4;
-  const dim3 grid(p.num_kv_heads, p.batch, p.chunk_tokens > 0 ? p.max_chunks : p.num_splits);
+  const dim3 grid = p.bal_blocks > 0
+                        ? dim3(p.bal_blocks)
+                        : dim3(p.num_kv_heads, p.batch, p.chunk_tokens > 0 ? p.max_chunks : p.num_splits);
   if (same)
     gqa_decode_split_kernel<DT, D, true, NW><<<grid, 64 * NW, 0, stream>>>(p);
   else
@@ -360,6 +389,32 @@ bool gqa_decode_supported(const AttnParams& p) {
   return p.qo_indptr == nullptr && p.q_dtype == p.kv_dtype && (p.q_dtype == BF16 || p.q_dtype == F16) &&
          p.dqk == p.dvo && (p.dqk == 64 || p.dqk == 128 || p.dqk == 256) &&
          p.q_len * p.group <= 16 && offsets32 && p.page_size <= 2048;
+}
+
+namespace {
+template <int DT, int D>
+const void* decode_kernel_ptr(bool same) {
+  if (same) return reinterpret_cast<const void*>(&gqa_decode_split_kernel<DT, D, true, 4>);
+  return reinterpret_cast<const void*>(&gqa_decode_split_kernel<DT, D, false, 4>);
+}
+}  // namespace
+
+int gqa_decode_blocks_per_cu(const AttnParams& p, bool same_strides) {
+  const void* f = nullptr;
+  if (p.q_dtype == BF16)
+    f = p.dqk == 64 ? decode_kernel_ptr<BF16, 64>(same_strides)
+        : p.dqk == 128 ? decode_kernel_ptr<BF16, 128>(same_strides)
+                       : decode_kernel_ptr<BF16, 256>(same_strides);
+  else
+    f = p.dqk == 64 ? decode_kernel_ptr<F16, 64>(same_strides)
+        : p.dqk == 128 ? decode_kernel_ptr<F16, 128>(same_strides)
+                       : decode_kernel_ptr<F16, 256>(same_strides);
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 256, 0) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = p.dqk > 128 ? 1 : 3;  // the kernel's launch bounds
+  }
+  return n;
 }
 
 hipError_t launch_gqa_decode(const AttnParams& p, bool same_strides, hipStream_t stream) {

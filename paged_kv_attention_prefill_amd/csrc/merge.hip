@@ -112,9 +112,10 @@ hipError_t launch_vt(const void* v, const float* s, int S, int64_t rows, int D, 
   return hipGetLastError();
 }
 
-// Merge of internal KV chunks (the same LSE formula): one group of D/4 lanes per
-// folded row (b, KV head g, row r < q_len*G); rows whose KV batch has a single
-// chunk were written directly by the attention kernel and are skipped here.
+// Merge of internal KV chunks or balanced-split segments (the same LSE formula):
+// one group of D/4 lanes per folded row (b, KV head g, row r < q_len*G); rows
+// whose item was done in one piece were written directly by the attention kernel
+// and are skipped here.
 __global__ __launch_bounds__(256) void chunk_merge_kernel(AttnParams p, int tpr) {
   const int rpb = blockDim.x / tpr;
   const int64_t rho = (int64_t)blockIdx.x * rpb + threadIdx.x / tpr;
@@ -127,13 +128,24 @@ __global__ __launch_bounds__(256) void chunk_merge_kernel(AttnParams p, int tpr)
   const int g = (int)((rho / WR) % p.num_kv_heads);
   const int b = (int)(rho / ((int64_t)WR * p.num_kv_heads));
   if (r >= R) return;
-  const int kb = p.broadcast ? 0 : b;
-  const int n = p.kv_indptr[kb + 1] - p.kv_indptr[kb];
-  const int L = n ? (n - 1) * p.page_size + p.kv_last[kb] : 0;
-  const int nch = num_chunks(L, p.chunk_tokens, p.max_chunks);
+  const int item = b * p.num_kv_heads + g;
+  int nch;
+  int64_t wrow0;
+  if (p.bal_blocks > 0) {
+    // balanced split: the item's partial states sit in slots item + i for its
+    // workgroups i = first..last
+    const int i0 = p.ws_seg[2 * item], i1 = p.ws_seg[2 * item + 1];
+    nch = i1 - i0 + 1;
+    wrow0 = ((int64_t)item + i0) * WR + r;
+  } else {
+    const int kb = p.broadcast ? 0 : b;
+    const int n = p.kv_indptr[kb + 1] - p.kv_indptr[kb];
+    const int L = n ? (n - 1) * p.page_size + p.kv_last[kb] : 0;
+    nch = num_chunks(L, p.chunk_tokens, p.max_chunks);
+    wrow0 = (int64_t)item * p.max_chunks * WR + r;
+  }
   if (nch <= 1) return;
   const int D = p.dvo;
-  const int64_t wrow0 = (int64_t)(b * p.num_kv_heads + g) * p.max_chunks * WR + r;
   const int d0 = li * 4;
   // loads are issued in unrolled blocks of 8 chunks so their latencies overlap
   constexpr int BLK = 8;

@@ -20,6 +20,7 @@
 //     row-major from LDS.
 // Chunks of long KV batches leave partial states (O normalised by the chunk's
 // own sum, LSE, max) in the workspace for the chunk-merge launch.
+#include "balance.h"
 #include "mfma_common.h"
 
 namespace pa {
@@ -475,6 +476,28 @@ __device__ __forceinline__ void convert_tile(const uint8_t* src, uint8_t* dst, i
   }
 }
 
+// Token range of work item c (internal chunk or explicit split) of request b;
+// false if the item does not exist.
+__device__ __forceinline__ bool mla_item_range(const AttnParams& p, int b, int c, int& L, int& j0, int& j1,
+                                               bool& to_ws) {
+  const int kb = p.broadcast ? 0 : b;
+  const int n = p.kv_indptr[kb + 1] - p.kv_indptr[kb];
+  L = n ? (n - 1) * p.page_size + p.kv_last[kb] : 0;
+  to_ws = false;
+  if (p.chunk_tokens > 0) {
+    const int nch = num_chunks(L, p.chunk_tokens, p.max_chunks);
+    if (c >= nch) return false;
+    j0 = c * p.chunk_tokens;
+    j1 = (c == nch - 1) ? L : j0 + p.chunk_tokens;
+    to_ws = nch > 1;
+  } else {
+    if (c >= p.num_splits) return false;
+    j0 = (int)(((int64_t)c * n / p.num_splits) * p.page_size);
+    j1 = min((int)(((int64_t)(c + 1) * n / p.num_splits) * p.page_size), L);
+  }
+  return true;
+}
+
 struct MlaRow {
   float m;         // reference max (log2 units, scaled); re-based lazily
   float lsum;      // this lane's partial sum
@@ -580,52 +603,27 @@ __device__ __forceinline__ void mla_rows_tile(const uint8_t* kv, int jb, int lim
   }
 }
 
+// One (request b, KV head g, row tile from row0) token range [j0, j1) of the
+// many-rows kernel; output as for the narrow kernel.  Called by every thread.
 template <bool FP8>
-__global__ __launch_bounds__(64 * kNW2, 1) void mla_rows_kernel(AttnParams p, int nrt, int ngroups) {
+__device__ __forceinline__ void mla_rows_range(const AttnParams& p, int b, int g, int rt, int L, int j0,
+                                               int j1, bool to_ws, int64_t wslot, int c, uint8_t* s_kv0,
+                                               uint8_t* s_kv1, uint8_t* s_kv2, uint8_t* s_kv3,
+                                               uint8_t* s_wide, int* s_pages) {
   constexpr int KK = kDqk / 32;   // 18 k-steps of Q.K (16x16x32)
   constexpr int NDT = kDvo / 16;  // 32 16-dim tiles of O
-  // four stages (distinct LDS objects, so the compiler's wait counting tells
-  // the direct loads into one stage from the reads of another)
-  constexpr int STAGE = FP8 ? kStage8 : kStage2;
-  __shared__ __align__(16) uint8_t s_kv0[STAGE];
-  __shared__ __align__(16) uint8_t s_kv1[STAGE];
-  __shared__ __align__(16) uint8_t s_kv2[STAGE];
-  __shared__ __align__(16) uint8_t s_kv3[STAGE];
-  __shared__ __align__(16) uint8_t s_wide[FP8 ? kStage2 : 16];  // fp8: the widened tile
-  __shared__ int s_pages[kPageWinM];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
   const int l16 = lane & 15, lg = lane >> 4;
-
-  // ---- work item: (request b, KV head g, row tile rt, chunk c); the row tiles
-  // of one (b, g, c) share an XCD so the KV chunk is read once into its L2
-  const int lam = blockIdx.x;
-  const int xcd = lam % 8, k8 = lam / 8;
-  const int rt = k8 % nrt;
-  const int gi = (k8 / nrt) * 8 + xcd;
-  if (gi >= ngroups) return;
-  const int b = gi / (p.num_kv_heads * p.max_chunks);
-  const int g = (gi / p.max_chunks) % p.num_kv_heads;
-  const int c = gi % p.max_chunks;
+  // the range is the workgroup's: scalar registers
+  b = uni(b);
+  g = uni(g);
+  L = uni(L);
+  j0 = uni(j0);
+  j1 = uni(j1);
   const int kb = p.broadcast ? 0 : b;
   const int pbeg = p.kv_indptr[kb];
-  const int n = p.kv_indptr[kb + 1] - pbeg;
-  const int L = n ? (n - 1) * p.page_size + p.kv_last[kb] : 0;
-  int j0, j1;
-  bool to_ws = false;
-  if (p.chunk_tokens > 0) {
-    const int nch = num_chunks(L, p.chunk_tokens, p.max_chunks);
-    if (c >= nch) return;
-    j0 = c * p.chunk_tokens;
-    j1 = (c == nch - 1) ? L : j0 + p.chunk_tokens;
-    to_ws = nch > 1;
-  } else {
-    if (c >= p.num_splits) return;
-    j0 = (int)(((int64_t)c * n / p.num_splits) * p.page_size);
-    j1 = min((int)(((int64_t)(c + 1) * n / p.num_splits) * p.page_size), L);
-  }
   const int R = p.q_len * p.group;
   const int row0 = rt * kRT2;
 
@@ -729,7 +727,7 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_rows_kernel(AttnParams p, in
   const float scale = empty ? 0.f : p.v_scale / ltot;
   const int64_t rid = (int64_t)(b * p.q_len + row / p.group) * p.num_qo_heads + (int64_t)g * p.group +
                       row % p.group;
-  const int64_t wrow = ((int64_t)(b * p.num_kv_heads + g) * p.max_chunks + c) * p.ws_rows + row;
+  const int64_t wrow = wslot * p.ws_rows + row;
 #pragma unroll
   for (int d = 0; d < NDT; ++d) {
     const int dim = 16 * d + 4 * lg;
@@ -760,6 +758,300 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_rows_kernel(AttnParams p, in
   }
 }
 
+// Workgroups: (request, KV head, row tile, chunk or explicit split) items, the
+// row tiles of one item on one XCD so its KV chunk is read once into that L2;
+// or, under the balanced split (one row tile), equal shares of the (request,
+// KV head, 32-token unit) sequence.
+template <bool FP8>
+__global__ __launch_bounds__(64 * kNW2, 1) void mla_rows_kernel(AttnParams p, int nrt, int ngroups) {
+  // four stages (distinct LDS objects, so the compiler's wait counting tells
+  // the direct loads into one stage from the reads of another)
+  constexpr int STAGE = FP8 ? kStage8 : kStage2;
+  __shared__ __align__(16) uint8_t s_kv0[STAGE];
+  __shared__ __align__(16) uint8_t s_kv1[STAGE];
+  __shared__ __align__(16) uint8_t s_kv2[STAGE];
+  __shared__ __align__(16) uint8_t s_kv3[STAGE];
+  __shared__ __align__(16) uint8_t s_wide[FP8 ? kStage2 : 16];  // fp8: the widened tile
+  __shared__ int s_pages[kPageWinM];
+  if (p.bal_blocks > 0) {
+    BalCursor cur;
+    if (!cur.start(p, blockIdx.x)) return;
+    do {
+      mla_rows_range<FP8>(p, cur.b, cur.g, 0, cur.L, cur.j0(p), cur.j1(p), !cur.whole(), cur.slot(p), 0,
+                          s_kv0, s_kv1, s_kv2, s_kv3, s_wide, s_pages);
+    } while (cur.next(p));
+    return;
+  }
+  const int lam = blockIdx.x;
+  const int xcd = lam % 8, k8 = lam / 8;
+  const int rt = k8 % nrt;
+  const int gi = (k8 / nrt) * 8 + xcd;
+  if (gi >= ngroups) return;
+  const int b = gi / (p.num_kv_heads * p.max_chunks);
+  const int g = (gi / p.max_chunks) % p.num_kv_heads;
+  const int c = gi % p.max_chunks;
+  int L, j0, j1;
+  bool to_ws;
+  if (!mla_item_range(p, b, c, L, j0, j1, to_ws)) return;
+  mla_rows_range<FP8>(p, b, g, rt, L, j0, j1, to_ws, (int64_t)(b * p.num_kv_heads + g) * p.max_chunks + c,
+                      c, s_kv0, s_kv1, s_kv2, s_kv3, s_wide, s_pages);
+}
+
+// ---------------------------------------------------------------------------
+// Up to 16 rows per request (q_len x H <= 16): one row block is too little MFMA
+// work for one wave to keep up with HBM, so the tile is shared out by dims.
+// Per 32-token tile (three LDS stages fed by direct loads, as above):
+//   S^T = K Q^T is split over the 576 dims: waves 0..5 each take three 32-dim
+//   k-steps (one 16x16x32 MFMA per k-step and 16-token block) and leave their
+//   partial scores in LDS; after a barrier every wave adds the six partials for
+//   all 16 rows x 32 tokens and runs the same online softmax (identical state in
+//   every wave);
+//   O^T += V^T P^T is split over the 512 V dims: wave w owns dims [64w, 64w+64).
+constexpr int kNS = kDqk / 32 / 3;  // waves that compute partial scores (6)
+
+// One (request b, KV head g) token range [j0, j1) of the narrow kernel; the
+// result goes to the final O / LSE (split c_out) or to workspace slot wslot.
+// Called by every thread of the workgroup.
+template <bool FP8>
+__device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int g, int L, int j0, int j1,
+                                                 bool to_ws, int64_t wslot, int c, uint8_t* s_kv0,
+                                                 uint8_t* s_kv1, uint8_t* s_kv2, uint8_t* s_wide,
+                                                 f32x4_t (*s_part)[2][64], int* s_pages) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int kb = p.broadcast ? 0 : b;
+  const int pbeg = p.kv_indptr[kb];
+  const int R = p.q_len * p.group;
+  const int row = l16;  // every wave covers the same 16 rows
+  const bool row_ok = row < R;
+  int lim = j1;
+  if (row_ok && p.causal) lim = min(lim, L - p.q_len + row / p.group + 1);
+  if (!row_ok) lim = INT_MIN;
+  int lo = row_ok ? lim : INT_MAX;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) lo = min(lo, __shfl_xor(lo, off, 64));
+  const int wave_lim_min = __builtin_amdgcn_readfirstlane(lo);
+  int jhi = j1;
+  if (p.causal) jhi = min(j1, L - p.q_len + (R - 1) / p.group + 1);
+
+  // Q^T operands of this wave's three k-steps (waves 0..5)
+  i16x8_t qreg[3];
+  {
+    const int qi = row_ok ? row / p.group : 0, qh = row_ok ? row % p.group : 0;
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) +
+                         ((int64_t)(b * p.q_len + qi) * p.num_qo_heads + (int64_t)g * p.group + qh) * kDqk +
+                         8 * lg;
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+      qreg[u] = row_ok && w < kNS ? *reinterpret_cast<const i16x8_t*>(qp + 32 * (3 * w + u))
+                                  : i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+
+  float m = -INFINITY, lsum = 0.f, true_max = -INFINITY;
+  f32x4_t oacc[4];  // dims 64w + 16d + 4lg + i, row l16
+#pragma unroll
+  for (int d = 0; d < 4; ++d) oacc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const float qk_scale = p.sm_scale * p.k_scale * kLog2e;
+  const int P = p.page_size;
+
+  // one tile from a stage (bf16 swizzled layout)
+  auto tile = [&](const uint8_t* kv, int jb) __attribute__((always_inline)) {
+    if (w < kNS) {
+      f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+      const int sw = mla_swz(l16);  // rows l16 and 16 + l16 share the swizzle
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const int kk = 3 * w + u;
+        const int piece = 4 * kk + lg;
+        const int q = (piece & ~7) | ((piece & 7) ^ sw);
+#pragma unroll
+        for (int st2 = 0; st2 < 2; ++st2) {
+          const i16x8_t a = *reinterpret_cast<const i16x8_t*>(kv + (16 * st2 + l16) * kKP2 + 16 * q);
+          sacc[st2] = mfma16<BF16>(a, qreg[u], sacc[st2]);
+        }
+      }
+      s_part[w][0][lane] = sacc[0];
+      s_part[w][1][lane] = sacc[1];
+    }
+    __syncthreads();
+    f32x4_t ssum[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int v = 0; v < kNS; ++v) {
+      ssum[0] += s_part[v][0][lane];
+      ssum[1] += s_part[v][1][lane];
+    }
+    // lane holds row l16, tokens jb + 16st + 4lg + i
+    const bool need_mask = jb + kTK2 > wave_lim_min;
+    float sv[2][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = jb + 16 * st2 + 4 * lg + i;
+        sv[st2][i] = (!need_mask || j < lim) ? ssum[st2][i] : -INFINITY;
+        tmax = fmaxf(tmax, sv[st2][i]);
+      }
+    tmax = xor32_max(xor16_max(tmax)) * qk_scale;
+    true_max = fmaxf(true_max, tmax);
+    const bool grow = tmax > m + 8.f;
+    if (__ballot(grow)) {
+      const float mnew = grow ? tmax : m;
+      const float alpha = fast_exp2((m == -INFINITY ? -INFINITY : m) - (mnew == -INFINITY ? 0.f : mnew));
+      const float a = grow ? alpha : 1.f;
+      lsum *= a;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) oacc[d] *= a;
+      m = mnew;
+    }
+    const float nmref = -(m == -INFINITY ? 0.f : m);
+    float e[8];
+#pragma unroll
+    for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[4 * st2 + i] = fast_exp2(fmaf(sv[st2][i], qk_scale, nmref));
+    const uint4 bits = make_uint4(pack2<BF16>(e[0], e[1]), pack2<BF16>(e[2], e[3]),
+                                  pack2<BF16>(e[4], e[5]), pack2<BF16>(e[6], e[7]));
+    const i16x8_t pb = as_i16x8(bits);
+    lsum = sum2<BF16>(bits.x, sum2<BF16>(bits.y, sum2<BF16>(bits.z, sum2<BF16>(bits.w, lsum))));
+    // O^T += V^T P^T for dims 64w + 16d: V^T by two transposed 4x16 reads
+    const int rr = 4 * lg + (l16 >> 2);
+    const int vsw = mla_swz(rr);
+    const int hp = (l16 & 3) >> 1;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int piece = 2 * (4 * w + d) + hp;  // dims 16 (4w + d) + 4 (l16 % 4): piece, half
+      const int q = (piece & ~7) | ((piece & 7) ^ vsw);
+      const uint16_t* a0 = reinterpret_cast<const uint16_t*>(kv + rr * kKP2 + 16 * q + 8 * (l16 & 1));
+      const i16x4_t lo4 = lds_read_tr(a0);
+      const i16x4_t hi4 = lds_read_tr(a0 + 16 * (kKP2 / 2));
+      const i16x8_t va = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      oacc[d] = mfma16<BF16>(va, pb, oacc[d]);
+    }
+  };
+
+  if (jhi > j0) {
+    const int pfirst = j0 / P, plast = (jhi - 1) / P;
+    for (int wb = pfirst; wb <= plast; wb += kPageWinM) {
+      const int npw = min(kPageWinM, plast - wb + 1);
+      __syncthreads();  // the previous window's readers are done
+      for (int i = tid; i < npw; i += 64 * kNW2) s_pages[i] = p.kv_indices[pbeg + wb + i];
+      __syncthreads();
+      const int ws = max(j0, wb * P), we = min(jhi, (wb + npw) * P);
+      const int nk = (we - ws + kTK2 - 1) / kTK2;
+      // tile k in stage k % 3; tiles k+1, k+2 in flight during tile k.  With at
+      // least kMinDma direct loads per wave per tile, vmcnt(kMinDma) after
+      // issuing tile k+1 means tile k has landed.
+      constexpr int kMinDma = (FP8 ? kDma8 : kDma) / kNW2;
+      constexpr int kWaitImm = (kMinDma & 0xF) | ((kMinDma >> 4) << 14) | 0x70 | 0xF00;
+      const int wbP = wb * P;
+      auto tile_at = [&](int k) { return ws + min(k, nk - 1) * kTK2; };
+      auto dma = [&](uint8_t* stage, int jb) __attribute__((always_inline)) {
+        if constexpr (FP8)
+          dma_tile8(p, s_pages, stage, jb, we, wbP, g, w, lane);
+        else
+          dma_tile(p, s_pages, stage, jb, we, wbP, g, w, lane);
+      };
+      dma(s_kv0, tile_at(0));
+      dma(s_kv1, tile_at(1));
+#define PA_MLA_NSTEP(K, CUR, NEXT2)                                                           \
+  {                                                                                         \
+    __builtin_amdgcn_s_waitcnt(kWaitImm); /* tile K's direct loads are done */              \
+    __syncthreads();                                                                        \
+    dma(NEXT2, tile_at((K) + 2));                                                           \
+    const uint8_t* src = CUR;                                                               \
+    if constexpr (FP8) {                                                                    \
+      convert_tile(CUR, s_wide, tid);                                                       \
+      __syncthreads();                                                                      \
+      src = s_wide;                                                                         \
+    }                                                                                       \
+    tile(src, ws + (K) * kTK2);                                                             \
+  }
+      for (int k = 0; k < nk; k += 3) {
+        PA_MLA_NSTEP(k, s_kv0, s_kv2);
+        if (k + 1 >= nk) break;
+        PA_MLA_NSTEP(k + 1, s_kv1, s_kv0);
+        if (k + 2 >= nk) break;
+        PA_MLA_NSTEP(k + 2, s_kv2, s_kv1);
+      }
+#undef PA_MLA_NSTEP
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no loads in flight into the stages
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: wave w writes dims [64w, 64w+64) of the R rows; wave 0 the stats
+  const float ltot = xor32_sum(xor16_sum(lsum));
+  if (!row_ok) return;
+  const bool empty = !(ltot > 0.f);
+  const float scale = empty ? 0.f : p.v_scale / ltot;
+  const int64_t rid = (int64_t)(b * p.q_len + row / p.group) * p.num_qo_heads + (int64_t)g * p.group +
+                      row % p.group;
+  const int64_t wrow = wslot * p.ws_rows + row;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int dim = 64 * w + 16 * d + 4 * lg;
+    const float x0 = oacc[d][0] * scale, x1 = oacc[d][1] * scale;
+    const float x2 = oacc[d][2] * scale, x3 = oacc[d][3] * scale;
+    if (to_ws) {
+      *reinterpret_cast<float4*>(p.ws_o + wrow * kDvo + dim) = make_float4(x0, x1, x2, x3);
+    } else if (p.o_dtype == F32) {
+      *reinterpret_cast<float4*>(static_cast<float*>(p.o) + c * p.o_split_stride + rid * kDvo + dim) =
+          make_float4(x0, x1, x2, x3);
+    } else {
+      const uint2 v = p.o_dtype == F16 ? make_uint2(pack2<F16>(x0, x1), pack2<F16>(x2, x3))
+                                       : make_uint2(pack2<BF16>(x0, x1), pack2<BF16>(x2, x3));
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + c * p.o_split_stride + rid * kDvo + dim) = v;
+    }
+  }
+  if (w == 0 && lg == 0) {
+    const float lse = empty ? -INFINITY : (m + fast_log2(ltot)) * kLn2;
+    const float mx = empty ? -INFINITY : true_max * kLn2;
+    if (to_ws) {
+      p.ws_lse[wrow] = lse;
+      p.ws_mx[wrow] = mx;
+    } else {
+      const int64_t sidx = c * p.s_split_stride + rid;
+      if (p.lse) p.lse[sidx] = lse;
+      if (p.mx) p.mx[sidx] = mx;
+    }
+  }
+}
+
+// Workgroups: (request, KV head, chunk or explicit split) items, or, under the
+// balanced split, equal shares of the (request, KV head, 32-token unit) sequence.
+template <bool FP8>
+__global__ __launch_bounds__(64 * kNW2, 1) void mla_narrow_kernel(AttnParams p, int ngroups) {
+  constexpr int STAGE = FP8 ? kStage8 : kStage2;
+  __shared__ __align__(16) uint8_t s_kv0[STAGE];
+  __shared__ __align__(16) uint8_t s_kv1[STAGE];
+  __shared__ __align__(16) uint8_t s_kv2[STAGE];
+  __shared__ __align__(16) uint8_t s_wide[FP8 ? kStage2 : 16];  // fp8: the widened tile
+  __shared__ __align__(16) f32x4_t s_part[kNS][2][64];           // partial scores
+  __shared__ int s_pages[kPageWinM];
+  if (p.bal_blocks > 0) {
+    BalCursor cur;
+    if (!cur.start(p, blockIdx.x)) return;
+    do {
+      mla_narrow_range<FP8>(p, cur.b, cur.g, cur.L, cur.j0(p), cur.j1(p), !cur.whole(), cur.slot(p), 0,
+                            s_kv0, s_kv1, s_kv2, s_wide, s_part, s_pages);
+    } while (cur.next(p));
+    return;
+  }
+  const int gi = blockIdx.x;
+  if (gi >= ngroups) return;
+  const int b = gi / (p.num_kv_heads * p.max_chunks);
+  const int g = (gi / p.max_chunks) % p.num_kv_heads;
+  const int c = gi % p.max_chunks;
+  int L, j0, j1;
+  bool to_ws;
+  if (!mla_item_range(p, b, c, L, j0, j1, to_ws)) return;
+  mla_narrow_range<FP8>(p, b, g, L, j0, j1, to_ws, (int64_t)(b * p.num_kv_heads + g) * p.max_chunks + c,
+                        c, s_kv0, s_kv1, s_kv2, s_wide, s_part, s_pages);
+}
+
 hipError_t launch_rows(const AttnParams& p, hipStream_t stream) {
   const int R = p.q_len * p.group;
   const int nrt = (R + kRT2 - 1) / kRT2;
@@ -767,11 +1059,17 @@ hipError_t launch_rows(const AttnParams& p, hipStream_t stream) {
   AttnParams q = p;
   if (p.chunk_tokens <= 0) q.max_chunks = items;
   const int ngroups = p.batch * p.num_kv_heads * items;
-  const int blocks = nrt * 8 * ((ngroups + 7) / 8);
-  if (p.kv_dtype == FP8)
+  const int blocks = p.bal_blocks > 0 ? p.bal_blocks : nrt * 8 * ((ngroups + 7) / 8);
+  if (R <= kRW) {
+    if (p.kv_dtype == FP8)
+      mla_narrow_kernel<true><<<blocks, 64 * kNW2, 0, stream>>>(q, ngroups);
+    else
+      mla_narrow_kernel<false><<<blocks, 64 * kNW2, 0, stream>>>(q, ngroups);
+  } else if (p.kv_dtype == FP8) {
     mla_rows_kernel<true><<<blocks, 64 * kNW2, 0, stream>>>(q, nrt, ngroups);
-  else
+  } else {
     mla_rows_kernel<false><<<blocks, 64 * kNW2, 0, stream>>>(q, nrt, ngroups);
+  }
   return hipGetLastError();
 }
 
@@ -804,9 +1102,7 @@ bool mla_rows_path(const AttnParams& p) {
   // the 128-row kernel divides tokens within a page-id window by the page size
   // with a 32-bit reciprocal: window-relative tokens (< 256 pages) times the page
   // size below 2^32.
-  // fp8 KV with at most 16 rows per request streams faster through the
-  // register-staged kernel (measured: 185 vs 214 us for 16 heads, q_len 1)
-  const bool rows_pay = p.kv_dtype == BF16 || (p.kv_dtype == FP8 && p.q_len * p.group > 16);
+  const bool rows_pay = p.kv_dtype == BF16 || p.kv_dtype == FP8;
   return rows_pay && p.page_size <= 4096 &&
          p.ks0 < (int64_t(1) << 31) &&
          (p.page_size - 1) * p.ks1 + (p.num_kv_heads - 1) * p.ks2 + kDqk < (int64_t(1) << 31);
@@ -822,6 +1118,23 @@ int mla_rows_per_tile(const AttnParams& p) {
   const int R = p.q_len * p.group;
   if (mla_rows_path(p)) return kRT2;
   return R <= 16 ? 16 : R <= 32 ? 32 : 64;
+}
+
+bool mla_balanced_ok(const AttnParams& p) { return mla_rows_path(p) && p.q_len * p.group <= kRT2; }
+
+int mla_blocks_per_cu(const AttnParams& p) {
+  const bool fp8 = p.kv_dtype == FP8;
+  const bool narrow = p.q_len * p.group <= kRW;
+  const void* f = narrow ? (fp8 ? reinterpret_cast<const void*>(&mla_narrow_kernel<true>)
+                                : reinterpret_cast<const void*>(&mla_narrow_kernel<false>))
+                         : (fp8 ? reinterpret_cast<const void*>(&mla_rows_kernel<true>)
+                                : reinterpret_cast<const void*>(&mla_rows_kernel<false>));
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 64 * kNW2, 0) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = 1;  // the kernels' LDS stages fill a CU
+  }
+  return n;
 }
 
 hipError_t launch_mla_decode(const AttnParams& p, hipStream_t stream) {

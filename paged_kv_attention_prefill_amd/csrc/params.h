@@ -43,10 +43,20 @@ struct AttnParams {
   int32_t chunk_tokens;
   int32_t max_chunks;
   int32_t ws_rows;          // row slots per (batch, KV head, chunk) in the workspace
-  float* ws_o;              // [B][Hkv][max_chunks][ws_rows][dvo]
-  float* ws_lse;            // [B][Hkv][max_chunks][ws_rows]
-  float* ws_mx;             // [B][Hkv][max_chunks][ws_rows]
+  float* ws_o;              // [B][Hkv][max_chunks][ws_rows][dvo], or [slots][ws_rows][dvo]
+  float* ws_lse;            // [B][Hkv][max_chunks][ws_rows], or [slots][ws_rows]
+  float* ws_mx;             // same as ws_lse
+  // work-balanced split (decode, instead of chunks when bal_blocks > 0): bal_blocks
+  // workgroups take equal shares of the (batch, KV head, unit) sequence, units of
+  // bal_unit tokens; partial states go to slot item + workgroup, and ws_seg[2 item],
+  // ws_seg[2 item + 1] receive the item's first and last workgroup
+  int32_t bal_blocks;
+  int32_t bal_unit;
+  int32_t* ws_seg;          // [B * Hkv][2]
 };
+
+// Workspace slots of a balanced split: item + workgroup < items + blocks - 1.
+inline int64_t bal_slots(int64_t items, int blocks) { return items + blocks - 1; }
 
 // Number of chunks of a KV batch of L tokens under internal chunking.
 __host__ __device__ inline int num_chunks(int L, int chunk_tokens, int max_chunks) {
@@ -58,9 +68,12 @@ __host__ __device__ inline int num_chunks(int L, int chunk_tokens, int max_chunk
 hipError_t launch_generic(const AttnParams& p, hipStream_t stream);
 bool gqa_decode_supported(const AttnParams& p);
 hipError_t launch_gqa_decode(const AttnParams& p, bool same_strides, hipStream_t stream);
+int gqa_decode_blocks_per_cu(const AttnParams& p, bool same_strides);
 bool mla_decode_supported(const AttnParams& p);
 bool mla_rows_path(const AttnParams& p);
 int mla_rows_per_tile(const AttnParams& p);
+bool mla_balanced_ok(const AttnParams& p);
+int mla_blocks_per_cu(const AttnParams& p);
 hipError_t launch_mla_decode(const AttnParams& p, hipStream_t stream);
 bool flash_attn_supported(const AttnParams& p);
 hipError_t launch_flash_attn(const AttnParams& p, bool same_strides, hipStream_t stream);

@@ -201,6 +201,24 @@ def test_edge_lengths_and_empty_batches():
         run_and_check(dataclasses.replace(w, num_kv_splits=S), f"edge lengths S={S}")
 
 
+def test_balanced_split_ragged_batches():
+    # more than 2 x 64 query batches (the workgroups scan the batch 64 at a time),
+    # empty and sub-tile KV batches next to long ones: workgroup shares start and
+    # end inside items, items span many workgroups, and some workgroups hold
+    # several whole items
+    rng = np.random.default_rng(78)
+    kv_lens = rng.integers(0, 200, size=130)
+    kv_lens[[0, 5, 64, 127, 129]] = 0
+    kv_lens[[1, 65, 128]] = [1, 31, 33]
+    kv_lens[[10, 70, 100]] = [3000, 4097, 2500]
+    w = W.build(rng, 78, "balanced", q_lens=[1] * 130, kv_lens=kv_lens, num_qo_heads=16,
+                num_kv_heads=2, head_dim_qk=128, head_dim_vo=128, page_size=16,
+                q_dtype=W.DT_BF16, kv_dtype=W.DT_BF16)
+    run_and_check(w, "balanced ragged")
+    run_and_check(w, "balanced ragged, short hint", max_kv_len=300)
+    run_and_check(dataclasses.replace(w, causal=True), "balanced ragged causal")
+
+
 def test_causal_rows_that_see_nothing():
     # q_len 4 against KV lengths 1..3: the first queries see no token
     w = W.config4(num_heads=16, q_len=4, batch=6, min_len=1, max_len=3)

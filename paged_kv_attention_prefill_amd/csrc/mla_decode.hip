@@ -380,9 +380,114 @@ constexpr int kRT2 = kNW2 * kRW;         // rows per workgroup
 constexpr int kTK2 = 32;                 // KV tokens per tile
 constexpr int kPieces = kDqk / 8;       // 16-byte pieces per latent row (72)
 constexpr int kKP2 = kPieces * 16;       // LDS row pitch (bytes), unpadded
+static_assert(16 * kKP2 == 18432, "the asm LDS reads address row r + 16 with offset:18432");
 constexpr int kDma = kTK2 * kPieces / 64;  // 1-KB direct-load instructions per tile (36)
 constexpr int kStage2 = kDma * 1024;     // one tile in LDS
 static_assert(kTK2 * kPieces % 64 == 0, "a tile is a whole number of 1-KB wave loads");
+
+// Workgroup barrier for the LDS hand-offs of the narrow kernel's streaming loop.
+// The fence of __syncthreads makes every wave wait for all of its outstanding
+// vector-memory operations, which includes the direct-to-LDS loads of the tiles
+// still in flight (their LDS writes fall under the fence), so the pipeline
+// would drain at every barrier.  Here the LDS operations are completed
+// explicitly (lgkmcnt(0): writes visible to the other waves after the barrier),
+// the loads of the tile being handed over are waited for by the caller (vmcnt),
+// and the memory clobbers keep the compiler from moving LDS accesses across the
+// barrier.  (The many-rows kernel measured faster with __syncthreads.)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt: no wait
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return (uint32_t)(uintptr_t)(const PA_LDS void*)p;
+}
+
+// Reads of a stage that direct loads filled.  The caller has waited for the
+// tile's loads (vmcnt, then a barrier); the compiler cannot see that and, where
+// its tracking of direct-to-LDS loads loses the stages (at loop heads), waits
+// for every load in flight before such a read.  These reads are written in
+// inline asm, each block waiting for its own reads before it returns.
+__device__ __forceinline__ void lds_read6_b128(uint32_t a0, uint32_t a1, uint32_t a2, i32x4_t (&r)[6]) {
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %6 offset:18432\n\t"
+      "ds_read_b128 %2, %7\n\t"
+      "ds_read_b128 %3, %7 offset:18432\n\t"
+      "ds_read_b128 %4, %8\n\t"
+      "ds_read_b128 %5, %8 offset:18432\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5])
+      : "v"(a0), "v"(a1), "v"(a2)
+      : "memory");
+}
+// Eight transposed 4x16 reads (ds_read_b64_tr_b16) at b_d and b_d + 18432.
+__device__ __forceinline__ void lds_read8_tr(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3,
+                                             i32x2_t (&r)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:18432\n\t"
+      "ds_read_b64_tr_b16 %2, %9\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:18432\n\t"
+      "ds_read_b64_tr_b16 %4, %10\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:18432\n\t"
+      "ds_read_b64_tr_b16 %6, %11\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:18432\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+        "=&v"(r[7])
+      : "v"(b0), "v"(b1), "v"(b2), "v"(b3)
+      : "memory");
+}
+// Writes of 16-byte pieces into the widened tile (not a direct-load target, but
+// the compiler's tracking would order them after every load in flight),
+// completed before returning.
+__device__ __forceinline__ void lds_write4_b128(uint32_t a0, i32x4_t v0, uint32_t a1, i32x4_t v1,
+                                                uint32_t a2, i32x4_t v2, uint32_t a3, i32x4_t v3) {
+  asm volatile(
+      "ds_write_b128 %0, %1\n\t"
+      "ds_write_b128 %2, %3\n\t"
+      "ds_write_b128 %4, %5\n\t"
+      "ds_write_b128 %6, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      :
+      : "v"(a0), "v"(v0), "v"(a1), "v"(v1), "v"(a2), "v"(v2), "v"(a3), "v"(v3)
+      : "memory");
+}
+__device__ __forceinline__ void lds_write2_b128(uint32_t a0, i32x4_t v0, uint32_t a1, i32x4_t v1) {
+  asm volatile(
+      "ds_write_b128 %0, %1\n\t"
+      "ds_write_b128 %2, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      :
+      : "v"(a0), "v"(v0), "v"(a1), "v"(v1)
+      : "memory");
+}
+// Two 16-byte reads.
+__device__ __forceinline__ void lds_read2_b128(uint32_t a0, uint32_t a1, i32x4_t& r0, i32x4_t& r1) {
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1)
+      : "v"(a0), "v"(a1)
+      : "memory");
+}
+__device__ __forceinline__ i32x4_t lds_read_b128(uint32_t a0) {
+  i32x4_t r;
+  asm volatile(
+      "ds_read_b128 %0, %1\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r)
+      : "v"(a0)
+      : "memory");
+  return r;
+}
 
 // LDS swizzle: piece p of row r sits at slot p ^ swz(r) of the row (the XOR stays
 // within p's aligned group of 8 pieces).  With the 1152-byte pitch, even rows
@@ -456,23 +561,41 @@ __device__ __forceinline__ void dma_tile8(const AttnParams& p, const int* s_page
 
 // fp8 stage -> bf16 tile (swizzled layout of the bf16 path); e4m3 codes widen
 // exactly to bf16.  Every thread converts whole 16-code pieces.
-__device__ __forceinline__ void convert_tile(const uint8_t* src, uint8_t* dst, int tid) {
-  for (int q = tid; q < kTK2 * kPieces8; q += 64 * kNW2) {
-    const int row = q / kPieces8, piece = q - row * kPieces8;
-    const uint4 x = *reinterpret_cast<const uint4*>(src + 16 * q);
-    const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
-    uint32_t o[8];
+// One piece (16 codes of row q / kPieces8) -> its two 16-byte bf16 pieces and
+// their LDS addresses in the swizzled tile at dst.
+struct WidePiece {
+  uint32_t a0, a1;
+  i32x4_t v0, v1;
+};
+__device__ __forceinline__ WidePiece convert_piece(i32x4_t x, int q, uint32_t dst) {
+  const int row = q / kPieces8, piece = q - row * kPieces8;
+  const uint32_t wv[4] = {(uint32_t)x.x, (uint32_t)x.y, (uint32_t)x.z, (uint32_t)x.w};
+  int o[8];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const auto lo2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[h], false);
-      const auto hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[h], true);
-      o[2 * h] = (__float_as_uint(lo2[0]) >> 16) | (__float_as_uint(lo2[1]) & 0xffff0000u);
-      o[2 * h + 1] = (__float_as_uint(hi2[0]) >> 16) | (__float_as_uint(hi2[1]) & 0xffff0000u);
-    }
-    const int sw = mla_swz(row);
-    uint8_t* drow = dst + row * kKP2;
-    *reinterpret_cast<uint4*>(drow + 16 * ((2 * piece) ^ sw)) = make_uint4(o[0], o[1], o[2], o[3]);
-    *reinterpret_cast<uint4*>(drow + 16 * ((2 * piece + 1) ^ sw)) = make_uint4(o[4], o[5], o[6], o[7]);
+  for (int h = 0; h < 4; ++h) {
+    const auto lo2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[h], false);
+    const auto hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[h], true);
+    o[2 * h] = (int)((__float_as_uint(lo2[0]) >> 16) | (__float_as_uint(lo2[1]) & 0xffff0000u));
+    o[2 * h + 1] = (int)((__float_as_uint(hi2[0]) >> 16) | (__float_as_uint(hi2[1]) & 0xffff0000u));
+  }
+  const int sw = mla_swz(row);
+  const uint32_t drow = dst + row * kKP2;
+  return WidePiece{drow + 16 * ((2 * piece) ^ sw), drow + 16 * ((2 * piece + 1) ^ sw),
+                   i32x4_t{o[0], o[1], o[2], o[3]}, i32x4_t{o[4], o[5], o[6], o[7]}};
+}
+
+__device__ __forceinline__ void convert_tile(const uint8_t* src, uint8_t* dst, int tid) {
+  static_assert(kTK2 * kPieces8 > 2 * 64 * kNW2 && kTK2 * kPieces8 <= 3 * 64 * kNW2, "three rounds");
+  const uint32_t a = lds_off(src) + 16 * tid;
+  const uint32_t d = lds_off(dst);
+  i32x4_t x0, x1;
+  lds_read2_b128(a, a + 16 * 64 * kNW2, x0, x1);
+  const WidePiece p0 = convert_piece(x0, tid, d);
+  const WidePiece p1 = convert_piece(x1, tid + 64 * kNW2, d);
+  lds_write4_b128(p0.a0, p0.v0, p0.a1, p0.v1, p1.a0, p1.v0, p1.a1, p1.v1);
+  if (tid + 2 * 64 * kNW2 < kTK2 * kPieces8) {
+    const WidePiece p2 = convert_piece(lds_read_b128(a + 2 * 16 * 64 * kNW2), tid + 2 * 64 * kNW2, d);
+    lds_write2_b128(p2.a0, p2.v0, p2.a1, p2.v1);
   }
 }
 
@@ -669,11 +792,11 @@ __device__ __forceinline__ void mla_rows_range(const AttnParams& p, int b, int g
       const int ws = max(j0, wb * P), we = min(jhi, (wb + npw) * P);
       const int nk = (we - ws + kTK2 - 1) / kTK2;
       // tile k lives in stage k % 4; tiles k+1..k+3 are in flight during the
-      // math of tile k.  A wave issues at least kMinDma direct loads per tile, so
+      // math of tile k.  A wave issues kMinDma direct loads per tile, so
       // vmcnt(2 kMinDma) after issuing tile k+2 means tile k's loads are done;
       // the barrier then covers every wave's loads, and every wave is done with
       // tile k-1, whose stage takes tile k+3.
-      constexpr int kMinDma = (FP8 ? kDma8 : kDma) / kNW2;  // direct loads per wave per tile, at least
+      constexpr int kMinDma = (FP8 ? kDma8 : kDma) / kNW2;  // direct loads per wave per tile
       constexpr int kWait = 2 * kMinDma;     // vmcnt that leaves only tiles k+1, k+2 in flight
       static_assert(kWait < 64, "vmcnt field");
       constexpr int kWaitImm = (kWait & 0xF) | ((kWait >> 4) << 14) | 0x70 | 0xF00;
@@ -693,12 +816,12 @@ __device__ __forceinline__ void mla_rows_range(const AttnParams& p, int b, int g
 #define PA_MLA_STEP(K, CUR, NEXT3)                                                            \
   {                                                                                         \
     __builtin_amdgcn_s_waitcnt(kWaitImm); /* tile K's direct loads are done */              \
-    __syncthreads();                                                                        \
+    __syncthreads();                                                                         \
     dma(NEXT3, tile_at((K) + 3));                                                           \
     const uint8_t* src = CUR;                                                               \
     if constexpr (FP8) {                                                                    \
       convert_tile(CUR, s_wide, tid);                                                       \
-      __syncthreads();                                                                      \
+      __syncthreads();                                                                       \
       src = s_wide;                                                                         \
     }                                                                                       \
     const int jb = ws + (K) * kTK2;                                                         \
@@ -800,7 +923,7 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_rows_kernel(AttnParams p, in
 // ---------------------------------------------------------------------------
 // Up to 16 rows per request (q_len x H <= 16): one row block is too little MFMA
 // work for one wave to keep up with HBM, so the tile is shared out by dims.
-// Per 32-token tile (three LDS stages fed by direct loads, as above):
+// Per 32-token tile (LDS stages fed by direct loads, as above):
 //   S^T = K Q^T is split over the 576 dims: waves 0..5 each take three 32-dim
 //   k-steps (one 16x16x32 MFMA per k-step and 16-token block) and leave their
 //   partial scores in LDS; after a barrier every wave adds the six partials for
@@ -808,6 +931,10 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_rows_kernel(AttnParams p, in
 //   every wave);
 //   O^T += V^T P^T is split over the 512 V dims: wave w owns dims [64w, 64w+64).
 constexpr int kNS = kDqk / 32 / 3;  // waves that compute partial scores (6)
+// LDS stages (tiles in flight + 1): as many as fit next to the score exchange
+// (bf16: 4 x 36 KB; fp8: 6 x 18 KB plus the 36 KB widened tile)
+template <bool FP8>
+constexpr int kNarrowStages = FP8 ? 6 : 4;
 
 // One (request b, KV head g) token range [j0, j1) of the narrow kernel; the
 // result goes to the final O / LSE (split c_out) or to workspace slot wslot.
@@ -815,8 +942,10 @@ constexpr int kNS = kDqk / 32 / 3;  // waves that compute partial scores (6)
 template <bool FP8>
 __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int g, int L, int j0, int j1,
                                                  bool to_ws, int64_t wslot, int c, uint8_t* s_kv0,
-                                                 uint8_t* s_kv1, uint8_t* s_kv2, uint8_t* s_wide,
+                                                 uint8_t* s_kv1, uint8_t* s_kv2, uint8_t* s_kv3,
+                                                 uint8_t* s_kv4, uint8_t* s_kv5, uint8_t* s_wide,
                                                  f32x4_t (*s_part)[2][64], int* s_pages) {
+  constexpr int NST = kNarrowStages<FP8>;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -861,26 +990,43 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
     if (w < kNS) {
       f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
       const int sw = mla_swz(l16);  // rows l16 and 16 + l16 share the swizzle
+      uint32_t ka[3];
 #pragma unroll
       for (int u = 0; u < 3; ++u) {
-        const int kk = 3 * w + u;
-        const int piece = 4 * kk + lg;
-        const int q = (piece & ~7) | ((piece & 7) ^ sw);
-#pragma unroll
-        for (int st2 = 0; st2 < 2; ++st2) {
-          const i16x8_t a = *reinterpret_cast<const i16x8_t*>(kv + (16 * st2 + l16) * kKP2 + 16 * q);
-          sacc[st2] = mfma16<BF16>(a, qreg[u], sacc[st2]);
-        }
+        const int piece = 4 * (3 * w + u) + lg;
+        ka[u] = lds_off(kv) + l16 * kKP2 + 16 * ((piece & ~7) | ((piece & 7) ^ sw));
       }
+      i32x4_t kr[6];  // (k-step u, block st2) at 2u + st2
+      lds_read6_b128(ka[0], ka[1], ka[2], kr);
+#pragma unroll
+      for (int u = 0; u < 3; ++u)
+#pragma unroll
+        for (int st2 = 0; st2 < 2; ++st2)
+          sacc[st2] = mfma16<BF16>(__builtin_bit_cast(i16x8_t, kr[2 * u + st2]), qreg[u], sacc[st2]);
       s_part[w][0][lane] = sacc[0];
       s_part[w][1][lane] = sacc[1];
     }
-    __syncthreads();
+    lds_barrier();
     f32x4_t ssum[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int v = 0; v < kNS; ++v) {
       ssum[0] += s_part[v][0][lane];
       ssum[1] += s_part[v][1][lane];
+    }
+    // V^T operands of dims 64w + 16d: two transposed 4x16 reads each (row rr
+    // and rr + 16, same swizzle), lane quad l16 % 4 = dims 4 (l16 % 4)..+3
+    i32x2_t vr[8];
+    {
+      const int rr = 4 * lg + (l16 >> 2);
+      const int vsw = mla_swz(rr);
+      const int hp = (l16 & 3) >> 1;
+      uint32_t vb[4];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int piece = 2 * (4 * w + d) + hp;
+        vb[d] = lds_off(kv) + rr * kKP2 + 16 * ((piece & ~7) | ((piece & 7) ^ vsw)) + 8 * (l16 & 1);
+      }
+      lds_read8_tr(vb[0], vb[1], vb[2], vb[3], vr);
     }
     // lane holds row l16, tokens jb + 16st + 4lg + i
     const bool need_mask = jb + kTK2 > wave_lim_min;
@@ -916,19 +1062,11 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
                                   pack2<BF16>(e[4], e[5]), pack2<BF16>(e[6], e[7]));
     const i16x8_t pb = as_i16x8(bits);
     lsum = sum2<BF16>(bits.x, sum2<BF16>(bits.y, sum2<BF16>(bits.z, sum2<BF16>(bits.w, lsum))));
-    // O^T += V^T P^T for dims 64w + 16d: V^T by two transposed 4x16 reads
-    const int rr = 4 * lg + (l16 >> 2);
-    const int vsw = mla_swz(rr);
-    const int hp = (l16 & 3) >> 1;
+    // O^T += V^T P^T for dims 64w + 16d
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const int piece = 2 * (4 * w + d) + hp;  // dims 16 (4w + d) + 4 (l16 % 4): piece, half
-      const int q = (piece & ~7) | ((piece & 7) ^ vsw);
-      const uint16_t* a0 = reinterpret_cast<const uint16_t*>(kv + rr * kKP2 + 16 * q + 8 * (l16 & 1));
-      const i16x4_t lo4 = lds_read_tr(a0);
-      const i16x4_t hi4 = lds_read_tr(a0 + 16 * (kKP2 / 2));
-      const i16x8_t va = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-      oacc[d] = mfma16<BF16>(va, pb, oacc[d]);
+      const i32x4_t v4 = {vr[2 * d].x, vr[2 * d].y, vr[2 * d + 1].x, vr[2 * d + 1].y};
+      oacc[d] = mfma16<BF16>(__builtin_bit_cast(i16x8_t, v4), pb, oacc[d]);
     }
   };
 
@@ -941,11 +1079,13 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
       __syncthreads();
       const int ws = max(j0, wb * P), we = min(jhi, (wb + npw) * P);
       const int nk = (we - ws + kTK2 - 1) / kTK2;
-      // tile k in stage k % 3; tiles k+1, k+2 in flight during tile k.  With at
-      // least kMinDma direct loads per wave per tile, vmcnt(kMinDma) after
-      // issuing tile k+1 means tile k has landed.
-      constexpr int kMinDma = (FP8 ? kDma8 : kDma) / kNW2;
-      constexpr int kWaitImm = (kMinDma & 0xF) | ((kMinDma >> 4) << 14) | 0x70 | 0xF00;
+      // tile k in stage k % NST; tiles k+1 .. k+NST-1 in flight during tile k
+      // (a wave issues kMinDma direct loads per tile, so vmcnt(kWait)
+      // after issuing tile k+NST-2 means tile k has landed)
+      constexpr int kMinDma = (FP8 ? kDma8 : kDma) / kNW2;  // loads per wave per tile
+      constexpr int kWait = (NST - 2) * kMinDma;
+      static_assert(kWait < 64, "vmcnt field");
+      constexpr int kWaitImm = (kWait & 0xF) | ((kWait >> 4) << 14) | 0x70 | 0xF00;
       const int wbP = wb * P;
       auto tile_at = [&](int k) { return ws + min(k, nk - 1) * kTK2; };
       auto dma = [&](uint8_t* stage, int jb) __attribute__((always_inline)) {
@@ -956,25 +1096,46 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
       };
       dma(s_kv0, tile_at(0));
       dma(s_kv1, tile_at(1));
-#define PA_MLA_NSTEP(K, CUR, NEXT2)                                                           \
+      dma(s_kv2, tile_at(2));
+      if constexpr (NST > 4) dma(s_kv3, tile_at(3));
+      if constexpr (NST > 5) dma(s_kv4, tile_at(4));
+#define PA_MLA_NSTEP(K, CUR, NEXT)                                                            \
   {                                                                                         \
     __builtin_amdgcn_s_waitcnt(kWaitImm); /* tile K's direct loads are done */              \
-    __syncthreads();                                                                        \
-    dma(NEXT2, tile_at((K) + 2));                                                           \
+    lds_barrier();                                                                           \
+    dma(NEXT, tile_at((K) + NST - 1));                                                      \
     const uint8_t* src = CUR;                                                               \
     if constexpr (FP8) {                                                                    \
       convert_tile(CUR, s_wide, tid);                                                       \
-      __syncthreads();                                                                      \
+      lds_barrier();                                                                         \
       src = s_wide;                                                                         \
     }                                                                                       \
     tile(src, ws + (K) * kTK2);                                                             \
   }
-      for (int k = 0; k < nk; k += 3) {
-        PA_MLA_NSTEP(k, s_kv0, s_kv2);
-        if (k + 1 >= nk) break;
-        PA_MLA_NSTEP(k + 1, s_kv1, s_kv0);
-        if (k + 2 >= nk) break;
-        PA_MLA_NSTEP(k + 2, s_kv2, s_kv1);
+      if constexpr (NST == 4) {
+        for (int k = 0; k < nk; k += 4) {
+          PA_MLA_NSTEP(k, s_kv0, s_kv3);
+          if (k + 1 >= nk) break;
+          PA_MLA_NSTEP(k + 1, s_kv1, s_kv0);
+          if (k + 2 >= nk) break;
+          PA_MLA_NSTEP(k + 2, s_kv2, s_kv1);
+          if (k + 3 >= nk) break;
+          PA_MLA_NSTEP(k + 3, s_kv3, s_kv2);
+        }
+      } else {
+        for (int k = 0; k < nk; k += 6) {
+          PA_MLA_NSTEP(k, s_kv0, s_kv5);
+          if (k + 1 >= nk) break;
+          PA_MLA_NSTEP(k + 1, s_kv1, s_kv0);
+          if (k + 2 >= nk) break;
+          PA_MLA_NSTEP(k + 2, s_kv2, s_kv1);
+          if (k + 3 >= nk) break;
+          PA_MLA_NSTEP(k + 3, s_kv3, s_kv2);
+          if (k + 4 >= nk) break;
+          PA_MLA_NSTEP(k + 4, s_kv4, s_kv3);
+          if (k + 5 >= nk) break;
+          PA_MLA_NSTEP(k + 5, s_kv5, s_kv4);
+        }
       }
 #undef PA_MLA_NSTEP
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no loads in flight into the stages
@@ -1025,9 +1186,13 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
 template <bool FP8>
 __global__ __launch_bounds__(64 * kNW2, 1) void mla_narrow_kernel(AttnParams p, int ngroups) {
   constexpr int STAGE = FP8 ? kStage8 : kStage2;
+  constexpr int NST = kNarrowStages<FP8>;
   __shared__ __align__(16) uint8_t s_kv0[STAGE];
   __shared__ __align__(16) uint8_t s_kv1[STAGE];
   __shared__ __align__(16) uint8_t s_kv2[STAGE];
+  __shared__ __align__(16) uint8_t s_kv3[STAGE];
+  __shared__ __align__(16) uint8_t s_kv4[NST > 4 ? STAGE : 16];
+  __shared__ __align__(16) uint8_t s_kv5[NST > 5 ? STAGE : 16];
   __shared__ __align__(16) uint8_t s_wide[FP8 ? kStage2 : 16];  // fp8: the widened tile
   __shared__ __align__(16) f32x4_t s_part[kNS][2][64];           // partial scores
   __shared__ int s_pages[kPageWinM];
@@ -1036,7 +1201,7 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_narrow_kernel(AttnParams p, 
     if (!cur.start(p, blockIdx.x)) return;
     do {
       mla_narrow_range<FP8>(p, cur.b, cur.g, cur.L, cur.j0(p), cur.j1(p), !cur.whole(), cur.slot(p), 0,
-                            s_kv0, s_kv1, s_kv2, s_wide, s_part, s_pages);
+                            s_kv0, s_kv1, s_kv2, s_kv3, s_kv4, s_kv5, s_wide, s_part, s_pages);
     } while (cur.next(p));
     return;
   }
@@ -1049,7 +1214,7 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_narrow_kernel(AttnParams p, 
   bool to_ws;
   if (!mla_item_range(p, b, c, L, j0, j1, to_ws)) return;
   mla_narrow_range<FP8>(p, b, g, L, j0, j1, to_ws, (int64_t)(b * p.num_kv_heads + g) * p.max_chunks + c,
-                        c, s_kv0, s_kv1, s_kv2, s_wide, s_part, s_pages);
+                        c, s_kv0, s_kv1, s_kv2, s_kv3, s_kv4, s_kv5, s_wide, s_part, s_pages);
 }
 
 hipError_t launch_rows(const AttnParams& p, hipStream_t stream) {

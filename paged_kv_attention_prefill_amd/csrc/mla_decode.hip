@@ -20,6 +20,8 @@
 //     row-major from LDS.
 // Chunks of long KV batches leave partial states (O normalised by the chunk's
 // own sum, LSE, max) in the workspace for the chunk-merge launch.
+#include <type_traits>
+
 #include "balance.h"
 #include "mfma_common.h"
 
@@ -559,6 +561,54 @@ __device__ __forceinline__ void dma_tile8(const AttnParams& p, const int* s_page
   }
 }
 
+// Tiles that lie within one page (the page size a multiple of the tile): the
+// page's offset is uniform, and the (row, piece) each lane loads is fixed per
+// load instruction, so the per-lane part is precomputed once (PageLanes) and a
+// load costs a clamp, a multiply-add and the address add.
+template <bool FP8>
+struct PageLanes {
+  static constexpr int N = ((FP8 ? kDma8 : kDma) + kNW2 - 1) / kNW2;  // load rounds
+  int row[N];       // tile row of this lane's piece in round r
+  uint32_t off[N];  // element offset of the piece within the row (+ KV head)
+  __device__ __forceinline__ void init(const AttnParams& p, int g, int w, int lane) {
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+      const int i = r * kNW2 + w;
+      const int slot = 64 * i + lane;
+      if constexpr (FP8) {
+        row[r] = slot / kPieces8;
+        off[r] = (uint32_t)(g * p.ks2) + 16 * (slot - row[r] * kPieces8);
+      } else {
+        row[r] = slot / kPieces;
+        const int q = slot - row[r] * kPieces;
+        off[r] = (uint32_t)(g * p.ks2) + 8 * (q ^ mla_swz(row[r]));
+      }
+    }
+  }
+};
+
+template <bool FP8>
+__device__ __forceinline__ void dma_tile_page(const AttnParams& p, const int* s_pages, uint8_t* stage,
+                                              int jb, int we, int wbP, const PageLanes<FP8>& pl, int w) {
+  using E = typename std::conditional<FP8, uint8_t, uint16_t>::type;
+  const E* kbase = static_cast<const E*>(p.k);
+  constexpr int kD = FP8 ? kDma8 : kDma;
+  const uint32_t rel = (uint32_t)(jb - wbP);
+  const uint32_t pi = div_by_magic(rel, p.page_magic);
+  const int page = __builtin_amdgcn_readfirstlane(s_pages[pi]);
+  const uint64_t base = (uint64_t)(uint32_t)page * (uint64_t)p.ks0 +
+                        (uint64_t)((rel - pi * (uint32_t)p.page_size) * (uint32_t)p.ks1);
+  const int last = we - 1 - jb;  // rows past the range load the last valid row
+  const uint32_t ks1 = (uint32_t)p.ks1;
+#pragma unroll
+  for (int r = 0; r < PageLanes<FP8>::N; ++r) {
+    const int i = r * kNW2 + w;
+    const uint32_t off = (uint32_t)min(pl.row[r], last) * ks1 + pl.off[r];
+    if (i < kD)
+      __builtin_amdgcn_global_load_lds(kbase + base + off, (PA_LDS void*)(stage + 1024 * i), 16, 0, 0);
+  }
+}
+
 // fp8 stage -> bf16 tile (swizzled layout of the bf16 path); e4m3 codes widen
 // exactly to bf16.  Every thread converts whole 16-code pieces.
 // One piece (16 codes of row q / kPieces8) -> its two 16-byte bf16 pieces and
@@ -1028,16 +1078,21 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
       }
       lds_read8_tr(vb[0], vb[1], vb[2], vb[3], vr);
     }
-    // lane holds row l16, tokens jb + 16st + 4lg + i
-    const bool need_mask = jb + kTK2 > wave_lim_min;
+    // lane holds row l16, tokens jb + 16st + 4lg + i; the mask only on boundary tiles
+    if (jb + kTK2 > wave_lim_min) {
+#pragma unroll
+      for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (jb + 16 * st2 + 4 * lg + i >= lim) ssum[st2][i] = -INFINITY;
+    }
     float sv[2][4];
     float tmax = -INFINITY;
 #pragma unroll
     for (int st2 = 0; st2 < 2; ++st2)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = jb + 16 * st2 + 4 * lg + i;
-        sv[st2][i] = (!need_mask || j < lim) ? ssum[st2][i] : -INFINITY;
+        sv[st2][i] = ssum[st2][i];
         tmax = fmaxf(tmax, sv[st2][i]);
       }
     tmax = xor32_max(xor16_max(tmax)) * qk_scale;
@@ -1070,6 +1125,11 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
     }
   };
 
+  // tiles never straddle a page when the page size is a multiple of the tile
+  // (range starts are multiples of the tile or of the page)
+  const bool page_tiles = P % kTK2 == 0 && j0 % kTK2 == 0;
+  PageLanes<FP8> plane;
+  if (page_tiles) plane.init(p, g, w, lane);
   if (jhi > j0) {
     const int pfirst = j0 / P, plast = (jhi - 1) / P;
     for (int wb = pfirst; wb <= plast; wb += kPageWinM) {
@@ -1080,7 +1140,7 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
       const int ws = max(j0, wb * P), we = min(jhi, (wb + npw) * P);
       const int nk = (we - ws + kTK2 - 1) / kTK2;
       // tile k in stage k % NST; tiles k+1 .. k+NST-1 in flight during tile k
-      // (a wave issues kMinDma direct loads per tile, so vmcnt(kWait)
+      // (a wave issues at least kMinDma direct loads per tile, so vmcnt(kWait)
       // after issuing tile k+NST-2 means tile k has landed)
       constexpr int kMinDma = (FP8 ? kDma8 : kDma) / kNW2;  // loads per wave per tile
       constexpr int kWait = (NST - 2) * kMinDma;
@@ -1089,7 +1149,9 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
       const int wbP = wb * P;
       auto tile_at = [&](int k) { return ws + min(k, nk - 1) * kTK2; };
       auto dma = [&](uint8_t* stage, int jb) __attribute__((always_inline)) {
-        if constexpr (FP8)
+        if (page_tiles)
+          dma_tile_page<FP8>(p, s_pages, stage, jb, we, wbP, plane, w);
+        else if constexpr (FP8)
           dma_tile8(p, s_pages, stage, jb, we, wbP, g, w, lane);
         else
           dma_tile(p, s_pages, stage, jb, we, wbP, g, w, lane);

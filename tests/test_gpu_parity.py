@@ -245,6 +245,20 @@ def test_mla_row_tiles_and_page_sizes(heads, q_len, page_size):
     run_and_check(w, label)
 
 
+@pytest.mark.parametrize("heads,q_len,page_size,dt", [(16, 1, 32, W.DT_BF16), (8, 2, 96, W.DT_BF16),
+                                                      (16, 1, 32, W.DT_FP8), (4, 3, 96, W.DT_FP8),
+                                                      (16, 1, 24, W.DT_FP8)])
+def test_mla_narrow_page_sizes(heads, q_len, page_size, dt):
+    # up to 16 rows per request: page sizes that hold whole 32-token tiles (32, 96:
+    # the tile's page offset is uniform) and one that does not (24); long enough
+    # that the KV is split over workgroups
+    label = f"MLA narrow h{heads} q{q_len} page {page_size} dt {dt}"
+    print(label, flush=True)
+    w = mla_build(950 + heads + page_size + dt, heads, q_len, [0, 31, 33, 3000, 4500, 96 * 20], page_size,
+                  dt=dt)
+    run_and_check(w, label)
+
+
 def test_mla_explicit_splits():
     w = mla_build(991, 128, 1, [0, 5, 640, 999], 64)
     d = R.upload(w)

@@ -634,19 +634,23 @@ __device__ __forceinline__ WidePiece convert_piece(i32x4_t x, int q, uint32_t ds
                    i32x4_t{o[0], o[1], o[2], o[3]}, i32x4_t{o[4], o[5], o[6], o[7]}};
 }
 
-__device__ __forceinline__ void convert_tile(const uint8_t* src, uint8_t* dst, int tid) {
-  static_assert(kTK2 * kPieces8 > 2 * 64 * kNW2 && kTK2 * kPieces8 <= 3 * 64 * kNW2, "three rounds");
-  const uint32_t a = lds_off(src) + 16 * tid;
+// Widening of a whole tile by n threads (t = 0..n-1), 2n < pieces <= 3n.
+__device__ __forceinline__ void convert_tile(const uint8_t* src, uint8_t* dst, int t, int n) {
+  const uint32_t a = lds_off(src) + 16 * t;
   const uint32_t d = lds_off(dst);
   i32x4_t x0, x1;
-  lds_read2_b128(a, a + 16 * 64 * kNW2, x0, x1);
-  const WidePiece p0 = convert_piece(x0, tid, d);
-  const WidePiece p1 = convert_piece(x1, tid + 64 * kNW2, d);
+  lds_read2_b128(a, a + 16 * n, x0, x1);
+  const WidePiece p0 = convert_piece(x0, t, d);
+  const WidePiece p1 = convert_piece(x1, t + n, d);
   lds_write4_b128(p0.a0, p0.v0, p0.a1, p0.v1, p1.a0, p1.v0, p1.a1, p1.v1);
-  if (tid + 2 * 64 * kNW2 < kTK2 * kPieces8) {
-    const WidePiece p2 = convert_piece(lds_read_b128(a + 2 * 16 * 64 * kNW2), tid + 2 * 64 * kNW2, d);
+  if (t + 2 * n < kTK2 * kPieces8) {
+    const WidePiece p2 = convert_piece(lds_read_b128(a + 2 * 16 * n), t + 2 * n, d);
     lds_write2_b128(p2.a0, p2.v0, p2.a1, p2.v1);
   }
+}
+__device__ __forceinline__ void convert_tile(const uint8_t* src, uint8_t* dst, int tid) {
+  static_assert(kTK2 * kPieces8 > 2 * 64 * kNW2 && kTK2 * kPieces8 <= 3 * 64 * kNW2, "three rounds");
+  convert_tile(src, dst, tid, 64 * kNW2);
 }
 
 // Token range of work item c (internal chunk or explicit split) of request b;
@@ -980,7 +984,15 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_rows_kernel(AttnParams p, in
 //   all 16 rows x 32 tokens and runs the same online softmax (identical state in
 //   every wave);
 //   O^T += V^T P^T is split over the 512 V dims: wave w owns dims [64w, 64w+64).
-constexpr int kNS = kDqk / 32 / 3;  // waves that compute partial scores (6)
+constexpr int kNS = kDqk / 32 / 3;  // waves that compute partial scores (6); wave kNS reduces
+static_assert(kNS < kNW2, "a wave beyond the partial-score waves does the softmax");
+// exchange from the reducing wave to the others
+struct NarrowX {
+  i16x8_t pb[64];      // P^T in the PV B-operand layout
+  float alpha[16];     // rows' rescale factors of the current tile (valid when flag)
+  float stat[16][3];   // final: row sum, reference max, running max
+  int flag;            // some row's reference max moved in this tile
+};
 // LDS stages (tiles in flight + 1): as many as fit next to the score exchange
 // (bf16: 4 x 36 KB; fp8: 6 x 18 KB plus the 36 KB widened tile)
 template <bool FP8>
@@ -994,7 +1006,7 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
                                                  bool to_ws, int64_t wslot, int c, uint8_t* s_kv0,
                                                  uint8_t* s_kv1, uint8_t* s_kv2, uint8_t* s_kv3,
                                                  uint8_t* s_kv4, uint8_t* s_kv5, uint8_t* s_wide,
-                                                 f32x4_t (*s_part)[2][64], int* s_pages) {
+                                                 f32x4_t (*s_part)[2][64], NarrowX* s_x, int* s_pages) {
   constexpr int NST = kNarrowStages<FP8>;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1028,6 +1040,7 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
                                   : i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
   }
 
+  // softmax state: kept by the reducing wave (kNS) only
   float m = -INFINITY, lsum = 0.f, true_max = -INFINITY;
   f32x4_t oacc[4];  // dims 64w + 16d + 4lg + i, row l16
 #pragma unroll
@@ -1035,8 +1048,13 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
   const float qk_scale = p.sm_scale * p.k_scale * kLog2e;
   const int P = p.page_size;
 
-  // one tile from a stage (bf16 swizzled layout)
-  auto tile = [&](const uint8_t* kv, int jb) __attribute__((always_inline)) {
+  // One tile of a (bf16, swizzled) tile buffer kv in four parts: waves
+  // 0..kNS-1 compute the partial scores (part_s) and every wave reads its V^T
+  // operands (part_v); after a barrier wave kNS sums the partials, runs the
+  // online softmax and publishes P^T (16-bit, in the PV B-operand layout) and
+  // the rows' rescale factors (part_r); after another barrier every wave does
+  // PV for its 64 dims (part_pv).
+  auto part_s = [&](const uint8_t* kv) __attribute__((always_inline)) {
     if (w < kNS) {
       f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
       const int sw = mla_swz(l16);  // rows l16 and 16 + l16 share the swizzle
@@ -1056,27 +1074,27 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
       s_part[w][0][lane] = sacc[0];
       s_part[w][1][lane] = sacc[1];
     }
-    lds_barrier();
-    f32x4_t ssum[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  };
+  // V^T operands of dims 64w + 16d: two transposed 4x16 reads each (row rr and
+  // rr + 16, same swizzle), lane quad l16 % 4 = dims 4 (l16 % 4)..+3
+  auto part_v = [&](const uint8_t* kv, i32x2_t (&vr)[8]) __attribute__((always_inline)) {
+    const int rr = 4 * lg + (l16 >> 2);
+    const int vsw = mla_swz(rr);
+    const int hp = (l16 & 3) >> 1;
+    uint32_t vb[4];
 #pragma unroll
-    for (int v = 0; v < kNS; ++v) {
+    for (int d = 0; d < 4; ++d) {
+      const int piece = 2 * (4 * w + d) + hp;
+      vb[d] = lds_off(kv) + rr * kKP2 + 16 * ((piece & ~7) | ((piece & 7) ^ vsw)) + 8 * (l16 & 1);
+    }
+    lds_read8_tr(vb[0], vb[1], vb[2], vb[3], vr);
+  };
+  auto part_r = [&](int jb) __attribute__((always_inline)) {
+    f32x4_t ssum[2] = {s_part[0][0][lane], s_part[0][1][lane]};
+#pragma unroll
+    for (int v = 1; v < kNS; ++v) {
       ssum[0] += s_part[v][0][lane];
       ssum[1] += s_part[v][1][lane];
-    }
-    // V^T operands of dims 64w + 16d: two transposed 4x16 reads each (row rr
-    // and rr + 16, same swizzle), lane quad l16 % 4 = dims 4 (l16 % 4)..+3
-    i32x2_t vr[8];
-    {
-      const int rr = 4 * lg + (l16 >> 2);
-      const int vsw = mla_swz(rr);
-      const int hp = (l16 & 3) >> 1;
-      uint32_t vb[4];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const int piece = 2 * (4 * w + d) + hp;
-        vb[d] = lds_off(kv) + rr * kKP2 + 16 * ((piece & ~7) | ((piece & 7) ^ vsw)) + 8 * (l16 & 1);
-      }
-      lds_read8_tr(vb[0], vb[1], vb[2], vb[3], vr);
     }
     // lane holds row l16, tokens jb + 16st + 4lg + i; the mask only on boundary tiles
     if (jb + kTK2 > wave_lim_min) {
@@ -1086,37 +1104,42 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
         for (int i = 0; i < 4; ++i)
           if (jb + 16 * st2 + 4 * lg + i >= lim) ssum[st2][i] = -INFINITY;
     }
-    float sv[2][4];
     float tmax = -INFINITY;
 #pragma unroll
     for (int st2 = 0; st2 < 2; ++st2)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[st2][i] = ssum[st2][i];
-        tmax = fmaxf(tmax, sv[st2][i]);
-      }
+      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, ssum[st2][i]);
     tmax = xor32_max(xor16_max(tmax)) * qk_scale;
     true_max = fmaxf(true_max, tmax);
     const bool grow = tmax > m + 8.f;
-    if (__ballot(grow)) {
+    const bool any = __ballot(grow) != 0;
+    if (any) {
       const float mnew = grow ? tmax : m;
       const float alpha = fast_exp2((m == -INFINITY ? -INFINITY : m) - (mnew == -INFINITY ? 0.f : mnew));
       const float a = grow ? alpha : 1.f;
       lsum *= a;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) oacc[d] *= a;
       m = mnew;
+      if (lg == 0) s_x->alpha[l16] = a;
     }
     const float nmref = -(m == -INFINITY ? 0.f : m);
     float e[8];
 #pragma unroll
     for (int st2 = 0; st2 < 2; ++st2)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) e[4 * st2 + i] = fast_exp2(fmaf(sv[st2][i], qk_scale, nmref));
+      for (int i = 0; i < 4; ++i) e[4 * st2 + i] = fast_exp2(fmaf(ssum[st2][i], qk_scale, nmref));
     const uint4 bits = make_uint4(pack2<BF16>(e[0], e[1]), pack2<BF16>(e[2], e[3]),
                                   pack2<BF16>(e[4], e[5]), pack2<BF16>(e[6], e[7]));
-    const i16x8_t pb = as_i16x8(bits);
     lsum = sum2<BF16>(bits.x, sum2<BF16>(bits.y, sum2<BF16>(bits.z, sum2<BF16>(bits.w, lsum))));
+    s_x->pb[lane] = as_i16x8(bits);
+    if (lane == 0) s_x->flag = any;
+  };
+  auto part_pv = [&](const i32x2_t (&vr)[8]) __attribute__((always_inline)) {
+    if (__builtin_amdgcn_readfirstlane(s_x->flag)) {
+      const float a = s_x->alpha[l16];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) oacc[d] *= a;
+    }
+    const i16x8_t pb = s_x->pb[lane];
     // O^T += V^T P^T for dims 64w + 16d
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -1161,20 +1184,22 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
       dma(s_kv2, tile_at(2));
       if constexpr (NST > 4) dma(s_kv3, tile_at(3));
       if constexpr (NST > 5) dma(s_kv4, tile_at(4));
+      if constexpr (!FP8) {
+        // tile K read in place from its stage
 #define PA_MLA_NSTEP(K, CUR, NEXT)                                                            \
   {                                                                                         \
     __builtin_amdgcn_s_waitcnt(kWaitImm); /* tile K's direct loads are done */              \
     lds_barrier();                                                                           \
     dma(NEXT, tile_at((K) + NST - 1));                                                      \
-    const uint8_t* src = CUR;                                                               \
-    if constexpr (FP8) {                                                                    \
-      convert_tile(CUR, s_wide, tid);                                                       \
-      lds_barrier();                                                                         \
-      src = s_wide;                                                                         \
-    }                                                                                       \
-    tile(src, ws + (K) * kTK2);                                                             \
+    part_s(CUR);                                                                            \
+    i32x2_t vr[8];                                                                          \
+    part_v(CUR, vr);                                                                        \
+    lds_barrier();                                                                           \
+    if (w == kNS) part_r(ws + (K) * kTK2);                                                  \
+    lds_barrier();                                                                           \
+    part_pv(vr);                                                                            \
   }
-      if constexpr (NST == 4) {
+        static_assert(NST == 4, "bf16 stage rotation");
         for (int k = 0; k < nk; k += 4) {
           PA_MLA_NSTEP(k, s_kv0, s_kv3);
           if (k + 1 >= nk) break;
@@ -1184,29 +1209,66 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
           if (k + 3 >= nk) break;
           PA_MLA_NSTEP(k + 3, s_kv3, s_kv2);
         }
-      } else {
-        for (int k = 0; k < nk; k += 6) {
-          PA_MLA_NSTEP(k, s_kv0, s_kv5);
-          if (k + 1 >= nk) break;
-          PA_MLA_NSTEP(k + 1, s_kv1, s_kv0);
-          if (k + 2 >= nk) break;
-          PA_MLA_NSTEP(k + 2, s_kv2, s_kv1);
-          if (k + 3 >= nk) break;
-          PA_MLA_NSTEP(k + 3, s_kv3, s_kv2);
-          if (k + 4 >= nk) break;
-          PA_MLA_NSTEP(k + 4, s_kv4, s_kv3);
-          if (k + 5 >= nk) break;
-          PA_MLA_NSTEP(k + 5, s_kv5, s_kv4);
-        }
-      }
 #undef PA_MLA_NSTEP
+      } else {
+        // fp8: the bf16 tile buffer holds tile K during step K; tile K+1 is
+        // widened into it by the waves other than kNS while wave kNS runs the
+        // softmax of tile K (the buffer's reads for tile K are all done by then)
+        const int tw = w < kNS ? tid : tid - 64;  // widening thread index, 0..447
+        __builtin_amdgcn_s_waitcnt(kWaitImm);  // tile 0's direct loads are done
+        lds_barrier();
+        convert_tile(s_kv0, s_wide, tid);
+#define PA_MLA_FSTEP(K, NEXTRAW, DST)                                                         \
+  {                                                                                         \
+    lds_barrier();                                                                           \
+    dma(DST, tile_at((K) + NST - 1));                                                       \
+    part_s(s_wide);                                                                         \
+    i32x2_t vr[8];                                                                          \
+    part_v(s_wide, vr);                                                                     \
+    __builtin_amdgcn_s_waitcnt(kWaitImm); /* tile K+1's direct loads are done */            \
+    lds_barrier();                                                                           \
+    if (w == kNS)                                                                           \
+      part_r(ws + (K) * kTK2);                                                              \
+    else                                                                                    \
+      convert_tile(NEXTRAW, s_wide, tw, 64 * (kNW2 - 1));                                   \
+    lds_barrier();                                                                           \
+    part_pv(vr);                                                                            \
+  }
+        static_assert(NST == 6, "fp8 stage rotation");
+        for (int k = 0; k < nk; k += 6) {
+          PA_MLA_FSTEP(k, s_kv1, s_kv5);
+          if (k + 1 >= nk) break;
+          PA_MLA_FSTEP(k + 1, s_kv2, s_kv0);
+          if (k + 2 >= nk) break;
+          PA_MLA_FSTEP(k + 2, s_kv3, s_kv1);
+          if (k + 3 >= nk) break;
+          PA_MLA_FSTEP(k + 3, s_kv4, s_kv2);
+          if (k + 4 >= nk) break;
+          PA_MLA_FSTEP(k + 4, s_kv5, s_kv3);
+          if (k + 5 >= nk) break;
+          PA_MLA_FSTEP(k + 5, s_kv0, s_kv4);
+        }
+#undef PA_MLA_FSTEP
+      }
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no loads in flight into the stages
       __syncthreads();
     }
   }
 
-  // ---- epilogue: wave w writes dims [64w, 64w+64) of the R rows; wave 0 the stats
-  const float ltot = xor32_sum(xor16_sum(lsum));
+  // ---- epilogue: the reducing wave publishes the rows' sums and maxima; wave w
+  // writes dims [64w, 64w+64) of the R rows, the reducing wave the stats
+  if (w == kNS) {
+    const float lt = xor32_sum(xor16_sum(lsum));
+    if (lg == 0) {
+      s_x->stat[l16][0] = lt;
+      s_x->stat[l16][1] = m;
+      s_x->stat[l16][2] = true_max;
+    }
+  }
+  __syncthreads();
+  const float ltot = s_x->stat[l16][0];
+  const float mref = s_x->stat[l16][1], tmx = s_x->stat[l16][2];
+  __syncthreads();  // the stats are read before the next range overwrites them
   if (!row_ok) return;
   const bool empty = !(ltot > 0.f);
   const float scale = empty ? 0.f : p.v_scale / ltot;
@@ -1229,9 +1291,9 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
       *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + c * p.o_split_stride + rid * kDvo + dim) = v;
     }
   }
-  if (w == 0 && lg == 0) {
-    const float lse = empty ? -INFINITY : (m + fast_log2(ltot)) * kLn2;
-    const float mx = empty ? -INFINITY : true_max * kLn2;
+  if (w == kNS && lg == 0) {
+    const float lse = empty ? -INFINITY : (mref + fast_log2(ltot)) * kLn2;
+    const float mx = empty ? -INFINITY : tmx * kLn2;
     if (to_ws) {
       p.ws_lse[wrow] = lse;
       p.ws_mx[wrow] = mx;
@@ -1257,13 +1319,14 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_narrow_kernel(AttnParams p, 
   __shared__ __align__(16) uint8_t s_kv5[NST > 5 ? STAGE : 16];
   __shared__ __align__(16) uint8_t s_wide[FP8 ? kStage2 : 16];  // fp8: the widened tile
   __shared__ __align__(16) f32x4_t s_part[kNS][2][64];           // partial scores
+  __shared__ __align__(16) NarrowX s_x;
   __shared__ int s_pages[kPageWinM];
   if (p.bal_blocks > 0) {
     BalCursor cur;
     if (!cur.start(p, blockIdx.x)) return;
     do {
       mla_narrow_range<FP8>(p, cur.b, cur.g, cur.L, cur.j0(p), cur.j1(p), !cur.whole(), cur.slot(p), 0,
-                            s_kv0, s_kv1, s_kv2, s_kv3, s_kv4, s_kv5, s_wide, s_part, s_pages);
+                            s_kv0, s_kv1, s_kv2, s_kv3, s_kv4, s_kv5, s_wide, s_part, &s_x, s_pages);
     } while (cur.next(p));
     return;
   }
@@ -1276,7 +1339,7 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_narrow_kernel(AttnParams p, 
   bool to_ws;
   if (!mla_item_range(p, b, c, L, j0, j1, to_ws)) return;
   mla_narrow_range<FP8>(p, b, g, L, j0, j1, to_ws, (int64_t)(b * p.num_kv_heads + g) * p.max_chunks + c,
-                        c, s_kv0, s_kv1, s_kv2, s_kv3, s_kv4, s_kv5, s_wide, s_part, s_pages);
+                        c, s_kv0, s_kv1, s_kv2, s_kv3, s_kv4, s_kv5, s_wide, s_part, &s_x, s_pages);
 }
 
 hipError_t launch_rows(const AttnParams& p, hipStream_t stream) {

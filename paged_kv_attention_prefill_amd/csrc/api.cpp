@@ -280,8 +280,9 @@ Plan make_plan(const AttnParams& p, uint32_t flags) {
     const int ct = mla_chunk_tokens(p, flags);
     if (ct > 0 && pa::mla_balanced_ok(p)) {
       // one row tile per request: balanced split over one wave of workgroups
-      static int occ[2][2] = {};
-      int& o = occ[p.kv_dtype == PA_FP8_E4M3][p.q_len * p.group <= 16];
+      static int occ[2][4] = {};
+      const int R = p.q_len * p.group;
+      int& o = occ[p.kv_dtype == PA_FP8_E4M3][R <= 16 ? 0 : R <= 32 ? 1 : R <= 64 ? 2 : 3];
       if (o <= 0) o = pa::mla_blocks_per_cu(p);
       pl.bal_unit = 32;
       pl.bal_blocks = o * device_cus();

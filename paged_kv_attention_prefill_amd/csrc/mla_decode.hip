@@ -20,8 +20,6 @@
 //     row-major from LDS.
 // Chunks of long KV batches leave partial states (O normalised by the chunk's
 // own sum, LSE, max) in the workspace for the chunk-merge launch.
-#include <type_traits>
-
 #include "balance.h"
 #include "mfma_common.h"
 
@@ -470,6 +468,81 @@ __device__ __forceinline__ void lds_write2_b128(uint32_t a0, i32x4_t v0, uint32_
       : "v"(a0), "v"(v0), "v"(a1), "v"(v1)
       : "memory");
 }
+// Four 16-byte reads at a0, a0 + 18432, a1, a1 + 18432.
+__device__ __forceinline__ void lds_read4_b128(uint32_t a0, uint32_t a1, i32x4_t (&r)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:18432\n\t"
+      "ds_read_b128 %2, %5\n\t"
+      "ds_read_b128 %3, %5 offset:18432\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(a0), "v"(a1)
+      : "memory");
+}
+// Two 16-byte reads at a0, a0 + 18432.
+__device__ __forceinline__ void lds_read2x_b128(uint32_t a0, i32x4_t (&r)[2]) {
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %2 offset:18432\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1])
+      : "v"(a0)
+      : "memory");
+}
+// Partial-score reads of a row block: 2 KS 16-byte reads at base + S k + 1024 st
+// (k < KS, st < 2), completed on return.
+template <int KS, int S>
+__device__ __forceinline__ void lds_read_parts(uint32_t base, f32x4_t (&r)[KS][2]) {
+  if constexpr (KS == 2) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:1024\n\t"
+        "ds_read_b128 %2, %4 offset:%5\n\t"
+        "ds_read_b128 %3, %4 offset:%6\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[1][0]), "=&v"(r[1][1])
+        : "v"(base), "i"(S), "i"(S + 1024)
+        : "memory");
+  } else {
+    static_assert(KS == 4, "2 or 4 slices");
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b128 %2, %8 offset:%9\n\t"
+        "ds_read_b128 %3, %8 offset:%10\n\t"
+        "ds_read_b128 %4, %8 offset:%11\n\t"
+        "ds_read_b128 %5, %8 offset:%12\n\t"
+        "ds_read_b128 %6, %8 offset:%13\n\t"
+        "ds_read_b128 %7, %8 offset:%14\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0][0]), "=&v"(r[0][1]), "=&v"(r[1][0]), "=&v"(r[1][1]), "=&v"(r[2][0]), "=&v"(r[2][1]),
+          "=&v"(r[3][0]), "=&v"(r[3][1])
+        : "v"(base), "i"(S), "i"(S + 1024), "i"(2 * S), "i"(2 * S + 1024), "i"(3 * S), "i"(3 * S + 1024)
+        : "memory");
+  }
+}
+
+// A wave's partial scores: 16 bytes per lane at a and a + 1024, completed on return.
+__device__ __forceinline__ void lds_write_part(uint32_t a, f32x4_t v0, f32x4_t v1) {
+  asm volatile(
+      "ds_write_b128 %0, %1\n\t"
+      "ds_write_b128 %0, %2 offset:1024\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      :
+      : "v"(a), "v"(v0), "v"(v1)
+      : "memory");
+}
+
+// One 4-byte write (an exchange word next to the stages), completed on return.
+__device__ __forceinline__ void lds_write_b32(uint32_t a, int v) {
+  asm volatile(
+      "ds_write_b32 %0, %1\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      :
+      : "v"(a), "v"(v)
+      : "memory");
+}
 // Two 16-byte reads.
 __device__ __forceinline__ void lds_read2_b128(uint32_t a0, uint32_t a1, i32x4_t& r0, i32x4_t& r1) {
   asm volatile(
@@ -587,27 +660,32 @@ struct PageLanes {
   }
 };
 
-template <bool FP8>
-__device__ __forceinline__ void dma_tile_page(const AttnParams& p, const int* s_pages, uint8_t* stage,
-                                              int jb, int we, int wbP, const PageLanes<FP8>& pl, int w) {
-  using E = typename std::conditional<FP8, uint8_t, uint16_t>::type;
-  const E* kbase = static_cast<const E*>(p.k);
-  constexpr int kD = FP8 ? kDma8 : kDma;
-  const uint32_t rel = (uint32_t)(jb - wbP);
-  const uint32_t pi = div_by_magic(rel, p.page_magic);
-  const int page = __builtin_amdgcn_readfirstlane(s_pages[pi]);
-  const uint64_t base = (uint64_t)(uint32_t)page * (uint64_t)p.ks0 +
-                        (uint64_t)((rel - pi * (uint32_t)p.page_size) * (uint32_t)p.ks1);
-  const int last = we - 1 - jb;  // rows past the range load the last valid row
-  const uint32_t ks1 = (uint32_t)p.ks1;
-#pragma unroll
-  for (int r = 0; r < PageLanes<FP8>::N; ++r) {
-    const int i = r * kNW2 + w;
-    const uint32_t off = (uint32_t)min(pl.row[r], last) * ks1 + pl.off[r];
-    if (i < kD)
-      __builtin_amdgcn_global_load_lds(kbase + base + off, (PA_LDS void*)(stage + 1024 * i), 16, 0, 0);
+// (plain functions, one per storage type: a template holding these builtins
+// fails to instantiate in the host compilation pass)
+#define PA_DMA_PAGE_BODY(E, KD, LANES)                                                        \
+  const E* kbase = static_cast<const E*>(p.k);                                                 \
+  const uint32_t rel = (uint32_t)(jb - wbP);                                                  \
+  const uint32_t pi = div_by_magic(rel, p.page_magic);                                        \
+  const int page = __builtin_amdgcn_readfirstlane(s_pages[pi]);                               \
+  const uint64_t base = (uint64_t)(uint32_t)page * (uint64_t)p.ks0 +                          \
+                        (uint64_t)((rel - pi * (uint32_t)p.page_size) * (uint32_t)p.ks1);     \
+  const int last = we - 1 - jb; /* rows past the range load the last valid row */            \
+  const uint32_t ks1 = (uint32_t)p.ks1;                                                       \
+  _Pragma("unroll") for (int r = 0; r < LANES::N; ++r) {                                      \
+    const int i = r * kNW2 + w;                                                               \
+    const uint32_t off = (uint32_t)min(pl.row[r], last) * ks1 + pl.off[r];                    \
+    if (i < KD)                                                                               \
+      __builtin_amdgcn_global_load_lds(kbase + base + off, (PA_LDS void*)(stage + 1024 * i), 16, 0, 0); \
   }
+__device__ __forceinline__ void dma_page_bf16(const AttnParams& p, const int* s_pages, uint8_t* stage, int jb,
+                                              int we, int wbP, const PageLanes<false>& pl, int w) {
+  PA_DMA_PAGE_BODY(uint16_t, kDma, PageLanes<false>)
 }
+__device__ __forceinline__ void dma_page_fp8(const AttnParams& p, const int* s_pages, uint8_t* stage, int jb,
+                                             int we, int wbP, const PageLanes<true>& pl, int w) {
+  PA_DMA_PAGE_BODY(uint8_t, kDma8, PageLanes<true>)
+}
+#undef PA_DMA_PAGE_BODY
 
 // fp8 stage -> bf16 tile (swizzled layout of the bf16 path); e4m3 codes widen
 // exactly to bf16.  Every thread converts whole 16-code pieces.
@@ -1071,8 +1149,7 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
 #pragma unroll
         for (int st2 = 0; st2 < 2; ++st2)
           sacc[st2] = mfma16<BF16>(__builtin_bit_cast(i16x8_t, kr[2 * u + st2]), qreg[u], sacc[st2]);
-      s_part[w][0][lane] = sacc[0];
-      s_part[w][1][lane] = sacc[1];
+      lds_write_part(lds_off(&s_part[w][0][lane]), sacc[0], sacc[1]);
     }
   };
   // V^T operands of dims 64w + 16d: two transposed 4x16 reads each (row rr and
@@ -1131,7 +1208,7 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
                                   pack2<BF16>(e[4], e[5]), pack2<BF16>(e[6], e[7]));
     lsum = sum2<BF16>(bits.x, sum2<BF16>(bits.y, sum2<BF16>(bits.z, sum2<BF16>(bits.w, lsum))));
     s_x->pb[lane] = as_i16x8(bits);
-    if (lane == 0) s_x->flag = any;
+    if (lane == 0) lds_write_b32(lds_off(&s_x->flag), any);
   };
   auto part_pv = [&](const i32x2_t (&vr)[8]) __attribute__((always_inline)) {
     if (__builtin_amdgcn_readfirstlane(s_x->flag)) {
@@ -1172,12 +1249,17 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
       const int wbP = wb * P;
       auto tile_at = [&](int k) { return ws + min(k, nk - 1) * kTK2; };
       auto dma = [&](uint8_t* stage, int jb) __attribute__((always_inline)) {
-        if (page_tiles)
-          dma_tile_page<FP8>(p, s_pages, stage, jb, we, wbP, plane, w);
-        else if constexpr (FP8)
-          dma_tile8(p, s_pages, stage, jb, we, wbP, g, w, lane);
-        else
-          dma_tile(p, s_pages, stage, jb, we, wbP, g, w, lane);
+        if constexpr (FP8) {
+          if (page_tiles)
+            dma_page_fp8(p, s_pages, stage, jb, we, wbP, plane, w);
+          else
+            dma_tile8(p, s_pages, stage, jb, we, wbP, g, w, lane);
+        } else {
+          if (page_tiles)
+            dma_page_bf16(p, s_pages, stage, jb, we, wbP, plane, w);
+          else
+            dma_tile(p, s_pages, stage, jb, we, wbP, g, w, lane);
+        }
       };
       dma(s_kv0, tile_at(0));
       dma(s_kv1, tile_at(1));
@@ -1342,6 +1424,389 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_narrow_kernel(AttnParams p, 
                         c, s_kv0, s_kv1, s_kv2, s_kv3, s_kv4, s_kv5, s_wide, s_part, &s_x, s_pages);
 }
 
+// ---------------------------------------------------------------------------
+// 17..64 rows per request: NRB = 2 or 4 row blocks of 16 rows.  Wave w takes
+// row block w % NRB and k-step slice w / NRB of the 576-dim contraction
+// (KS = 8 / NRB slices), so every wave computes partial scores; waves
+// 0..NRB-1 then each sum one row block's partials and run its online softmax;
+// every wave does PV for its 64 V dims over all row blocks.  The KV stream is
+// the narrow kernel's (direct loads, bare barriers, stage reads in asm); three
+// bf16 stages or five fp8 raw stages fit next to the 16 KB of partial scores.
+template <int NRB>
+struct MidX {
+  i16x8_t pb[NRB][64];    // P^T of each row block in the PV B-operand layout
+  float alpha[NRB][16];   // rescale factors of the current tile (valid when flag)
+  float stat[NRB][16][3]; // final: row sum, reference max, running max
+  int flag[NRB];
+};
+template <bool FP8>
+constexpr int kMidStages = FP8 ? 5 : 3;
+
+template <bool FP8, int NRB>
+__device__ __forceinline__ void mla_mid_range(const AttnParams& p, int b, int g, int L, int j0, int j1,
+                                              bool to_ws, int64_t wslot, int c, uint8_t* s_kv0,
+                                              uint8_t* s_kv1, uint8_t* s_kv2, uint8_t* s_kv3,
+                                              uint8_t* s_kv4, uint8_t* s_wide,
+                                              f32x4_t (*s_part)[2][64], MidX<NRB>* s_x, int* s_pages) {
+  constexpr int NST = kMidStages<FP8>;
+  constexpr int KS = kNW2 / NRB;                  // k-step slices per row block
+  constexpr int KK = kDqk / 32;                   // 18 k-steps
+  constexpr int KMAX = (KK + KS - 1) / KS;        // k-steps of the largest slice
+  static_assert(KS * NRB == kNW2 && KMAX >= 3, "wave split");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int rbw = w % NRB, ksw = w / NRB;
+  const int k0 = ksw * KK / KS, nks = (ksw + 1) * KK / KS - k0;  // this wave's k-steps
+  const int kb = p.broadcast ? 0 : b;
+  const int pbeg = p.kv_indptr[kb];
+  const int R = p.q_len * p.group;
+  // row of this lane in its wave's row block (scores, softmax)
+  const int row = 16 * rbw + l16;
+  const bool row_ok = row < R;
+  int lim = j1;
+  if (row_ok && p.causal) lim = min(lim, L - p.q_len + row / p.group + 1);
+  if (!row_ok) lim = INT_MIN;
+  int lo = row_ok ? lim : INT_MAX;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) lo = min(lo, __shfl_xor(lo, off, 64));
+  const int wave_lim_min = __builtin_amdgcn_readfirstlane(lo);
+  int jhi = j1;
+  if (p.causal) jhi = min(j1, L - p.q_len + (R - 1) / p.group + 1);
+
+  // Q^T operands of this wave's k-steps k0 .. k0 + nks - 1
+  i16x8_t qreg[KMAX];
+  {
+    const int qi = row_ok ? row / p.group : 0, qh = row_ok ? row % p.group : 0;
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) +
+                         ((int64_t)(b * p.q_len + qi) * p.num_qo_heads + (int64_t)g * p.group + qh) * kDqk +
+                         8 * lg;
+#pragma unroll
+    for (int u = 0; u < KMAX; ++u)
+      qreg[u] = row_ok && u < nks ? *reinterpret_cast<const i16x8_t*>(qp + 32 * (k0 + u))
+                                  : i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+
+  // softmax state of row block w, kept by wave w < NRB
+  float m = -INFINITY, lsum = 0.f, true_max = -INFINITY;
+  f32x4_t oacc[NRB][4];  // row block rb: dims 64w + 16d + 4lg + i, row 16 rb + l16
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) oacc[rb][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const float qk_scale = p.sm_scale * p.k_scale * kLog2e;
+  const int P = p.page_size;
+
+  auto part_s = [&](const uint8_t* kv) __attribute__((always_inline)) {
+    f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    const int sw = mla_swz(l16);
+    const uint32_t kbase = lds_off(kv) + l16 * kKP2;
+    auto kaddr = [&](int kk) {
+      const int piece = 4 * kk + lg;
+      return kbase + 16 * ((piece & ~7) | ((piece & 7) ^ sw));
+    };
+    // whole groups of three k-steps, then a rest of one or two
+#pragma unroll
+    for (int j = 0; j + 3 <= KMAX; j += 3) {
+      if (j + 3 <= nks) {
+        i32x4_t kr[6];
+        lds_read6_b128(kaddr(k0 + j), kaddr(k0 + j + 1), kaddr(k0 + j + 2), kr);
+#pragma unroll
+        for (int u = 0; u < 3; ++u)
+#pragma unroll
+          for (int st2 = 0; st2 < 2; ++st2)
+            sacc[st2] = mfma16<BF16>(__builtin_bit_cast(i16x8_t, kr[2 * u + st2]), qreg[j + u], sacc[st2]);
+      }
+    }
+    if constexpr (KMAX % 3 != 0) {
+      constexpr int j = KMAX / 3 * 3;
+      if (nks - j == 2) {
+        i32x4_t kr[4];
+        lds_read4_b128(kaddr(k0 + j), kaddr(k0 + j + 1), kr);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int st2 = 0; st2 < 2; ++st2)
+            sacc[st2] = mfma16<BF16>(__builtin_bit_cast(i16x8_t, kr[2 * u + st2]), qreg[j + u], sacc[st2]);
+      } else if (nks - j == 1) {
+        i32x4_t kr[2];
+        lds_read2x_b128(kaddr(k0 + j), kr);
+#pragma unroll
+        for (int st2 = 0; st2 < 2; ++st2)
+          sacc[st2] = mfma16<BF16>(__builtin_bit_cast(i16x8_t, kr[st2]), qreg[j], sacc[st2]);
+      }
+    }
+    lds_write_part(lds_off(&s_part[w][0][lane]), sacc[0], sacc[1]);
+  };
+  auto part_v = [&](const uint8_t* kv, i32x2_t (&vr)[8]) __attribute__((always_inline)) {
+    const int rr = 4 * lg + (l16 >> 2);
+    const int vsw = mla_swz(rr);
+    const int hp = (l16 & 3) >> 1;
+    uint32_t vb[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int piece = 2 * (4 * w + d) + hp;
+      vb[d] = lds_off(kv) + rr * kKP2 + 16 * ((piece & ~7) | ((piece & 7) ^ vsw)) + 8 * (l16 & 1);
+    }
+    lds_read8_tr(vb[0], vb[1], vb[2], vb[3], vr);
+  };
+  // wave w < NRB: row block w
+  auto part_r = [&](int jb) __attribute__((always_inline)) {
+    // s_part[w + NRB k][st][lane] for the KS slices k (2 KB per wave)
+    f32x4_t pr[KS][2];
+    lds_read_parts<KS, 2048 * NRB>(lds_off(&s_part[w][0][lane]), pr);
+    f32x4_t ssum[2] = {pr[0][0], pr[0][1]};
+#pragma unroll
+    for (int k = 1; k < KS; ++k) {
+      ssum[0] += pr[k][0];
+      ssum[1] += pr[k][1];
+    }
+    if (jb + kTK2 > wave_lim_min) {
+#pragma unroll
+      for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (jb + 16 * st2 + 4 * lg + i >= lim) ssum[st2][i] = -INFINITY;
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, ssum[st2][i]);
+    tmax = xor32_max(xor16_max(tmax)) * qk_scale;
+    true_max = fmaxf(true_max, tmax);
+    const bool grow = tmax > m + 8.f;
+    const bool any = __ballot(grow) != 0;
+    if (any) {
+      const float mnew = grow ? tmax : m;
+      const float alpha = fast_exp2((m == -INFINITY ? -INFINITY : m) - (mnew == -INFINITY ? 0.f : mnew));
+      const float a = grow ? alpha : 1.f;
+      lsum *= a;
+      m = mnew;
+      if (lg == 0) s_x->alpha[w][l16] = a;
+    }
+    const float nmref = -(m == -INFINITY ? 0.f : m);
+    float e[8];
+#pragma unroll
+    for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[4 * st2 + i] = fast_exp2(fmaf(ssum[st2][i], qk_scale, nmref));
+    const uint4 bits = make_uint4(pack2<BF16>(e[0], e[1]), pack2<BF16>(e[2], e[3]),
+                                  pack2<BF16>(e[4], e[5]), pack2<BF16>(e[6], e[7]));
+    lsum = sum2<BF16>(bits.x, sum2<BF16>(bits.y, sum2<BF16>(bits.z, sum2<BF16>(bits.w, lsum))));
+    s_x->pb[w][lane] = as_i16x8(bits);
+    if (lane == 0) lds_write_b32(lds_off(&s_x->flag[w]), any);
+  };
+  auto part_pv = [&](const i32x2_t (&vr)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      if (__builtin_amdgcn_readfirstlane(s_x->flag[rb])) {
+        const float a = s_x->alpha[rb][l16];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) oacc[rb][d] *= a;
+      }
+      const i16x8_t pb = s_x->pb[rb][lane];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const i32x4_t v4 = {vr[2 * d].x, vr[2 * d].y, vr[2 * d + 1].x, vr[2 * d + 1].y};
+        oacc[rb][d] = mfma16<BF16>(__builtin_bit_cast(i16x8_t, v4), pb, oacc[rb][d]);
+      }
+    }
+  };
+
+  const bool page_tiles = P % kTK2 == 0 && j0 % kTK2 == 0;
+  PageLanes<FP8> plane;
+  if (page_tiles) plane.init(p, g, w, lane);
+  if (jhi > j0) {
+    const int pfirst = j0 / P, plast = (jhi - 1) / P;
+    for (int wb = pfirst; wb <= plast; wb += kPageWinM) {
+      const int npw = min(kPageWinM, plast - wb + 1);
+      __syncthreads();  // the previous window's readers are done
+      for (int i = tid; i < npw; i += 64 * kNW2) s_pages[i] = p.kv_indices[pbeg + wb + i];
+      __syncthreads();
+      const int ws = max(j0, wb * P), we = min(jhi, (wb + npw) * P);
+      const int nk = (we - ws + kTK2 - 1) / kTK2;
+      // tile k in stage k % NST; a wave issues at least kMinDma direct loads per
+      // tile, so vmcnt(kWait) leaves at most NST - 2 tiles in flight
+      constexpr int kMinDma = (FP8 ? kDma8 : kDma) / kNW2;
+      constexpr int kWait = (NST - 2) * kMinDma;
+      static_assert(kWait < 64, "vmcnt field");
+      constexpr int kWaitImm = (kWait & 0xF) | ((kWait >> 4) << 14) | 0x70 | 0xF00;
+      const int wbP = wb * P;
+      auto tile_at = [&](int k) { return ws + min(k, nk - 1) * kTK2; };
+      auto dma = [&](uint8_t* stage, int jb) __attribute__((always_inline)) {
+        if constexpr (FP8) {
+          if (page_tiles)
+            dma_page_fp8(p, s_pages, stage, jb, we, wbP, plane, w);
+          else
+            dma_tile8(p, s_pages, stage, jb, we, wbP, g, w, lane);
+        } else {
+          if (page_tiles)
+            dma_page_bf16(p, s_pages, stage, jb, we, wbP, plane, w);
+          else
+            dma_tile(p, s_pages, stage, jb, we, wbP, g, w, lane);
+        }
+      };
+      dma(s_kv0, tile_at(0));
+      dma(s_kv1, tile_at(1));
+      if constexpr (NST > 3) dma(s_kv2, tile_at(2));
+      if constexpr (NST > 4) dma(s_kv3, tile_at(3));
+      if constexpr (!FP8) {
+#define PA_MLA_MSTEP(K, CUR, NEXT)                                                            \
+  {                                                                                         \
+    __builtin_amdgcn_s_waitcnt(kWaitImm); /* tile K's direct loads are done */              \
+    lds_barrier();                                                                           \
+    dma(NEXT, tile_at((K) + NST - 1));                                                      \
+    part_s(CUR);                                                                            \
+    i32x2_t vr[8];                                                                          \
+    part_v(CUR, vr);                                                                        \
+    lds_barrier();                                                                           \
+    if (w < NRB) part_r(ws + (K) * kTK2);                                                   \
+    lds_barrier();                                                                           \
+    part_pv(vr);                                                                            \
+  }
+        static_assert(NST == 3, "bf16 stage rotation");
+        for (int k = 0; k < nk; k += 3) {
+          PA_MLA_MSTEP(k, s_kv0, s_kv2);
+          if (k + 1 >= nk) break;
+          PA_MLA_MSTEP(k + 1, s_kv1, s_kv0);
+          if (k + 2 >= nk) break;
+          PA_MLA_MSTEP(k + 2, s_kv2, s_kv1);
+        }
+#undef PA_MLA_MSTEP
+      } else {
+        // fp8: as in the narrow kernel, the bf16 tile buffer holds tile K during
+        // step K and tile K+1 is widened into it after the reducing waves' softmax
+        __builtin_amdgcn_s_waitcnt(kWaitImm);  // tile 0's direct loads are done
+        lds_barrier();
+        convert_tile(s_kv0, s_wide, tid);
+#define PA_MLA_MFSTEP(K, NEXTRAW, DST)                                                        \
+  {                                                                                         \
+    lds_barrier();                                                                           \
+    dma(DST, tile_at((K) + NST - 1));                                                       \
+    part_s(s_wide);                                                                         \
+    i32x2_t vr[8];                                                                          \
+    part_v(s_wide, vr);                                                                     \
+    __builtin_amdgcn_s_waitcnt(kWaitImm); /* tile K+1's direct loads are done */            \
+    lds_barrier();                                                                           \
+    if (w < NRB) part_r(ws + (K) * kTK2);                                                   \
+    convert_tile(NEXTRAW, s_wide, tid);                                                     \
+    lds_barrier();                                                                           \
+    part_pv(vr);                                                                            \
+  }
+        static_assert(NST == 5, "fp8 stage rotation");
+        for (int k = 0; k < nk; k += 5) {
+          PA_MLA_MFSTEP(k, s_kv1, s_kv4);
+          if (k + 1 >= nk) break;
+          PA_MLA_MFSTEP(k + 1, s_kv2, s_kv0);
+          if (k + 2 >= nk) break;
+          PA_MLA_MFSTEP(k + 2, s_kv3, s_kv1);
+          if (k + 3 >= nk) break;
+          PA_MLA_MFSTEP(k + 3, s_kv4, s_kv2);
+          if (k + 4 >= nk) break;
+          PA_MLA_MFSTEP(k + 4, s_kv0, s_kv3);
+        }
+#undef PA_MLA_MFSTEP
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no loads in flight into the stages
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: waves 0..NRB-1 publish their row block's sums and maxima;
+  // wave w writes dims [64w, 64w+64) of every row
+  if (w < NRB) {
+    const float lt = xor32_sum(xor16_sum(lsum));
+    if (lg == 0) {
+      s_x->stat[w][l16][0] = lt;
+      s_x->stat[w][l16][1] = m;
+      s_x->stat[w][l16][2] = true_max;
+    }
+  }
+  __syncthreads();
+  float ltot[NRB], mref[NRB], tmx[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    ltot[rb] = s_x->stat[rb][l16][0];
+    mref[rb] = s_x->stat[rb][l16][1];
+    tmx[rb] = s_x->stat[rb][l16][2];
+  }
+  __syncthreads();  // the stats are read before the next range overwrites them
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int orow = 16 * rb + l16;
+    if (orow >= R) continue;
+    const bool empty = !(ltot[rb] > 0.f);
+    const float scale = empty ? 0.f : p.v_scale / ltot[rb];
+    const int64_t rid = (int64_t)(b * p.q_len + orow / p.group) * p.num_qo_heads + (int64_t)g * p.group +
+                        orow % p.group;
+    const int64_t wrow = wslot * p.ws_rows + orow;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int dim = 64 * w + 16 * d + 4 * lg;
+      const float x0 = oacc[rb][d][0] * scale, x1 = oacc[rb][d][1] * scale;
+      const float x2 = oacc[rb][d][2] * scale, x3 = oacc[rb][d][3] * scale;
+      if (to_ws) {
+        *reinterpret_cast<float4*>(p.ws_o + wrow * kDvo + dim) = make_float4(x0, x1, x2, x3);
+      } else if (p.o_dtype == F32) {
+        *reinterpret_cast<float4*>(static_cast<float*>(p.o) + c * p.o_split_stride + rid * kDvo + dim) =
+            make_float4(x0, x1, x2, x3);
+      } else {
+        const uint2 v = p.o_dtype == F16 ? make_uint2(pack2<F16>(x0, x1), pack2<F16>(x2, x3))
+                                         : make_uint2(pack2<BF16>(x0, x1), pack2<BF16>(x2, x3));
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + c * p.o_split_stride + rid * kDvo + dim) = v;
+      }
+    }
+    if (w == rb && lg == 0) {
+      const float lse = empty ? -INFINITY : (mref[rb] + fast_log2(ltot[rb])) * kLn2;
+      const float mx = empty ? -INFINITY : tmx[rb] * kLn2;
+      if (to_ws) {
+        p.ws_lse[wrow] = lse;
+        p.ws_mx[wrow] = mx;
+      } else {
+        const int64_t sidx = c * p.s_split_stride + rid;
+        if (p.lse) p.lse[sidx] = lse;
+        if (p.mx) p.mx[sidx] = mx;
+      }
+    }
+  }
+}
+
+template <bool FP8, int NRB>
+__global__ __launch_bounds__(64 * kNW2, 1) void mla_mid_kernel(AttnParams p, int ngroups) {
+  constexpr int STAGE = FP8 ? kStage8 : kStage2;
+  constexpr int NST = kMidStages<FP8>;
+  __shared__ __align__(16) uint8_t s_kv0[STAGE];
+  __shared__ __align__(16) uint8_t s_kv1[STAGE];
+  __shared__ __align__(16) uint8_t s_kv2[STAGE];
+  __shared__ __align__(16) uint8_t s_kv3[NST > 3 ? STAGE : 16];
+  __shared__ __align__(16) uint8_t s_kv4[NST > 4 ? STAGE : 16];
+  __shared__ __align__(16) uint8_t s_wide[FP8 ? kStage2 : 16];  // fp8: the widened tile
+  __shared__ __align__(16) f32x4_t s_part[kNW2][2][64];          // partial scores
+  __shared__ __align__(16) MidX<NRB> s_x;
+  __shared__ int s_pages[kPageWinM];
+  if (p.bal_blocks > 0) {
+    BalCursor cur;
+    if (!cur.start(p, blockIdx.x)) return;
+    do {
+      mla_mid_range<FP8, NRB>(p, cur.b, cur.g, cur.L, cur.j0(p), cur.j1(p), !cur.whole(), cur.slot(p), 0,
+                              s_kv0, s_kv1, s_kv2, s_kv3, s_kv4, s_wide, s_part, &s_x, s_pages);
+    } while (cur.next(p));
+    return;
+  }
+  const int gi = blockIdx.x;
+  if (gi >= ngroups) return;
+  const int b = gi / (p.num_kv_heads * p.max_chunks);
+  const int g = (gi / p.max_chunks) % p.num_kv_heads;
+  const int c = gi % p.max_chunks;
+  int L, j0, j1;
+  bool to_ws;
+  if (!mla_item_range(p, b, c, L, j0, j1, to_ws)) return;
+  mla_mid_range<FP8, NRB>(p, b, g, L, j0, j1, to_ws, (int64_t)(b * p.num_kv_heads + g) * p.max_chunks + c,
+                          c, s_kv0, s_kv1, s_kv2, s_kv3, s_kv4, s_wide, s_part, &s_x, s_pages);
+}
+
 hipError_t launch_rows(const AttnParams& p, hipStream_t stream) {
   const int R = p.q_len * p.group;
   const int nrt = (R + kRT2 - 1) / kRT2;
@@ -1355,6 +1820,16 @@ hipError_t launch_rows(const AttnParams& p, hipStream_t stream) {
       mla_narrow_kernel<true><<<blocks, 64 * kNW2, 0, stream>>>(q, ngroups);
     else
       mla_narrow_kernel<false><<<blocks, 64 * kNW2, 0, stream>>>(q, ngroups);
+  } else if (R <= 2 * kRW) {
+    if (p.kv_dtype == FP8)
+      mla_mid_kernel<true, 2><<<blocks, 64 * kNW2, 0, stream>>>(q, ngroups);
+    else
+      mla_mid_kernel<false, 2><<<blocks, 64 * kNW2, 0, stream>>>(q, ngroups);
+  } else if (R <= 4 * kRW) {
+    if (p.kv_dtype == FP8)
+      mla_mid_kernel<true, 4><<<blocks, 64 * kNW2, 0, stream>>>(q, ngroups);
+    else
+      mla_mid_kernel<false, 4><<<blocks, 64 * kNW2, 0, stream>>>(q, ngroups);
   } else if (p.kv_dtype == FP8) {
     mla_rows_kernel<true><<<blocks, 64 * kNW2, 0, stream>>>(q, nrt, ngroups);
   } else {
@@ -1414,11 +1889,15 @@ bool mla_balanced_ok(const AttnParams& p) { return mla_rows_path(p) && p.q_len *
 
 int mla_blocks_per_cu(const AttnParams& p) {
   const bool fp8 = p.kv_dtype == FP8;
-  const bool narrow = p.q_len * p.group <= kRW;
-  const void* f = narrow ? (fp8 ? reinterpret_cast<const void*>(&mla_narrow_kernel<true>)
-                                : reinterpret_cast<const void*>(&mla_narrow_kernel<false>))
-                         : (fp8 ? reinterpret_cast<const void*>(&mla_rows_kernel<true>)
-                                : reinterpret_cast<const void*>(&mla_rows_kernel<false>));
+  const int R = p.q_len * p.group;
+  const void* f = R <= kRW       ? (fp8 ? reinterpret_cast<const void*>(&mla_narrow_kernel<true>)
+                                        : reinterpret_cast<const void*>(&mla_narrow_kernel<false>))
+                  : R <= 2 * kRW ? (fp8 ? reinterpret_cast<const void*>(&mla_mid_kernel<true, 2>)
+                                        : reinterpret_cast<const void*>(&mla_mid_kernel<false, 2>))
+                  : R <= 4 * kRW ? (fp8 ? reinterpret_cast<const void*>(&mla_mid_kernel<true, 4>)
+                                        : reinterpret_cast<const void*>(&mla_mid_kernel<false, 4>))
+                                 : (fp8 ? reinterpret_cast<const void*>(&mla_rows_kernel<true>)
+                                        : reinterpret_cast<const void*>(&mla_rows_kernel<false>));
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 64 * kNW2, 0) != hipSuccess || n <= 0) {
     (void)hipGetLastError();

@@ -247,11 +247,15 @@ def test_mla_row_tiles_and_page_sizes(heads, q_len, page_size):
 
 @pytest.mark.parametrize("heads,q_len,page_size,dt", [(16, 1, 32, W.DT_BF16), (8, 2, 96, W.DT_BF16),
                                                       (16, 1, 32, W.DT_FP8), (4, 3, 96, W.DT_FP8),
-                                                      (16, 1, 24, W.DT_FP8)])
+                                                      (16, 1, 24, W.DT_FP8),
+                                                      (16, 2, 96, W.DT_BF16), (16, 4, 32, W.DT_FP8),
+                                                      (12, 3, 24, W.DT_BF16), (10, 3, 64, W.DT_FP8),
+                                                      (16, 4, 64, W.DT_BF16)])
 def test_mla_narrow_page_sizes(heads, q_len, page_size, dt):
-    # up to 16 rows per request: page sizes that hold whole 32-token tiles (32, 96:
-    # the tile's page offset is uniform) and one that does not (24); long enough
-    # that the KV is split over workgroups
+    # up to 16 rows per request (one row block) and 17..64 (two or four row blocks
+    # sharing the contraction over waves): page sizes that hold whole 32-token
+    # tiles (32, 64, 96: the tile's page offset is uniform) and one that does not
+    # (24); long enough that the KV is split over workgroups
     label = f"MLA narrow h{heads} q{q_len} page {page_size} dt {dt}"
     print(label, flush=True)
     w = mla_build(950 + heads + page_size + dt, heads, q_len, [0, 31, 33, 3000, 4500, 96 * 20], page_size,

@@ -7,8 +7,8 @@
 //   s_out = m + ln(sum_c w_c); -inf states carry no weight; all -inf -> 0, -inf.
 //
 // HBM-bound: each row's S x D partials are read once (16-byte loads of four
-// fp32 elements per lane, issued eight states at a time so their latencies
-// overlap), the S LSEs once per lane from cache.
+// fp32 elements per lane, issued eight states at a time together with their
+// LSEs, folded by a running maximum so a block of states needs one round trip).
 #include "device_common.h"
 
 namespace pa {
@@ -50,23 +50,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const void* v, const float* 
   const int li = threadIdx.x % tpr;
   if (threadIdx.x >= rpb * tpr || row >= rows) return;
   const int d0 = li * 4;
-  // loads are issued in unrolled blocks of BLK states so their latencies overlap
+  // one pass over blocks of BLK states: their LSEs and partials are loaded
+  // together (one round trip per block) and folded into a running maximum m,
+  // weight sum and accumulator, rescaled when m grows
   constexpr int BLK = 8;
-  float m = -INFINITY;
-  for (int c0 = 0; c0 < S; c0 += BLK) {
-    float ls[BLK];
-#pragma unroll
-    for (int k = 0; k < BLK; ++k) ls[k] = c0 + k < S ? s[(c0 + k) * s_ss + row] : -INFINITY;
-#pragma unroll
-    for (int k = 0; k < BLK; ++k) m = fmaxf(m, ls[k]);
-  }
+  float m = -INFINITY, wsum = 0.f;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  if (m == -INFINITY) {
-    store4<OT>(out, row * D + d0, acc);
-    if (s_out && li == 0) s_out[row] = -INFINITY;
-    return;
-  }
-  float wsum = 0.f;
   for (int c0 = 0; c0 < S; c0 += BLK) {
     float ls[BLK];
     float x[BLK][4];
@@ -80,13 +69,28 @@ __global__ __launch_bounds__(256) void merge_kernel(const void* v, const float* 
         x[k][0] = x[k][1] = x[k][2] = x[k][3] = 0.f;
       }
     }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < BLK; ++k) bm = fmaxf(bm, ls[k]);
+    const float mn = fmaxf(m, bm);
+    if (mn == -INFINITY) continue;  // every state so far is empty
+    const float a = m == -INFINITY ? 0.f : fast_exp2((m - mn) * kLog2e);
+    wsum *= a;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] *= a;
 #pragma unroll
     for (int k = 0; k < BLK; ++k) {
-      const float w = ls[k] == -INFINITY ? 0.f : fast_exp2((ls[k] - m) * kLog2e);
+      const float w = ls[k] == -INFINITY ? 0.f : fast_exp2((ls[k] - mn) * kLog2e);
       wsum += w;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, x[k][i], acc[i]);
     }
+    m = mn;
+  }
+  if (m == -INFINITY) {
+    store4<OT>(out, row * D + d0, acc);
+    if (s_out && li == 0) s_out[row] = -INFINITY;
+    return;
   }
   const float inv = 1.f / wsum;
 #pragma unroll
@@ -147,46 +151,48 @@ __global__ __launch_bounds__(256) void chunk_merge_kernel(AttnParams p, int tpr)
   if (nch <= 1) return;
   const int D = p.dvo;
   const int d0 = li * 4;
-  // loads are issued in unrolled blocks of 8 chunks so their latencies overlap
+  // one pass: the LSE, max and O of a block of 8 partial states are loaded
+  // together and folded into a running (M, weight sum, acc) that is rescaled
+  // when M grows, so the loads of a row need a single round trip
   constexpr int BLK = 8;
   float M = -INFINITY, MX = -INFINITY;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
   for (int c0 = 0; c0 < nch; c0 += BLK) {
     float ls[BLK], ms[BLK];
+    float4 x[BLK];
 #pragma unroll
     for (int k = 0; k < BLK; ++k) {
       const bool ok = c0 + k < nch;
-      ls[k] = ok ? p.ws_lse[wrow0 + (int64_t)(c0 + k) * WR] : -INFINITY;
-      ms[k] = ok ? p.ws_mx[wrow0 + (int64_t)(c0 + k) * WR] : -INFINITY;
+      const int64_t wr = wrow0 + (int64_t)(c0 + k) * WR;
+      ls[k] = ok ? p.ws_lse[wr] : -INFINITY;
+      ms[k] = ok ? p.ws_mx[wr] : -INFINITY;
+      x[k] = ok ? *reinterpret_cast<const float4*>(p.ws_o + wr * D + d0) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    float bm = -INFINITY;
 #pragma unroll
     for (int k = 0; k < BLK; ++k) {
-      M = fmaxf(M, ls[k]);
+      bm = fmaxf(bm, ls[k]);
       MX = fmaxf(MX, ms[k]);
     }
-  }
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  if (M != -INFINITY) {
-    for (int c0 = 0; c0 < nch; c0 += BLK) {
-      float ls[BLK];
-      float4 x[BLK];
+    const float Mn = fmaxf(M, bm);
+    if (Mn == -INFINITY) continue;  // every state so far is empty
+    const float a = M == -INFINITY ? 0.f : fast_exp2((M - Mn) * kLog2e);
+    wsum *= a;
 #pragma unroll
-      for (int k = 0; k < BLK; ++k) {
-        const bool ok = c0 + k < nch;
-        ls[k] = ok ? p.ws_lse[wrow0 + (int64_t)(c0 + k) * WR] : -INFINITY;
-        x[k] = ok ? *reinterpret_cast<const float4*>(p.ws_o + (wrow0 + (int64_t)(c0 + k) * WR) * D + d0)
-                  : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+    for (int i = 0; i < 4; ++i) acc[i] *= a;
 #pragma unroll
-      for (int k = 0; k < BLK; ++k) {
-        const float w = ls[k] == -INFINITY ? 0.f : fast_exp2((ls[k] - M) * kLog2e);
-        wsum += w;
-        acc[0] = fmaf(w, x[k].x, acc[0]);
-        acc[1] = fmaf(w, x[k].y, acc[1]);
-        acc[2] = fmaf(w, x[k].z, acc[2]);
-        acc[3] = fmaf(w, x[k].w, acc[3]);
-      }
+    for (int k = 0; k < BLK; ++k) {
+      const float w = ls[k] == -INFINITY ? 0.f : fast_exp2((ls[k] - Mn) * kLog2e);
+      wsum += w;
+      acc[0] = fmaf(w, x[k].x, acc[0]);
+      acc[1] = fmaf(w, x[k].y, acc[1]);
+      acc[2] = fmaf(w, x[k].z, acc[2]);
+      acc[3] = fmaf(w, x[k].w, acc[3]);
     }
+    M = Mn;
+  }
+  if (M != -INFINITY) {
     const float inv = 1.f / wsum;
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] *= inv;

@@ -45,7 +45,7 @@ def test_c5_broadcast_split_decode_full():
 
 
 @pytest.mark.parametrize("h,ql,dt", [(16, 1, W.DT_BF16), (128, 4, W.DT_FP8), (128, 1, W.DT_BF16),
-                                     (16, 4, W.DT_FP8)])
+                                     (16, 4, W.DT_FP8), (16, 1, W.DT_FP8), (16, 4, W.DT_BF16)])
 def test_c4_mla_decode_full(h, ql, dt):
     run_sampled(W.config4(num_heads=h, q_len=ql, kv_dtype=dt), f"c4 full h{h} q{ql} {W.DT_NAMES[dt]}",
                 n=96)

@@ -179,6 +179,32 @@ def test_broadcast_equals_replicated():
     assert (to64(a["lse"]) - to64(b["lse"])).__abs__().max() <= tol_l
 
 
+@pytest.mark.parametrize("kind", ["gqa", "mla_narrow", "mla_mid"])
+def test_broadcast_decode_split(kind):
+    # one KV batch read by a few query batches, long enough that the decode
+    # kernels split it over workgroups (each query batch walks its own copy of
+    # the range); checked against the oracle and against replicated page lists
+    rng = np.random.default_rng(80 + len(kind))
+    if kind == "gqa":
+        w = W.build(rng, 81, "bcast gqa", q_lens=[1, 1], kv_lens=[3000], num_qo_heads=16,
+                    num_kv_heads=2, head_dim_qk=128, head_dim_vo=128, page_size=16,
+                    q_dtype=W.DT_BF16, kv_dtype=W.DT_BF16, kv_broadcast=True)
+    else:
+        ql = 1 if kind == "mla_narrow" else 2
+        w = W.build(rng, 82 + ql, f"bcast {kind}", q_lens=[ql] * 3, kv_lens=[5000], num_qo_heads=16,
+                    num_kv_heads=1, head_dim_qk=576, head_dim_vo=512, page_size=64,
+                    q_dtype=W.DT_BF16, kv_dtype=W.DT_BF16, shared_kv=True, causal=True,
+                    sm_scale=1.0 / np.sqrt(192.0), kv_broadcast=True)
+    print(kind, flush=True)
+    run_and_check(w, f"broadcast {kind}")
+    a = R.run(R.upload(w))
+    b = R.run(R.upload(W.replicate_broadcast(w)))
+    torch.cuda.synchronize()
+    tol_o, tol_l = tolerances(w)
+    assert np.abs(to64(a["o"]) - to64(b["o"])).max() <= tol_o
+    assert np.abs(to64(a["lse"]) - to64(b["lse"])).max() <= tol_l
+
+
 def test_prefill_entry_on_decode_shapes():
     # the prefill entry point with uniform q lengths computes what decode computes
     w = c4_small(16, 4, W.DT_BF16)

@@ -109,8 +109,9 @@ typedef struct {
   const int32_t* kv_indices;       /* [kv_indptr[num_kv_batches]] physical page ids */
   const int32_t* kv_last_page_len; /* [num_kv_batches], in [1, page_size] when n >= 1 */
   int32_t num_kv_batches;
-  int32_t max_kv_len_hint;  /* host value: >= every kv_len, or 0 if unknown; only sizes the
-                               grid (internal KV splitting needs it) */
+  int32_t max_kv_len_hint;  /* host value: >= every kv_len, or 0 if unknown; decides whether
+                               a decode splits the KV internally (0: never) and sizes the
+                               workspace; results do not depend on it */
 } pa_paged_kv;
 
 /* Decode: every query batch has the same number of queries, q_len. */
@@ -164,12 +165,15 @@ const char* pa_status_string(int status);
 
 /* Host-only: name of the kernel plan the call would run (a static string, e.g.
  * "gqa_decode_mfma" or "generic"), or NULL if the arguments are invalid.
- * Touches no GPU state. */
+ * Enqueues no GPU work (may make the device queries described below). */
 const char* paged_attn_decode_plan_name(const pa_decode_args* args);
 const char* paged_attn_prefill_plan_name(const pa_prefill_args* args);
 
 /* Host-only: bytes of device workspace the call needs (0 is possible).
- * Touches no GPU state. */
+ * Enqueues no GPU work.  The size of the internal KV split of a decode depends
+ * on the current device (its compute-unit count and the kernels' occupancy,
+ * read once per device with HIP device queries): query with the device current
+ * that the call will run on. */
 int paged_attn_decode_workspace_size(const pa_decode_args* args, size_t* bytes);
 int paged_attn_prefill_workspace_size(const pa_prefill_args* args, size_t* bytes);
 

@@ -111,7 +111,7 @@ typedef struct {
   int32_t num_kv_batches;
   int32_t max_kv_len_hint;  /* host value: >= every kv_len, or 0 if unknown; decides whether
                                a decode splits the KV internally (0: never) and sizes the
-                               workspace; results do not depend on it */
+                               workspace; it changes results only by rounding */
 } pa_paged_kv;
 
 /* Decode: every query batch has the same number of queries, q_len. */

@@ -543,7 +543,67 @@ __device__ __forceinline__ void lds_write_b32(uint32_t a, int v) {
       : "v"(a), "v"(v)
       : "memory");
 }
-// Two 16-byte reads.
+// P^T block (16 bytes), one row's rescale factor and the flag word, in one round trip.
+__device__ __forceinline__ void lds_read_pv(uint32_t apb, uint32_t aal, uint32_t afl, i32x4_t& pb, float& al,
+                                            int& fl) {
+  asm volatile(
+      "ds_read_b128 %0, %3\n\t"
+      "ds_read_b32 %1, %4\n\t"
+      "ds_read_b32 %2, %5\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(pb), "=&v"(al), "=&v"(fl)
+      : "v"(apb), "v"(aal), "v"(afl)
+      : "memory");
+}
+// Twelve 16-byte reads at a + 1024 k, k = 0..11 (the partial-score blocks).
+__device__ __forceinline__ void lds_read12_b128(uint32_t a, i32x4_t (&r)[12]) {
+  asm volatile(
+      "ds_read_b128 %0, %12\n\t"
+      "ds_read_b128 %1, %12 offset:1024\n\t"
+      "ds_read_b128 %2, %12 offset:2048\n\t"
+      "ds_read_b128 %3, %12 offset:3072\n\t"
+      "ds_read_b128 %4, %12 offset:4096\n\t"
+      "ds_read_b128 %5, %12 offset:5120\n\t"
+      "ds_read_b128 %6, %12 offset:6144\n\t"
+      "ds_read_b128 %7, %12 offset:7168\n\t"
+      "ds_read_b128 %8, %12 offset:8192\n\t"
+      "ds_read_b128 %9, %12 offset:9216\n\t"
+      "ds_read_b128 %10, %12 offset:10240\n\t"
+      "ds_read_b128 %11, %12 offset:11264\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11])
+      : "v"(a)
+      : "memory");
+}
+// Three 16-byte reads at a0, a1, a2.
+__device__ __forceinline__ void lds_read3_b128(uint32_t a0, uint32_t a1, uint32_t a2, i32x4_t& r0, i32x4_t& r1,
+                                               i32x4_t& r2) {
+  asm volatile(
+      "ds_read_b128 %0, %3\n\t"
+      "ds_read_b128 %1, %4\n\t"
+      "ds_read_b128 %2, %5\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2)
+      : "v"(a0), "v"(a1), "v"(a2)
+      : "memory");
+}
+__device__ __forceinline__ void lds_write6_b128(uint32_t a0, i32x4_t v0, uint32_t a1, i32x4_t v1,
+                                                uint32_t a2, i32x4_t v2, uint32_t a3, i32x4_t v3,
+                                                uint32_t a4, i32x4_t v4, uint32_t a5, i32x4_t v5) {
+  asm volatile(
+      "ds_write_b128 %0, %1\n\t"
+      "ds_write_b128 %2, %3\n\t"
+      "ds_write_b128 %4, %5\n\t"
+      "ds_write_b128 %6, %7\n\t"
+      "ds_write_b128 %8, %9\n\t"
+      "ds_write_b128 %10, %11\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      :
+      : "v"(a0), "v"(v0), "v"(a1), "v"(v1), "v"(a2), "v"(v2), "v"(a3), "v"(v3), "v"(a4), "v"(v4),
+        "v"(a5), "v"(v5)
+      : "memory");
+}
 __device__ __forceinline__ void lds_read2_b128(uint32_t a0, uint32_t a1, i32x4_t& r0, i32x4_t& r1) {
   asm volatile(
       "ds_read_b128 %0, %2\n\t"
@@ -666,7 +726,6 @@ struct PageLanes {
   const E* kbase = static_cast<const E*>(p.k);                                                 \
   const uint32_t rel = (uint32_t)(jb - wbP);                                                  \
   const uint32_t pi = div_by_magic(rel, p.page_magic);                                        \
-  const int page = __builtin_amdgcn_readfirstlane(s_pages[pi]);                               \
   const uint64_t base = (uint64_t)(uint32_t)page * (uint64_t)p.ks0 +                          \
                         (uint64_t)((rel - pi * (uint32_t)p.page_size) * (uint32_t)p.ks1);     \
   const int last = we - 1 - jb; /* rows past the range load the last valid row */            \
@@ -677,11 +736,11 @@ struct PageLanes {
     if (i < KD)                                                                               \
       __builtin_amdgcn_global_load_lds(kbase + base + off, (PA_LDS void*)(stage + 1024 * i), 16, 0, 0); \
   }
-__device__ __forceinline__ void dma_page_bf16(const AttnParams& p, const int* s_pages, uint8_t* stage, int jb,
+__device__ __forceinline__ void dma_page_bf16(const AttnParams& p, int page, uint8_t* stage, int jb,
                                               int we, int wbP, const PageLanes<false>& pl, int w) {
   PA_DMA_PAGE_BODY(uint16_t, kDma, PageLanes<false>)
 }
-__device__ __forceinline__ void dma_page_fp8(const AttnParams& p, const int* s_pages, uint8_t* stage, int jb,
+__device__ __forceinline__ void dma_page_fp8(const AttnParams& p, int page, uint8_t* stage, int jb,
                                              int we, int wbP, const PageLanes<true>& pl, int w) {
   PA_DMA_PAGE_BODY(uint8_t, kDma8, PageLanes<true>)
 }
@@ -713,22 +772,42 @@ __device__ __forceinline__ WidePiece convert_piece(i32x4_t x, int q, uint32_t ds
 }
 
 // Widening of a whole tile by n threads (t = 0..n-1), 2n < pieces <= 3n.
+// BATCH: all reads of a thread in one LDS round trip and all writes in another
+// (whether a thread has a third piece is uniform over its wave: the callers' n
+// and 1152 - 2n are multiples of 64); otherwise two smaller rounds, which need
+// fewer registers.
+template <bool BATCH = true>
 __device__ __forceinline__ void convert_tile(const uint8_t* src, uint8_t* dst, int t, int n) {
   const uint32_t a = lds_off(src) + 16 * t;
   const uint32_t d = lds_off(dst);
   i32x4_t x0, x1;
-  lds_read2_b128(a, a + 16 * n, x0, x1);
-  const WidePiece p0 = convert_piece(x0, t, d);
-  const WidePiece p1 = convert_piece(x1, t + n, d);
-  lds_write4_b128(p0.a0, p0.v0, p0.a1, p0.v1, p1.a0, p1.v0, p1.a1, p1.v1);
-  if (t + 2 * n < kTK2 * kPieces8) {
-    const WidePiece p2 = convert_piece(lds_read_b128(a + 2 * 16 * n), t + 2 * n, d);
-    lds_write2_b128(p2.a0, p2.v0, p2.a1, p2.v1);
+  if (!BATCH) {
+    lds_read2_b128(a, a + 16 * n, x0, x1);
+    const WidePiece p0 = convert_piece(x0, t, d);
+    const WidePiece p1 = convert_piece(x1, t + n, d);
+    lds_write4_b128(p0.a0, p0.v0, p0.a1, p0.v1, p1.a0, p1.v0, p1.a1, p1.v1);
+    if (t + 2 * n < kTK2 * kPieces8) {
+      const WidePiece p2 = convert_piece(lds_read_b128(a + 2 * 16 * n), t + 2 * n, d);
+      lds_write2_b128(p2.a0, p2.v0, p2.a1, p2.v1);
+    }
+  } else if (__builtin_amdgcn_readfirstlane(t) + 2 * n < kTK2 * kPieces8) {
+    i32x4_t x2;
+    lds_read3_b128(a, a + 16 * n, a + 32 * n, x0, x1, x2);
+    const WidePiece p0 = convert_piece(x0, t, d);
+    const WidePiece p1 = convert_piece(x1, t + n, d);
+    const WidePiece p2 = convert_piece(x2, t + 2 * n, d);
+    lds_write6_b128(p0.a0, p0.v0, p0.a1, p0.v1, p1.a0, p1.v0, p1.a1, p1.v1, p2.a0, p2.v0, p2.a1, p2.v1);
+  } else {
+    lds_read2_b128(a, a + 16 * n, x0, x1);
+    const WidePiece p0 = convert_piece(x0, t, d);
+    const WidePiece p1 = convert_piece(x1, t + n, d);
+    lds_write4_b128(p0.a0, p0.v0, p0.a1, p0.v1, p1.a0, p1.v0, p1.a1, p1.v1);
   }
 }
+template <bool BATCH = true>
 __device__ __forceinline__ void convert_tile(const uint8_t* src, uint8_t* dst, int tid) {
   static_assert(kTK2 * kPieces8 > 2 * 64 * kNW2 && kTK2 * kPieces8 <= 3 * 64 * kNW2, "three rounds");
-  convert_tile(src, dst, tid, 64 * kNW2);
+  convert_tile<BATCH>(src, dst, tid, 64 * kNW2);
 }
 
 // Token range of work item c (internal chunk or explicit split) of request b;
@@ -952,7 +1031,7 @@ __device__ __forceinline__ void mla_rows_range(const AttnParams& p, int b, int g
     dma(NEXT3, tile_at((K) + 3));                                                           \
     const uint8_t* src = CUR;                                                               \
     if constexpr (FP8) {                                                                    \
-      convert_tile(CUR, s_wide, tid);                                                       \
+      convert_tile<false>(CUR, s_wide, tid);                                                \
       __syncthreads();                                                                       \
       src = s_wide;                                                                         \
     }                                                                                       \
@@ -1167,11 +1246,15 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
     lds_read8_tr(vb[0], vb[1], vb[2], vb[3], vr);
   };
   auto part_r = [&](int jb) __attribute__((always_inline)) {
-    f32x4_t ssum[2] = {s_part[0][0][lane], s_part[0][1][lane]};
+    // the kNS x 2 partial blocks of this lane, all read in one round trip
+    static_assert(kNS == 6, "twelve partial blocks");
+    i32x4_t pr[12];
+    lds_read12_b128(lds_off(&s_part[0][0][lane]), pr);
+    f32x4_t ssum[2] = {__builtin_bit_cast(f32x4_t, pr[0]), __builtin_bit_cast(f32x4_t, pr[1])};
 #pragma unroll
     for (int v = 1; v < kNS; ++v) {
-      ssum[0] += s_part[v][0][lane];
-      ssum[1] += s_part[v][1][lane];
+      ssum[0] += __builtin_bit_cast(f32x4_t, pr[2 * v]);
+      ssum[1] += __builtin_bit_cast(f32x4_t, pr[2 * v + 1]);
     }
     // lane holds row l16, tokens jb + 16st + 4lg + i; the mask only on boundary tiles
     if (jb + kTK2 > wave_lim_min) {
@@ -1211,12 +1294,16 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
     if (lane == 0) lds_write_b32(lds_off(&s_x->flag), any);
   };
   auto part_pv = [&](const i32x2_t (&vr)[8]) __attribute__((always_inline)) {
-    if (__builtin_amdgcn_readfirstlane(s_x->flag)) {
-      const float a = s_x->alpha[l16];
+    // P^T, the row's rescale factor (meaningful when the flag is set) and the flag
+    i32x4_t pbv;
+    float a;
+    int flag;
+    lds_read_pv(lds_off(&s_x->pb[lane]), lds_off(&s_x->alpha[l16]), lds_off(&s_x->flag), pbv, a, flag);
+    if (__builtin_amdgcn_readfirstlane(flag)) {
 #pragma unroll
       for (int d = 0; d < 4; ++d) oacc[d] *= a;
     }
-    const i16x8_t pb = s_x->pb[lane];
+    const i16x8_t pb = __builtin_bit_cast(i16x8_t, pbv);
     // O^T += V^T P^T for dims 64w + 16d
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -1248,36 +1335,48 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
       constexpr int kWaitImm = (kWait & 0xF) | ((kWait >> 4) << 14) | 0x70 | 0xF00;
       const int wbP = wb * P;
       auto tile_at = [&](int k) { return ws + min(k, nk - 1) * kTK2; };
-      auto dma = [&](uint8_t* stage, int jb) __attribute__((always_inline)) {
-        if constexpr (FP8) {
-          if (page_tiles)
-            dma_page_fp8(p, s_pages, stage, jb, we, wbP, plane, w);
+      // page-aligned tiles: lane i of ptab holds the page id of tile 64 (k / 64) + i,
+      // so the loads of tile k take its page with one uniform lane read instead of
+      // an LDS round trip per tile (tiles are issued in order 0, 1, 2, ...)
+      int ptab = 0;
+      auto dma = [&](uint8_t* stage, int k) __attribute__((always_inline)) {
+        const int jb = tile_at(k);
+        if (page_tiles) {
+          if ((k & 63) == 0) ptab = s_pages[div_by_magic((uint32_t)(tile_at(k + lane) - wbP), p.page_magic)];
+          const int page = __builtin_amdgcn_readlane(ptab, k & 63);
+          if constexpr (FP8)
+            dma_page_fp8(p, page, stage, jb, we, wbP, plane, w);
           else
-            dma_tile8(p, s_pages, stage, jb, we, wbP, g, w, lane);
+            dma_page_bf16(p, page, stage, jb, we, wbP, plane, w);
         } else {
-          if (page_tiles)
-            dma_page_bf16(p, s_pages, stage, jb, we, wbP, plane, w);
+          if constexpr (FP8)
+            dma_tile8(p, s_pages, stage, jb, we, wbP, g, w, lane);
           else
             dma_tile(p, s_pages, stage, jb, we, wbP, g, w, lane);
         }
       };
-      dma(s_kv0, tile_at(0));
-      dma(s_kv1, tile_at(1));
-      dma(s_kv2, tile_at(2));
-      if constexpr (NST > 4) dma(s_kv3, tile_at(3));
-      if constexpr (NST > 5) dma(s_kv4, tile_at(4));
+      dma(s_kv0, 0);
+      dma(s_kv1, 1);
+      dma(s_kv2, 2);
+      if constexpr (NST > 4) dma(s_kv3, 3);
+      if constexpr (NST > 5) dma(s_kv4, 4);
+      // Two barriers per tile.  Step K: scores and V operands of tile K | barrier |
+      // loads of tile K+NST-1 into the stage of tile K-1 (read before the barrier),
+      // softmax of tile K, wait for this wave's loads of tile K+1 | barrier (so
+      // P^T and the whole of tile K+1 are visible) | PV of tile K.
       if constexpr (!FP8) {
         // tile K read in place from its stage
+        __builtin_amdgcn_s_waitcnt(kWaitImm);  // tile 0's direct loads are done
+        lds_barrier();
 #define PA_MLA_NSTEP(K, CUR, NEXT)                                                            \
   {                                                                                         \
-    __builtin_amdgcn_s_waitcnt(kWaitImm); /* tile K's direct loads are done */              \
-    lds_barrier();                                                                           \
-    dma(NEXT, tile_at((K) + NST - 1));                                                      \
     part_s(CUR);                                                                            \
     i32x2_t vr[8];                                                                          \
     part_v(CUR, vr);                                                                        \
     lds_barrier();                                                                           \
+    dma(NEXT, (K) + NST - 1);                                                               \
     if (w == kNS) part_r(ws + (K) * kTK2);                                                  \
+    __builtin_amdgcn_s_waitcnt(kWaitImm); /* tile K+1's direct loads are done */            \
     lds_barrier();                                                                           \
     part_pv(vr);                                                                            \
   }
@@ -1300,10 +1399,14 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
         __builtin_amdgcn_s_waitcnt(kWaitImm);  // tile 0's direct loads are done
         lds_barrier();
         convert_tile(s_kv0, s_wide, tid);
+        lds_barrier();
+        // step K: loads of tile K+NST-1 into the stage of tile K-1 (widened in step
+        // K-2), scores and V operands of tile K | barrier | softmax of tile K and
+        // widening of tile K+1 | barrier | PV of tile K; the barrier ending step K-1
+        // orders everything step K reads or overwrites
 #define PA_MLA_FSTEP(K, NEXTRAW, DST)                                                         \
   {                                                                                         \
-    lds_barrier();                                                                           \
-    dma(DST, tile_at((K) + NST - 1));                                                       \
+    dma(DST, (K) + NST - 1);                                                                \
     part_s(s_wide);                                                                         \
     i32x2_t vr[8];                                                                          \
     part_v(s_wide, vr);                                                                     \
@@ -1635,29 +1738,36 @@ __device__ __forceinline__ void mla_mid_range(const AttnParams& p, int b, int g,
       constexpr int kWaitImm = (kWait & 0xF) | ((kWait >> 4) << 14) | 0x70 | 0xF00;
       const int wbP = wb * P;
       auto tile_at = [&](int k) { return ws + min(k, nk - 1) * kTK2; };
-      auto dma = [&](uint8_t* stage, int jb) __attribute__((always_inline)) {
-        if constexpr (FP8) {
-          if (page_tiles)
-            dma_page_fp8(p, s_pages, stage, jb, we, wbP, plane, w);
+      // page-aligned tiles: lane i of ptab holds the page id of tile 64 (k / 64) + i,
+      // so the loads of tile k take its page with one uniform lane read instead of
+      // an LDS round trip per tile (tiles are issued in order 0, 1, 2, ...)
+      int ptab = 0;
+      auto dma = [&](uint8_t* stage, int k) __attribute__((always_inline)) {
+        const int jb = tile_at(k);
+        if (page_tiles) {
+          if ((k & 63) == 0) ptab = s_pages[div_by_magic((uint32_t)(tile_at(k + lane) - wbP), p.page_magic)];
+          const int page = __builtin_amdgcn_readlane(ptab, k & 63);
+          if constexpr (FP8)
+            dma_page_fp8(p, page, stage, jb, we, wbP, plane, w);
           else
-            dma_tile8(p, s_pages, stage, jb, we, wbP, g, w, lane);
+            dma_page_bf16(p, page, stage, jb, we, wbP, plane, w);
         } else {
-          if (page_tiles)
-            dma_page_bf16(p, s_pages, stage, jb, we, wbP, plane, w);
+          if constexpr (FP8)
+            dma_tile8(p, s_pages, stage, jb, we, wbP, g, w, lane);
           else
             dma_tile(p, s_pages, stage, jb, we, wbP, g, w, lane);
         }
       };
-      dma(s_kv0, tile_at(0));
-      dma(s_kv1, tile_at(1));
-      if constexpr (NST > 3) dma(s_kv2, tile_at(2));
-      if constexpr (NST > 4) dma(s_kv3, tile_at(3));
+      dma(s_kv0, 0);
+      dma(s_kv1, 1);
+      if constexpr (NST > 3) dma(s_kv2, 2);
+      if constexpr (NST > 4) dma(s_kv3, 3);
       if constexpr (!FP8) {
 #define PA_MLA_MSTEP(K, CUR, NEXT)                                                            \
   {                                                                                         \
     __builtin_amdgcn_s_waitcnt(kWaitImm); /* tile K's direct loads are done */              \
     lds_barrier();                                                                           \
-    dma(NEXT, tile_at((K) + NST - 1));                                                      \
+    dma(NEXT, (K) + NST - 1);                                                               \
     part_s(CUR);                                                                            \
     i32x2_t vr[8];                                                                          \
     part_v(CUR, vr);                                                                        \
@@ -1684,7 +1794,7 @@ __device__ __forceinline__ void mla_mid_range(const AttnParams& p, int b, int g,
 #define PA_MLA_MFSTEP(K, NEXTRAW, DST)                                                        \
   {                                                                                         \
     lds_barrier();                                                                           \
-    dma(DST, tile_at((K) + NST - 1));                                                       \
+    dma(DST, (K) + NST - 1);                                                                \
     part_s(s_wide);                                                                         \
     i32x2_t vr[8];                                                                          \
     part_v(s_wide, vr);                                                                     \

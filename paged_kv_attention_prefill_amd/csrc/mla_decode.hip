@@ -555,6 +555,49 @@ __device__ __forceinline__ void lds_read_pv(uint32_t apb, uint32_t aal, uint32_t
       : "v"(apb), "v"(aal), "v"(afl)
       : "memory");
 }
+// The PV inputs of NRB row blocks in one round trip: P^T blocks at apb + 1024 rb,
+// rescale factors at aal + 64 rb, and the NRB flag words at afl.
+template <int NRB>
+__device__ __forceinline__ void lds_read_pv_blocks(uint32_t apb, uint32_t aal, uint32_t afl, i32x4_t (&pb)[NRB],
+                                                   float (&al)[NRB], int (&fl)[NRB]) {
+  static_assert(NRB == 2 || NRB == 4, "two or four row blocks");
+  if constexpr (NRB == 4) {
+    i32x4_t f;
+    asm volatile(
+        "ds_read_b128 %0, %9\n\t"
+        "ds_read_b128 %1, %9 offset:1024\n\t"
+        "ds_read_b128 %2, %9 offset:2048\n\t"
+        "ds_read_b128 %3, %9 offset:3072\n\t"
+        "ds_read_b32 %4, %10\n\t"
+        "ds_read_b32 %5, %10 offset:64\n\t"
+        "ds_read_b32 %6, %10 offset:128\n\t"
+        "ds_read_b32 %7, %10 offset:192\n\t"
+        "ds_read_b128 %8, %11\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(pb[0]), "=&v"(pb[1]), "=&v"(pb[2]), "=&v"(pb[3]), "=&v"(al[0]), "=&v"(al[1]),
+          "=&v"(al[2]), "=&v"(al[3]), "=&v"(f)
+        : "v"(apb), "v"(aal), "v"(afl)
+        : "memory");
+    fl[0] = f.x;
+    fl[1] = f.y;
+    fl[2] = f.z;
+    fl[3] = f.w;
+  } else {
+    i32x2_t f;
+    asm volatile(
+        "ds_read_b128 %0, %5\n\t"
+        "ds_read_b128 %1, %5 offset:1024\n\t"
+        "ds_read_b32 %2, %6\n\t"
+        "ds_read_b32 %3, %6 offset:64\n\t"
+        "ds_read_b64 %4, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(pb[0]), "=&v"(pb[1]), "=&v"(al[0]), "=&v"(al[1]), "=&v"(f)
+        : "v"(apb), "v"(aal), "v"(afl)
+        : "memory");
+    fl[0] = f.x;
+    fl[1] = f.y;
+  }
+}
 // Twelve 16-byte reads at a + 1024 k, k = 0..11 (the partial-score blocks).
 __device__ __forceinline__ void lds_read12_b128(uint32_t a, i32x4_t (&r)[12]) {
   asm volatile(
@@ -1540,7 +1583,7 @@ struct MidX {
   i16x8_t pb[NRB][64];    // P^T of each row block in the PV B-operand layout
   float alpha[NRB][16];   // rescale factors of the current tile (valid when flag)
   float stat[NRB][16][3]; // final: row sum, reference max, running max
-  int flag[NRB];
+  alignas(16) int flag[NRB];
 };
 template <bool FP8>
 constexpr int kMidStages = FP8 ? 5 : 3;
@@ -1702,14 +1745,20 @@ __device__ __forceinline__ void mla_mid_range(const AttnParams& p, int b, int g,
     if (lane == 0) lds_write_b32(lds_off(&s_x->flag[w]), any);
   };
   auto part_pv = [&](const i32x2_t (&vr)[8]) __attribute__((always_inline)) {
+    // every row block's P^T, rescale factor and flag in one LDS round trip
+    static_assert(sizeof(s_x->pb[0]) == 1024 && sizeof(s_x->alpha[0]) == 64, "exchange layout");
+    i32x4_t pbs[NRB];
+    float al[NRB];
+    int fl[NRB];
+    lds_read_pv_blocks<NRB>(lds_off(&s_x->pb[0][lane]), lds_off(&s_x->alpha[0][l16]), lds_off(&s_x->flag[0]), pbs,
+                            al, fl);
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
-      if (__builtin_amdgcn_readfirstlane(s_x->flag[rb])) {
-        const float a = s_x->alpha[rb][l16];
+      if (__builtin_amdgcn_readfirstlane(fl[rb])) {
 #pragma unroll
-        for (int d = 0; d < 4; ++d) oacc[rb][d] *= a;
+        for (int d = 0; d < 4; ++d) oacc[rb][d] *= al[rb];
       }
-      const i16x8_t pb = s_x->pb[rb][lane];
+      const i16x8_t pb = __builtin_bit_cast(i16x8_t, pbs[rb]);
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const i32x4_t v4 = {vr[2 * d].x, vr[2 * d].y, vr[2 * d + 1].x, vr[2 * d + 1].y};

@@ -1849,12 +1849,23 @@ __device__ __forceinline__ void mla_mid_range(const AttnParams& p, int b, int g,
     part_v(s_wide, vr);                                                                     \
     __builtin_amdgcn_s_waitcnt(kWaitImm); /* tile K+1's direct loads are done */            \
     lds_barrier();                                                                           \
-    if (w < NRB) part_r(ws + (K) * kTK2);                                                   \
-    convert_tile(NEXTRAW, s_wide, tid);                                                     \
+    if constexpr (NRB == 2) {                                                               \
+      if (w < NRB)                                                                          \
+        part_r(ws + (K) * kTK2);                                                            \
+      else                                                                                  \
+        convert_tile(NEXTRAW, s_wide, tid - 64 * NRB, 64 * (kNW2 - NRB));                   \
+    } else {                                                                                \
+      if (w < NRB) part_r(ws + (K) * kTK2);                                                 \
+      convert_tile(NEXTRAW, s_wide, tid);                                                   \
+    }                                                                                       \
     lds_barrier();                                                                           \
     part_pv(vr);                                                                            \
   }
         static_assert(NST == 5, "fp8 stage rotation");
+        // two row blocks: the six waves that do not run a softmax widen the next tile
+        // meanwhile (three pieces each); four row blocks: every wave widens a share
+        // after the softmaxes (four waves alone would need more registers than fit)
+        static_assert(kTK2 * kPieces8 == 3 * 64 * (kNW2 - 2), "three pieces per widening thread");
         for (int k = 0; k < nk; k += 5) {
           PA_MLA_MFSTEP(k, s_kv1, s_kv4);
           if (k + 1 >= nk) break;

@@ -289,6 +289,18 @@ def test_mla_narrow_page_sizes(heads, q_len, page_size, dt):
     run_and_check(w, label)
 
 
+@pytest.mark.parametrize("heads,q_len,page_size,dt", [(16, 1, 32, W.DT_BF16), (16, 1, 64, W.DT_FP8),
+                                                       (16, 4, 32, W.DT_FP8), (16, 2, 64, W.DT_BF16)])
+def test_mla_long_range_one_workgroup(heads, q_len, page_size, dt):
+    # internal splitting off: one workgroup walks a 20000-token KV, so a range crosses
+    # several page-id windows (256 pages each) and the page-aligned tile loads reload
+    # their per-wave table of page ids every 64 tiles
+    label = f"MLA one-workgroup range h{heads} q{q_len} page {page_size} dt {dt}"
+    print(label, flush=True)
+    w = mla_build(970 + heads + q_len + page_size + dt, heads, q_len, [20000, 7], page_size, dt=dt)
+    run_and_check(w, label, flags=B.FLAG_NO_INTERNAL_SPLIT)
+
+
 def test_mla_explicit_splits():
     w = mla_build(991, 128, 1, [0, 5, 640, 999], 64)
     d = R.upload(w)

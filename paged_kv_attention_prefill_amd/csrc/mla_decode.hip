@@ -631,6 +631,7 @@ __device__ __forceinline__ void lds_read3_b128(uint32_t a0, uint32_t a1, uint32_
       : "v"(a0), "v"(a1), "v"(a2)
       : "memory");
 }
+// Six 16-byte writes.
 __device__ __forceinline__ void lds_write6_b128(uint32_t a0, i32x4_t v0, uint32_t a1, i32x4_t v1,
                                                 uint32_t a2, i32x4_t v2, uint32_t a3, i32x4_t v3,
                                                 uint32_t a4, i32x4_t v4, uint32_t a5, i32x4_t v5) {
@@ -647,6 +648,7 @@ __device__ __forceinline__ void lds_write6_b128(uint32_t a0, i32x4_t v0, uint32_
         "v"(a5), "v"(v5)
       : "memory");
 }
+// Two 16-byte reads.
 __device__ __forceinline__ void lds_read2_b128(uint32_t a0, uint32_t a1, i32x4_t& r0, i32x4_t& r1) {
   asm volatile(
       "ds_read_b128 %0, %2\n\t"

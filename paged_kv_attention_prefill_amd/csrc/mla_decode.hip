@@ -648,6 +648,46 @@ __device__ __forceinline__ void lds_write6_b128(uint32_t a0, i32x4_t v0, uint32_
         "v"(a5), "v"(v5)
       : "memory");
 }
+// fp8 direct path: six 8-byte reads (three addresses, each also at +9216 = 16 rows).
+__device__ __forceinline__ void lds_read6_b64(uint32_t a0, uint32_t a1, uint32_t a2, i32x2_t (&r)[6]) {
+  asm volatile(
+      "ds_read_b64 %0, %6\n\t"
+      "ds_read_b64 %1, %6 offset:9216\n\t"
+      "ds_read_b64 %2, %7\n\t"
+      "ds_read_b64 %3, %7 offset:9216\n\t"
+      "ds_read_b64 %4, %8\n\t"
+      "ds_read_b64 %5, %8 offset:9216\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5])
+      : "v"(a0), "v"(a1), "v"(a2)
+      : "memory");
+}
+// fp8 direct path: four transposed 8-bit reads.  In each 16-lane group, lane 2j + h
+// gives the address of bytes 8h..8h+7 of its group's row j; lane c receives byte c
+// of the group's rows 0..7 (checked on the device).
+__device__ __forceinline__ void lds_read4_tr8(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                              i32x2_t (&r)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b8 %0, %4\n\t"
+      "ds_read_b64_tr_b8 %1, %5\n\t"
+      "ds_read_b64_tr_b8 %2, %6\n\t"
+      "ds_read_b64_tr_b8 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+}
+// Eight e4m3 codes (two words, code k in byte k) -> eight bf16 in order, exactly
+// (every e4m3 value is a bf16 value).  Written in asm: the compiler's builtin for
+// this instruction mis-packs the two halves of its result.
+__device__ __forceinline__ i16x8_t fp8x8_to_bf16(i32x2_t x) {
+  uint32_t o0, o1, o2, o3;
+  asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0" : "=v"(o0) : "v"(x.x));
+  asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0 op_sel:[1,0,0]" : "=v"(o1) : "v"(x.x));
+  asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0" : "=v"(o2) : "v"(x.y));
+  asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0 op_sel:[1,0,0]" : "=v"(o3) : "v"(x.y));
+  return as_i16x8(make_uint4(o0, o1, o2, o3));
+}
 // Two 16-byte reads.
 __device__ __forceinline__ void lds_read2_b128(uint32_t a0, uint32_t a1, i32x4_t& r0, i32x4_t& r1) {
   asm volatile(
@@ -716,6 +756,13 @@ constexpr int kDma8 = kTK2 * kPieces8 / 64;        // 1-KB direct loads per fp8 
 constexpr int kStage8 = kDma8 * 1024;
 static_assert(kTK2 * kPieces8 % 64 == 0, "an fp8 tile is a whole number of 1-KB wave loads");
 
+// fp8 stage layout read in place by the narrow kernel: piece p of row r at slot
+// p ^ swz8(r), within p's aligned group of four (36 pieces per row), so that the
+// 16 rows of an 8-byte operand read and the 8 rows of a transposed read fall on
+// distinct banks.
+__device__ __forceinline__ int swz8(int r) { return (r >> 2) & 3; }
+
+template <bool SWZ = false>
 __device__ __forceinline__ void dma_tile8(const AttnParams& p, const int* s_pages, uint8_t* stage,
                                           int jb, int we, int wbP, int g, int w, int lane) {
   const uint8_t* kbase = static_cast<const uint8_t*>(p.k);
@@ -733,7 +780,7 @@ __device__ __forceinline__ void dma_tile8(const AttnParams& p, const int* s_page
     const uint32_t pi = div_by_magic(jj, p.page_magic);
     const uint32_t pslot = jj - pi * (uint32_t)p.page_size;
     const uint32_t page = s_pages[pi];
-    const uint64_t off = (uint64_t)page * ks0 + (pslot * ks1 + kc + 16 * piece);
+    const uint64_t off = (uint64_t)page * ks0 + (pslot * ks1 + kc + 16 * (SWZ ? piece ^ swz8(row) : piece));
     if (i < kDma8)
       __builtin_amdgcn_global_load_lds(kbase + off, (PA_LDS void*)(stage + 1024 * i), 16, 0, 0);
   }
@@ -743,7 +790,7 @@ __device__ __forceinline__ void dma_tile8(const AttnParams& p, const int* s_page
 // page's offset is uniform, and the (row, piece) each lane loads is fixed per
 // load instruction, so the per-lane part is precomputed once (PageLanes) and a
 // load costs a clamp, a multiply-add and the address add.
-template <bool FP8>
+template <bool FP8, bool SWZ = false>
 struct PageLanes {
   static constexpr int N = ((FP8 ? kDma8 : kDma) + kNW2 - 1) / kNW2;  // load rounds
   int row[N];       // tile row of this lane's piece in round r
@@ -755,7 +802,8 @@ struct PageLanes {
       const int slot = 64 * i + lane;
       if constexpr (FP8) {
         row[r] = slot / kPieces8;
-        off[r] = (uint32_t)(g * p.ks2) + 16 * (slot - row[r] * kPieces8);
+        const int q = slot - row[r] * kPieces8;
+        off[r] = (uint32_t)(g * p.ks2) + 16 * (SWZ ? q ^ swz8(row[r]) : q);
       } else {
         row[r] = slot / kPieces;
         const int q = slot - row[r] * kPieces;
@@ -788,6 +836,11 @@ __device__ __forceinline__ void dma_page_bf16(const AttnParams& p, int page, uin
 __device__ __forceinline__ void dma_page_fp8(const AttnParams& p, int page, uint8_t* stage, int jb,
                                              int we, int wbP, const PageLanes<true>& pl, int w) {
   PA_DMA_PAGE_BODY(uint8_t, kDma8, PageLanes<true>)
+}
+using PageLanes8S = PageLanes<true, true>;  // swizzled fp8 stages
+__device__ __forceinline__ void dma_page_fp8s(const AttnParams& p, int page, uint8_t* stage, int jb,
+                                              int we, int wbP, const PageLanes8S& pl, int w) {
+  PA_DMA_PAGE_BODY(uint8_t, kDma8, PageLanes8S)
 }
 #undef PA_DMA_PAGE_BODY
 
@@ -1196,9 +1249,9 @@ struct NarrowX {
   int flag;            // some row's reference max moved in this tile
 };
 // LDS stages (tiles in flight + 1): as many as fit next to the score exchange
-// (bf16: 4 x 36 KB; fp8: 6 x 18 KB plus the 36 KB widened tile)
+// (bf16: 4 x 36 KB; fp8: 7 x 18 KB next to the double-buffered scores and P^T)
 template <bool FP8>
-constexpr int kNarrowStages = FP8 ? 6 : 4;
+constexpr int kNarrowStages = FP8 ? 7 : 4;
 
 // One (request b, KV head g) token range [j0, j1) of the narrow kernel; the
 // result goes to the final O / LSE (split c_out) or to workspace slot wslot.
@@ -1207,7 +1260,6 @@ template <bool FP8>
 __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int g, int L, int j0, int j1,
                                                  bool to_ws, int64_t wslot, int c, uint8_t* s_kv0,
                                                  uint8_t* s_kv1, uint8_t* s_kv2, uint8_t* s_kv3,
-                                                 uint8_t* s_kv4, uint8_t* s_kv5, uint8_t* s_wide,
                                                  f32x4_t (*s_part)[2][64], NarrowX* s_x, int* s_pages) {
   constexpr int NST = kNarrowStages<FP8>;
   const int tid = threadIdx.x;
@@ -1290,11 +1342,11 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
     }
     lds_read8_tr(vb[0], vb[1], vb[2], vb[3], vr);
   };
-  auto part_r = [&](int jb) __attribute__((always_inline)) {
+  auto part_r = [&](int jb, f32x4_t (*sp)[2][64], NarrowX* sx) __attribute__((always_inline)) {
     // the kNS x 2 partial blocks of this lane, all read in one round trip
     static_assert(kNS == 6, "twelve partial blocks");
     i32x4_t pr[12];
-    lds_read12_b128(lds_off(&s_part[0][0][lane]), pr);
+    lds_read12_b128(lds_off(&sp[0][0][lane]), pr);
     f32x4_t ssum[2] = {__builtin_bit_cast(f32x4_t, pr[0]), __builtin_bit_cast(f32x4_t, pr[1])};
 #pragma unroll
     for (int v = 1; v < kNS; ++v) {
@@ -1324,7 +1376,7 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
       const float a = grow ? alpha : 1.f;
       lsum *= a;
       m = mnew;
-      if (lg == 0) s_x->alpha[l16] = a;
+      if (lg == 0) sx->alpha[l16] = a;
     }
     const float nmref = -(m == -INFINITY ? 0.f : m);
     float e[8];
@@ -1335,8 +1387,8 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
     const uint4 bits = make_uint4(pack2<BF16>(e[0], e[1]), pack2<BF16>(e[2], e[3]),
                                   pack2<BF16>(e[4], e[5]), pack2<BF16>(e[6], e[7]));
     lsum = sum2<BF16>(bits.x, sum2<BF16>(bits.y, sum2<BF16>(bits.z, sum2<BF16>(bits.w, lsum))));
-    s_x->pb[lane] = as_i16x8(bits);
-    if (lane == 0) lds_write_b32(lds_off(&s_x->flag), any);
+    sx->pb[lane] = as_i16x8(bits);
+    if (lane == 0) lds_write_b32(lds_off(&sx->flag), any);
   };
   auto part_pv = [&](const i32x2_t (&vr)[8]) __attribute__((always_inline)) {
     // P^T, the row's rescale factor (meaningful when the flag is set) and the flag
@@ -1357,10 +1409,60 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
     }
   };
 
+  // fp8, read in place from the swizzled stages (see swz8): waves 0..kNS-1 read
+  // their K operands with 8-byte reads and widen them in registers (part_s8);
+  // every wave reads its V^T operands with transposed 8-bit reads whose rows
+  // follow P^T's token order (part_v8)
+  constexpr int kPitch8 = kPieces8 * 16;  // 576-byte fp8 rows
+  auto part_s8 = [&](const uint8_t* kv, f32x4_t (*sp)[2][64]) __attribute__((always_inline)) {
+    f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    const uint32_t base = lds_off(kv) + l16 * kPitch8 + 8 * (lg & 1);  // rows l16 and 16 + l16
+    const int sw = swz8(l16);                                           // (same swizzle)
+    uint32_t ka[3];
+#pragma unroll
+    for (int u = 0; u < 3; ++u) ka[u] = base + 16 * ((2 * (3 * w + u) + (lg >> 1)) ^ sw);
+    i32x2_t kr[6];  // (k-step u, block st2) at 2u + st2
+    lds_read6_b64(ka[0], ka[1], ka[2], kr);
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+#pragma unroll
+      for (int st2 = 0; st2 < 2; ++st2)
+        sacc[st2] = mfma16<BF16>(fp8x8_to_bf16(kr[2 * u + st2]), qreg[u], sacc[st2]);
+    lds_write_part(lds_off(&sp[w][0][lane]), sacc[0], sacc[1]);
+  };
+  auto part_v8 = [&](const uint8_t* kv, i16x8_t (&va)[4]) __attribute__((always_inline)) {
+    // lane group q holds P^T's k = 8q + j, i.e. tokens 4q + j (j < 4) and 12 + 4q + j
+    const int q = lane >> 4, j = (lane & 15) >> 1, h = lane & 1;
+    const int trow = j < 4 ? 4 * q + j : 12 + 4 * q + j;
+    const int sw = swz8(trow);
+    const uint32_t rb = lds_off(kv) + trow * kPitch8 + 8 * h;
+    i32x2_t vr[4];
+    lds_read4_tr8(rb + 16 * ((4 * w + 0) ^ sw), rb + 16 * ((4 * w + 1) ^ sw), rb + 16 * ((4 * w + 2) ^ sw),
+                  rb + 16 * ((4 * w + 3) ^ sw), vr);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) va[d] = fp8x8_to_bf16(vr[d]);
+  };
+  // PV of one tile from stage kv (wave w: dims 64w..64w+63)
+  auto part_pv8 = [&](const uint8_t* kv, const NarrowX* sx) __attribute__((always_inline)) {
+    i16x8_t va[4];
+    part_v8(kv, va);
+    i32x4_t pbv;
+    float a;
+    int flag;
+    lds_read_pv(lds_off(&sx->pb[lane]), lds_off(&sx->alpha[l16]), lds_off(&sx->flag), pbv, a, flag);
+    if (__builtin_amdgcn_readfirstlane(flag)) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) oacc[d] *= a;
+    }
+    const i16x8_t pb = __builtin_bit_cast(i16x8_t, pbv);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) oacc[d] = mfma16<BF16>(va[d], pb, oacc[d]);
+  };
+
   // tiles never straddle a page when the page size is a multiple of the tile
   // (range starts are multiples of the tile or of the page)
   const bool page_tiles = P % kTK2 == 0 && j0 % kTK2 == 0;
-  PageLanes<FP8> plane;
+  PageLanes<FP8, FP8> plane;
   if (page_tiles) plane.init(p, g, w, lane);
   if (jhi > j0) {
     const int pfirst = j0 / P, plast = (jhi - 1) / P;
@@ -1390,21 +1492,21 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
           if ((k & 63) == 0) ptab = s_pages[div_by_magic((uint32_t)(tile_at(k + lane) - wbP), p.page_magic)];
           const int page = __builtin_amdgcn_readlane(ptab, k & 63);
           if constexpr (FP8)
-            dma_page_fp8(p, page, stage, jb, we, wbP, plane, w);
+            dma_page_fp8s(p, page, stage, jb, we, wbP, plane, w);
           else
             dma_page_bf16(p, page, stage, jb, we, wbP, plane, w);
         } else {
           if constexpr (FP8)
-            dma_tile8(p, s_pages, stage, jb, we, wbP, g, w, lane);
+            dma_tile8<true>(p, s_pages, stage, jb, we, wbP, g, w, lane);
           else
             dma_tile(p, s_pages, stage, jb, we, wbP, g, w, lane);
         }
       };
-      dma(s_kv0, 0);
-      dma(s_kv1, 1);
-      dma(s_kv2, 2);
-      if constexpr (NST > 4) dma(s_kv3, 3);
-      if constexpr (NST > 5) dma(s_kv4, 4);
+      if constexpr (!FP8) {
+        dma(s_kv0, 0);
+        dma(s_kv1, 1);
+        dma(s_kv2, 2);
+      }
       // Two barriers per tile.  Step K: scores and V operands of tile K | barrier |
       // loads of tile K+NST-1 into the stage of tile K-1 (read before the barrier),
       // softmax of tile K, wait for this wave's loads of tile K+1 | barrier (so
@@ -1420,7 +1522,7 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
     part_v(CUR, vr);                                                                        \
     lds_barrier();                                                                           \
     dma(NEXT, (K) + NST - 1);                                                               \
-    if (w == kNS) part_r(ws + (K) * kTK2);                                                  \
+    if (w == kNS) part_r(ws + (K) * kTK2, s_part, s_x);                                     \
     __builtin_amdgcn_s_waitcnt(kWaitImm); /* tile K+1's direct loads are done */            \
     lds_barrier();                                                                           \
     part_pv(vr);                                                                            \
@@ -1437,48 +1539,34 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
         }
 #undef PA_MLA_NSTEP
       } else {
-        // fp8: the bf16 tile buffer holds tile K during step K; tile K+1 is
-        // widened into it by the waves other than kNS while wave kNS runs the
-        // softmax of tile K (the buffer's reads for tile K are all done by then)
-        const int tw = w < kNS ? tid : tid - 64;  // widening thread index, 0..447
-        __builtin_amdgcn_s_waitcnt(kWaitImm);  // tile 0's direct loads are done
+        // fp8 read in place, one barrier per tile: step K computes the partial
+        // scores of tile K+1 (waves 0..kNS-1) while wave kNS runs the softmax of
+        // tile K, then every wave does the PV of tile K-1.  Partial scores and P^T
+        // are double-buffered; stage t % NST holds tile t, tiles K+3..K+NST-2 are
+        // in flight at the end of step K.
+        static_assert(NST == 7, "fp8 stages");
+        constexpr int kWait3 = (NST - 3) * kMinDma, kWait4 = (NST - 4) * kMinDma;
+        static_assert(kWait3 < 16, "vmcnt field");
+        constexpr int kWaitImm3 = kWait3 | 0x70 | 0xF00, kWaitImm4 = kWait4 | 0x70 | 0xF00;
+        auto stage = [&](int t) { return s_kv0 + kStage8 * (t % NST); };
+#pragma unroll
+        for (int t = 0; t < NST - 2; ++t) dma(stage(t), t);
+        __builtin_amdgcn_s_waitcnt(kWaitImm3);  // tile 0 has landed
         lds_barrier();
-        convert_tile(s_kv0, s_wide, tid);
+        if (w < kNS) part_s8(stage(0), s_part);
+        __builtin_amdgcn_s_waitcnt(kWaitImm4);  // tile 1 has landed
         lds_barrier();
-        // step K: loads of tile K+NST-1 into the stage of tile K-1 (widened in step
-        // K-2), scores and V operands of tile K | barrier | softmax of tile K and
-        // widening of tile K+1 | barrier | PV of tile K; the barrier ending step K-1
-        // orders everything step K reads or overwrites
-#define PA_MLA_FSTEP(K, NEXTRAW, DST)                                                         \
-  {                                                                                         \
-    dma(DST, (K) + NST - 1);                                                                \
-    part_s(s_wide);                                                                         \
-    i32x2_t vr[8];                                                                          \
-    part_v(s_wide, vr);                                                                     \
-    __builtin_amdgcn_s_waitcnt(kWaitImm); /* tile K+1's direct loads are done */            \
-    lds_barrier();                                                                           \
-    if (w == kNS)                                                                           \
-      part_r(ws + (K) * kTK2);                                                              \
-    else                                                                                    \
-      convert_tile(NEXTRAW, s_wide, tw, 64 * (kNW2 - 1));                                   \
-    lds_barrier();                                                                           \
-    part_pv(vr);                                                                            \
-  }
-        static_assert(NST == 6, "fp8 stage rotation");
-        for (int k = 0; k < nk; k += 6) {
-          PA_MLA_FSTEP(k, s_kv1, s_kv5);
-          if (k + 1 >= nk) break;
-          PA_MLA_FSTEP(k + 1, s_kv2, s_kv0);
-          if (k + 2 >= nk) break;
-          PA_MLA_FSTEP(k + 2, s_kv3, s_kv1);
-          if (k + 3 >= nk) break;
-          PA_MLA_FSTEP(k + 3, s_kv4, s_kv2);
-          if (k + 4 >= nk) break;
-          PA_MLA_FSTEP(k + 4, s_kv5, s_kv3);
-          if (k + 5 >= nk) break;
-          PA_MLA_FSTEP(k + 5, s_kv0, s_kv4);
+        for (int k = 0; k < nk; ++k) {
+          dma(stage(k + NST - 2), k + NST - 2);  // the stage of tile k-2, read before the last barrier
+          if (w < kNS)
+            part_s8(stage(k + 1), s_part + kNS * ((k + 1) & 1));  // past the last tile: unused
+          else if (w == kNS)
+            part_r(ws + k * kTK2, s_part + kNS * (k & 1), s_x + (k & 1));
+          if (k > 0) part_pv8(stage(k - 1), s_x + ((k - 1) & 1));
+          __builtin_amdgcn_s_waitcnt(kWaitImm4);  // tile k+2 has landed
+          lds_barrier();
         }
-#undef PA_MLA_FSTEP
+        part_pv8(stage(nk - 1), s_x + ((nk - 1) & 1));
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no loads in flight into the stages
       __syncthreads();
@@ -1539,24 +1627,24 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
 // balanced split, equal shares of the (request, KV head, 32-token unit) sequence.
 template <bool FP8>
 __global__ __launch_bounds__(64 * kNW2, 1) void mla_narrow_kernel(AttnParams p, int ngroups) {
-  constexpr int STAGE = FP8 ? kStage8 : kStage2;
+  // bf16: four stages; fp8: the NST stages contiguous from s_kv0, and the partial
+  // scores and the P^T exchange double-buffered
   constexpr int NST = kNarrowStages<FP8>;
-  __shared__ __align__(16) uint8_t s_kv0[STAGE];
-  __shared__ __align__(16) uint8_t s_kv1[STAGE];
-  __shared__ __align__(16) uint8_t s_kv2[STAGE];
-  __shared__ __align__(16) uint8_t s_kv3[STAGE];
-  __shared__ __align__(16) uint8_t s_kv4[NST > 4 ? STAGE : 16];
-  __shared__ __align__(16) uint8_t s_kv5[NST > 5 ? STAGE : 16];
-  __shared__ __align__(16) uint8_t s_wide[FP8 ? kStage2 : 16];  // fp8: the widened tile
-  __shared__ __align__(16) f32x4_t s_part[kNS][2][64];           // partial scores
-  __shared__ __align__(16) NarrowX s_x;
+  static_assert(FP8 || NST == 4, "bf16 stages");
+  __shared__ __align__(16) uint8_t s_kv0[FP8 ? NST * kStage8 : kStage2];
+  __shared__ __align__(16) uint8_t s_kv1[FP8 ? 16 : kStage2];
+  __shared__ __align__(16) uint8_t s_kv2[FP8 ? 16 : kStage2];
+  __shared__ __align__(16) uint8_t s_kv3[FP8 ? 16 : kStage2];
+  __shared__ __align__(16) f32x4_t s_part[(FP8 ? 2 : 1) * kNS][2][64];  // partial scores
+  __shared__ __align__(16) NarrowX s_xb[FP8 ? 2 : 1];
+  NarrowX* const s_x = s_xb;
   __shared__ int s_pages[kPageWinM];
   if (p.bal_blocks > 0) {
     BalCursor cur;
     if (!cur.start(p, blockIdx.x)) return;
     do {
       mla_narrow_range<FP8>(p, cur.b, cur.g, cur.L, cur.j0(p), cur.j1(p), !cur.whole(), cur.slot(p), 0,
-                            s_kv0, s_kv1, s_kv2, s_kv3, s_kv4, s_kv5, s_wide, s_part, &s_x, s_pages);
+                            s_kv0, s_kv1, s_kv2, s_kv3, s_part, s_x, s_pages);
     } while (cur.next(p));
     return;
   }
@@ -1569,7 +1657,7 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_narrow_kernel(AttnParams p, 
   bool to_ws;
   if (!mla_item_range(p, b, c, L, j0, j1, to_ws)) return;
   mla_narrow_range<FP8>(p, b, g, L, j0, j1, to_ws, (int64_t)(b * p.num_kv_heads + g) * p.max_chunks + c,
-                        c, s_kv0, s_kv1, s_kv2, s_kv3, s_kv4, s_kv5, s_wide, s_part, &s_x, s_pages);
+                        c, s_kv0, s_kv1, s_kv2, s_kv3, s_part, s_x, s_pages);
 }
 
 // ---------------------------------------------------------------------------

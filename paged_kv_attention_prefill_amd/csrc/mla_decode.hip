@@ -662,6 +662,27 @@ __device__ __forceinline__ void lds_read6_b64(uint32_t a0, uint32_t a1, uint32_t
       : "v"(a0), "v"(a1), "v"(a2)
       : "memory");
 }
+// fp8 direct path: four / two 8-byte reads (each address also at +9216 = 16 rows).
+__device__ __forceinline__ void lds_read4_b64(uint32_t a0, uint32_t a1, i32x2_t (&r)[4]) {
+  asm volatile(
+      "ds_read_b64 %0, %4\n\t"
+      "ds_read_b64 %1, %4 offset:9216\n\t"
+      "ds_read_b64 %2, %5\n\t"
+      "ds_read_b64 %3, %5 offset:9216\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(a0), "v"(a1)
+      : "memory");
+}
+__device__ __forceinline__ void lds_read2_b64(uint32_t a0, i32x2_t (&r)[2]) {
+  asm volatile(
+      "ds_read_b64 %0, %2\n\t"
+      "ds_read_b64 %1, %2 offset:9216\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1])
+      : "v"(a0)
+      : "memory");
+}
 // fp8 direct path: four transposed 8-bit reads.  In each 16-lane group, lane 2j + h
 // gives the address of bytes 8h..8h+7 of its group's row j; lane c receives byte c
 // of the group's rows 0..7 (checked on the device).
@@ -1676,13 +1697,12 @@ struct MidX {
   alignas(16) int flag[NRB];
 };
 template <bool FP8>
-constexpr int kMidStages = FP8 ? 5 : 3;
+constexpr int kMidStages = FP8 ? 6 : 3;
 
 template <bool FP8, int NRB>
 __device__ __forceinline__ void mla_mid_range(const AttnParams& p, int b, int g, int L, int j0, int j1,
                                               bool to_ws, int64_t wslot, int c, uint8_t* s_kv0,
-                                              uint8_t* s_kv1, uint8_t* s_kv2, uint8_t* s_kv3,
-                                              uint8_t* s_kv4, uint8_t* s_wide,
+                                              uint8_t* s_kv1, uint8_t* s_kv2,
                                               f32x4_t (*s_part)[2][64], MidX<NRB>* s_x, int* s_pages) {
   constexpr int NST = kMidStages<FP8>;
   constexpr int KS = kNW2 / NRB;                  // k-step slices per row block
@@ -1788,10 +1808,10 @@ __device__ __forceinline__ void mla_mid_range(const AttnParams& p, int b, int g,
     lds_read8_tr(vb[0], vb[1], vb[2], vb[3], vr);
   };
   // wave w < NRB: row block w
-  auto part_r = [&](int jb) __attribute__((always_inline)) {
-    // s_part[w + NRB k][st][lane] for the KS slices k (2 KB per wave)
+  auto part_r = [&](int jb, f32x4_t (*sp)[2][64], MidX<NRB>* sx) __attribute__((always_inline)) {
+    // sp[w + NRB k][st][lane] for the KS slices k (2 KB per wave)
     f32x4_t pr[KS][2];
-    lds_read_parts<KS, 2048 * NRB>(lds_off(&s_part[w][0][lane]), pr);
+    lds_read_parts<KS, 2048 * NRB>(lds_off(&sp[w][0][lane]), pr);
     f32x4_t ssum[2] = {pr[0][0], pr[0][1]};
 #pragma unroll
     for (int k = 1; k < KS; ++k) {
@@ -1820,7 +1840,7 @@ __device__ __forceinline__ void mla_mid_range(const AttnParams& p, int b, int g,
       const float a = grow ? alpha : 1.f;
       lsum *= a;
       m = mnew;
-      if (lg == 0) s_x->alpha[w][l16] = a;
+      if (lg == 0) sx->alpha[w][l16] = a;
     }
     const float nmref = -(m == -INFINITY ? 0.f : m);
     float e[8];
@@ -1831,8 +1851,8 @@ __device__ __forceinline__ void mla_mid_range(const AttnParams& p, int b, int g,
     const uint4 bits = make_uint4(pack2<BF16>(e[0], e[1]), pack2<BF16>(e[2], e[3]),
                                   pack2<BF16>(e[4], e[5]), pack2<BF16>(e[6], e[7]));
     lsum = sum2<BF16>(bits.x, sum2<BF16>(bits.y, sum2<BF16>(bits.z, sum2<BF16>(bits.w, lsum))));
-    s_x->pb[w][lane] = as_i16x8(bits);
-    if (lane == 0) lds_write_b32(lds_off(&s_x->flag[w]), any);
+    sx->pb[w][lane] = as_i16x8(bits);
+    if (lane == 0) lds_write_b32(lds_off(&sx->flag[w]), any);
   };
   auto part_pv = [&](const i32x2_t (&vr)[8]) __attribute__((always_inline)) {
     // every row block's P^T, rescale factor and flag in one LDS round trip
@@ -1857,8 +1877,79 @@ __device__ __forceinline__ void mla_mid_range(const AttnParams& p, int b, int g,
     }
   };
 
+  // fp8, read in place from the swizzled stages (as in the narrow kernel)
+  constexpr int kPitch8 = kPieces8 * 16;
+  auto part_s8 = [&](const uint8_t* kv, f32x4_t (*sp)[2][64]) __attribute__((always_inline)) {
+    f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    const uint32_t base = lds_off(kv) + l16 * kPitch8 + 8 * (lg & 1);  // rows l16 and 16 + l16
+    const int sw = swz8(l16);
+    auto kaddr = [&](int kk) { return base + 16 * ((2 * kk + (lg >> 1)) ^ sw); };
+#pragma unroll
+    for (int j = 0; j + 3 <= KMAX; j += 3) {
+      if (j + 3 <= nks) {
+        i32x2_t kr[6];
+        lds_read6_b64(kaddr(k0 + j), kaddr(k0 + j + 1), kaddr(k0 + j + 2), kr);
+#pragma unroll
+        for (int u = 0; u < 3; ++u)
+#pragma unroll
+          for (int st2 = 0; st2 < 2; ++st2)
+            sacc[st2] = mfma16<BF16>(fp8x8_to_bf16(kr[2 * u + st2]), qreg[j + u], sacc[st2]);
+      }
+    }
+    if constexpr (KMAX % 3 != 0) {
+      constexpr int j = KMAX / 3 * 3;
+      if (nks - j == 2) {
+        i32x2_t kr[4];
+        lds_read4_b64(kaddr(k0 + j), kaddr(k0 + j + 1), kr);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int st2 = 0; st2 < 2; ++st2)
+            sacc[st2] = mfma16<BF16>(fp8x8_to_bf16(kr[2 * u + st2]), qreg[j + u], sacc[st2]);
+      } else if (nks - j == 1) {
+        i32x2_t kr[2];
+        lds_read2_b64(kaddr(k0 + j), kr);
+#pragma unroll
+        for (int st2 = 0; st2 < 2; ++st2)
+          sacc[st2] = mfma16<BF16>(fp8x8_to_bf16(kr[st2]), qreg[j], sacc[st2]);
+      }
+    }
+    lds_write_part(lds_off(&sp[w][0][lane]), sacc[0], sacc[1]);
+  };
+  auto part_v8 = [&](const uint8_t* kv, i16x8_t (&va)[4]) __attribute__((always_inline)) {
+    // lane group q holds P^T's k = 8q + j, i.e. tokens 4q + j (j < 4) and 12 + 4q + j
+    const int q = lane >> 4, j = (lane & 15) >> 1, h = lane & 1;
+    const int trow = j < 4 ? 4 * q + j : 12 + 4 * q + j;
+    const int sw = swz8(trow);
+    const uint32_t rb = lds_off(kv) + trow * kPitch8 + 8 * h;
+    i32x2_t vr[4];
+    lds_read4_tr8(rb + 16 * ((4 * w + 0) ^ sw), rb + 16 * ((4 * w + 1) ^ sw), rb + 16 * ((4 * w + 2) ^ sw),
+                  rb + 16 * ((4 * w + 3) ^ sw), vr);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) va[d] = fp8x8_to_bf16(vr[d]);
+  };
+  auto part_pv8 = [&](const uint8_t* kv, MidX<NRB>* sx) __attribute__((always_inline)) {
+    i16x8_t va[4];
+    part_v8(kv, va);
+    i32x4_t pbs[NRB];
+    float al[NRB];
+    int fl[NRB];
+    lds_read_pv_blocks<NRB>(lds_off(&sx->pb[0][lane]), lds_off(&sx->alpha[0][l16]), lds_off(&sx->flag[0]), pbs,
+                            al, fl);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      if (__builtin_amdgcn_readfirstlane(fl[rb])) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) oacc[rb][d] *= al[rb];
+      }
+      const i16x8_t pb = __builtin_bit_cast(i16x8_t, pbs[rb]);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) oacc[rb][d] = mfma16<BF16>(va[d], pb, oacc[rb][d]);
+    }
+  };
+
   const bool page_tiles = P % kTK2 == 0 && j0 % kTK2 == 0;
-  PageLanes<FP8> plane;
+  PageLanes<FP8, FP8> plane;
   if (page_tiles) plane.init(p, g, w, lane);
   if (jhi > j0) {
     const int pfirst = j0 / P, plast = (jhi - 1) / P;
@@ -1887,21 +1978,19 @@ __device__ __forceinline__ void mla_mid_range(const AttnParams& p, int b, int g,
           if ((k & 63) == 0) ptab = s_pages[div_by_magic((uint32_t)(tile_at(k + lane) - wbP), p.page_magic)];
           const int page = __builtin_amdgcn_readlane(ptab, k & 63);
           if constexpr (FP8)
-            dma_page_fp8(p, page, stage, jb, we, wbP, plane, w);
+            dma_page_fp8s(p, page, stage, jb, we, wbP, plane, w);
           else
             dma_page_bf16(p, page, stage, jb, we, wbP, plane, w);
         } else {
           if constexpr (FP8)
-            dma_tile8(p, s_pages, stage, jb, we, wbP, g, w, lane);
+            dma_tile8<true>(p, s_pages, stage, jb, we, wbP, g, w, lane);
           else
             dma_tile(p, s_pages, stage, jb, we, wbP, g, w, lane);
         }
       };
-      dma(s_kv0, 0);
-      dma(s_kv1, 1);
-      if constexpr (NST > 3) dma(s_kv2, 2);
-      if constexpr (NST > 4) dma(s_kv3, 3);
       if constexpr (!FP8) {
+        dma(s_kv0, 0);
+        dma(s_kv1, 1);
 #define PA_MLA_MSTEP(K, CUR, NEXT)                                                            \
   {                                                                                         \
     __builtin_amdgcn_s_waitcnt(kWaitImm); /* tile K's direct loads are done */              \
@@ -1911,7 +2000,7 @@ __device__ __forceinline__ void mla_mid_range(const AttnParams& p, int b, int g,
     i32x2_t vr[8];                                                                          \
     part_v(CUR, vr);                                                                        \
     lds_barrier();                                                                           \
-    if (w < NRB) part_r(ws + (K) * kTK2);                                                   \
+    if (w < NRB) part_r(ws + (K) * kTK2, s_part, s_x);                                      \
     lds_barrier();                                                                           \
     part_pv(vr);                                                                            \
   }
@@ -1925,49 +2014,31 @@ __device__ __forceinline__ void mla_mid_range(const AttnParams& p, int b, int g,
         }
 #undef PA_MLA_MSTEP
       } else {
-        // fp8: as in the narrow kernel, the bf16 tile buffer holds tile K during
-        // step K and tile K+1 is widened into it after the reducing waves' softmax
-        __builtin_amdgcn_s_waitcnt(kWaitImm);  // tile 0's direct loads are done
+        // fp8 read in place, one barrier per tile (as in the narrow kernel): step K
+        // computes the partial scores of tile K+1 on every wave, the softmax of tile
+        // K on waves 0..NRB-1 and the PV of tile K-1; partial scores and P^T are
+        // double-buffered, stage t % NST holds tile t
+        static_assert(NST == 6, "fp8 stages");
+        constexpr int kWait3 = (NST - 3) * kMinDma, kWait4 = (NST - 4) * kMinDma;
+        static_assert(kWait3 < 16, "vmcnt field");
+        constexpr int kWaitImm3 = kWait3 | 0x70 | 0xF00, kWaitImm4 = kWait4 | 0x70 | 0xF00;
+        auto stage = [&](int t) { return s_kv0 + kStage8 * (t % NST); };
+#pragma unroll
+        for (int t = 0; t < NST - 2; ++t) dma(stage(t), t);
+        __builtin_amdgcn_s_waitcnt(kWaitImm3);  // tile 0 has landed
         lds_barrier();
-        convert_tile(s_kv0, s_wide, tid);
-#define PA_MLA_MFSTEP(K, NEXTRAW, DST)                                                        \
-  {                                                                                         \
-    lds_barrier();                                                                           \
-    dma(DST, (K) + NST - 1);                                                                \
-    part_s(s_wide);                                                                         \
-    i32x2_t vr[8];                                                                          \
-    part_v(s_wide, vr);                                                                     \
-    __builtin_amdgcn_s_waitcnt(kWaitImm); /* tile K+1's direct loads are done */            \
-    lds_barrier();                                                                           \
-    if constexpr (NRB == 2) {                                                               \
-      if (w < NRB)                                                                          \
-        part_r(ws + (K) * kTK2);                                                            \
-      else                                                                                  \
-        convert_tile(NEXTRAW, s_wide, tid - 64 * NRB, 64 * (kNW2 - NRB));                   \
-    } else {                                                                                \
-      if (w < NRB) part_r(ws + (K) * kTK2);                                                 \
-      convert_tile(NEXTRAW, s_wide, tid);                                                   \
-    }                                                                                       \
-    lds_barrier();                                                                           \
-    part_pv(vr);                                                                            \
-  }
-        static_assert(NST == 5, "fp8 stage rotation");
-        // two row blocks: the six waves that do not run a softmax widen the next tile
-        // meanwhile (three pieces each); four row blocks: every wave widens a share
-        // after the softmaxes (four waves alone would need more registers than fit)
-        static_assert(kTK2 * kPieces8 == 3 * 64 * (kNW2 - 2), "three pieces per widening thread");
-        for (int k = 0; k < nk; k += 5) {
-          PA_MLA_MFSTEP(k, s_kv1, s_kv4);
-          if (k + 1 >= nk) break;
-          PA_MLA_MFSTEP(k + 1, s_kv2, s_kv0);
-          if (k + 2 >= nk) break;
-          PA_MLA_MFSTEP(k + 2, s_kv3, s_kv1);
-          if (k + 3 >= nk) break;
-          PA_MLA_MFSTEP(k + 3, s_kv4, s_kv2);
-          if (k + 4 >= nk) break;
-          PA_MLA_MFSTEP(k + 4, s_kv0, s_kv3);
+        part_s8(stage(0), s_part);
+        __builtin_amdgcn_s_waitcnt(kWaitImm4);  // tile 1 has landed
+        lds_barrier();
+        for (int k = 0; k < nk; ++k) {
+          dma(stage(k + NST - 2), k + NST - 2);  // the stage of tile k-2, read before the last barrier
+          part_s8(stage(k + 1), s_part + kNW2 * ((k + 1) & 1));  // past the last tile: unused
+          if (w < NRB) part_r(ws + k * kTK2, s_part + kNW2 * (k & 1), s_x + (k & 1));
+          if (k > 0) part_pv8(stage(k - 1), s_x + ((k - 1) & 1));
+          __builtin_amdgcn_s_waitcnt(kWaitImm4);  // tile k+2 has landed
+          lds_barrier();
         }
-#undef PA_MLA_MFSTEP
+        part_pv8(stage(nk - 1), s_x + ((nk - 1) & 1));
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no loads in flight into the stages
       __syncthreads();
@@ -2035,23 +2106,23 @@ __device__ __forceinline__ void mla_mid_range(const AttnParams& p, int b, int g,
 
 template <bool FP8, int NRB>
 __global__ __launch_bounds__(64 * kNW2, 1) void mla_mid_kernel(AttnParams p, int ngroups) {
-  constexpr int STAGE = FP8 ? kStage8 : kStage2;
+  // bf16: three stages; fp8: the NST stages contiguous from s_kv0, and the partial
+  // scores and the P^T exchange double-buffered
   constexpr int NST = kMidStages<FP8>;
-  __shared__ __align__(16) uint8_t s_kv0[STAGE];
-  __shared__ __align__(16) uint8_t s_kv1[STAGE];
-  __shared__ __align__(16) uint8_t s_kv2[STAGE];
-  __shared__ __align__(16) uint8_t s_kv3[NST > 3 ? STAGE : 16];
-  __shared__ __align__(16) uint8_t s_kv4[NST > 4 ? STAGE : 16];
-  __shared__ __align__(16) uint8_t s_wide[FP8 ? kStage2 : 16];  // fp8: the widened tile
-  __shared__ __align__(16) f32x4_t s_part[kNW2][2][64];          // partial scores
-  __shared__ __align__(16) MidX<NRB> s_x;
+  static_assert(FP8 || NST == 3, "bf16 stages");
+  __shared__ __align__(16) uint8_t s_kv0[FP8 ? NST * kStage8 : kStage2];
+  __shared__ __align__(16) uint8_t s_kv1[FP8 ? 16 : kStage2];
+  __shared__ __align__(16) uint8_t s_kv2[FP8 ? 16 : kStage2];
+  __shared__ __align__(16) f32x4_t s_part[(FP8 ? 2 : 1) * kNW2][2][64];  // partial scores
+  __shared__ __align__(16) MidX<NRB> s_xb[FP8 ? 2 : 1];
+  MidX<NRB>* const s_x = s_xb;
   __shared__ int s_pages[kPageWinM];
   if (p.bal_blocks > 0) {
     BalCursor cur;
     if (!cur.start(p, blockIdx.x)) return;
     do {
       mla_mid_range<FP8, NRB>(p, cur.b, cur.g, cur.L, cur.j0(p), cur.j1(p), !cur.whole(), cur.slot(p), 0,
-                              s_kv0, s_kv1, s_kv2, s_kv3, s_kv4, s_wide, s_part, &s_x, s_pages);
+                              s_kv0, s_kv1, s_kv2, s_part, s_x, s_pages);
     } while (cur.next(p));
     return;
   }
@@ -2064,7 +2135,7 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_mid_kernel(AttnParams p, int
   bool to_ws;
   if (!mla_item_range(p, b, c, L, j0, j1, to_ws)) return;
   mla_mid_range<FP8, NRB>(p, b, g, L, j0, j1, to_ws, (int64_t)(b * p.num_kv_heads + g) * p.max_chunks + c,
-                          c, s_kv0, s_kv1, s_kv2, s_kv3, s_kv4, s_wide, s_part, &s_x, s_pages);
+                          c, s_kv0, s_kv1, s_kv2, s_part, s_x, s_pages);
 }
 
 hipError_t launch_rows(const AttnParams& p, hipStream_t stream) {

@@ -619,35 +619,6 @@ __device__ __forceinline__ void lds_read12_b128(uint32_t a, i32x4_t (&r)[12]) {
       : "v"(a)
       : "memory");
 }
-// Three 16-byte reads at a0, a1, a2.
-__device__ __forceinline__ void lds_read3_b128(uint32_t a0, uint32_t a1, uint32_t a2, i32x4_t& r0, i32x4_t& r1,
-                                               i32x4_t& r2) {
-  asm volatile(
-      "ds_read_b128 %0, %3\n\t"
-      "ds_read_b128 %1, %4\n\t"
-      "ds_read_b128 %2, %5\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r0), "=&v"(r1), "=&v"(r2)
-      : "v"(a0), "v"(a1), "v"(a2)
-      : "memory");
-}
-// Six 16-byte writes.
-__device__ __forceinline__ void lds_write6_b128(uint32_t a0, i32x4_t v0, uint32_t a1, i32x4_t v1,
-                                                uint32_t a2, i32x4_t v2, uint32_t a3, i32x4_t v3,
-                                                uint32_t a4, i32x4_t v4, uint32_t a5, i32x4_t v5) {
-  asm volatile(
-      "ds_write_b128 %0, %1\n\t"
-      "ds_write_b128 %2, %3\n\t"
-      "ds_write_b128 %4, %5\n\t"
-      "ds_write_b128 %6, %7\n\t"
-      "ds_write_b128 %8, %9\n\t"
-      "ds_write_b128 %10, %11\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      :
-      : "v"(a0), "v"(v0), "v"(a1), "v"(v1), "v"(a2), "v"(v2), "v"(a3), "v"(v3), "v"(a4), "v"(v4),
-        "v"(a5), "v"(v5)
-      : "memory");
-}
 // fp8 direct path: six 8-byte reads (three addresses, each also at +9216 = 16 rows).
 __device__ __forceinline__ void lds_read6_b64(uint32_t a0, uint32_t a1, uint32_t a2, i32x2_t (&r)[6]) {
   asm volatile(
@@ -769,9 +740,10 @@ __device__ __forceinline__ void dma_tile(const AttnParams& p, const int* s_pages
   }
 }
 
-// fp8 KV: a tile is 32 rows x 576 one-byte codes, loaded linearly (36 pieces of
-// 16 codes per row, 18 wave instructions) and widened to the bf16 layout above
-// by convert_tile before the math.
+// fp8 KV: a tile is 32 rows x 576 one-byte codes (36 pieces of 16 codes per row,
+// 18 wave instructions).  The narrow and mid kernels read the codes in place from
+// a swizzled layout (swz8) and widen them in registers; the many-rows kernel loads
+// them linearly and widens the tile into the bf16 layout above (convert_tile).
 constexpr int kPieces8 = kDqk / 16;                // 16-byte pieces of an fp8 row (36)
 constexpr int kDma8 = kTK2 * kPieces8 / 64;        // 1-KB direct loads per fp8 tile (18)
 constexpr int kStage8 = kDma8 * 1024;
@@ -890,43 +862,22 @@ __device__ __forceinline__ WidePiece convert_piece(i32x4_t x, int q, uint32_t ds
                    i32x4_t{o[0], o[1], o[2], o[3]}, i32x4_t{o[4], o[5], o[6], o[7]}};
 }
 
-// Widening of a whole tile by n threads (t = 0..n-1), 2n < pieces <= 3n.
-// BATCH: all reads of a thread in one LDS round trip and all writes in another
-// (whether a thread has a third piece is uniform over its wave: the callers' n
-// and 1152 - 2n are multiples of 64); otherwise two smaller rounds, which need
-// fewer registers.
-template <bool BATCH = true>
-__device__ __forceinline__ void convert_tile(const uint8_t* src, uint8_t* dst, int t, int n) {
-  const uint32_t a = lds_off(src) + 16 * t;
+// Widening of a whole tile by the workgroup's threads (three rounds at most: two
+// pieces, then a third for the first threads).
+__device__ __forceinline__ void convert_tile(const uint8_t* src, uint8_t* dst, int tid) {
+  constexpr int n = 64 * kNW2;
+  static_assert(kTK2 * kPieces8 > 2 * n && kTK2 * kPieces8 <= 3 * n, "three rounds");
+  const uint32_t a = lds_off(src) + 16 * tid;
   const uint32_t d = lds_off(dst);
   i32x4_t x0, x1;
-  if (!BATCH) {
-    lds_read2_b128(a, a + 16 * n, x0, x1);
-    const WidePiece p0 = convert_piece(x0, t, d);
-    const WidePiece p1 = convert_piece(x1, t + n, d);
-    lds_write4_b128(p0.a0, p0.v0, p0.a1, p0.v1, p1.a0, p1.v0, p1.a1, p1.v1);
-    if (t + 2 * n < kTK2 * kPieces8) {
-      const WidePiece p2 = convert_piece(lds_read_b128(a + 2 * 16 * n), t + 2 * n, d);
-      lds_write2_b128(p2.a0, p2.v0, p2.a1, p2.v1);
-    }
-  } else if (__builtin_amdgcn_readfirstlane(t) + 2 * n < kTK2 * kPieces8) {
-    i32x4_t x2;
-    lds_read3_b128(a, a + 16 * n, a + 32 * n, x0, x1, x2);
-    const WidePiece p0 = convert_piece(x0, t, d);
-    const WidePiece p1 = convert_piece(x1, t + n, d);
-    const WidePiece p2 = convert_piece(x2, t + 2 * n, d);
-    lds_write6_b128(p0.a0, p0.v0, p0.a1, p0.v1, p1.a0, p1.v0, p1.a1, p1.v1, p2.a0, p2.v0, p2.a1, p2.v1);
-  } else {
-    lds_read2_b128(a, a + 16 * n, x0, x1);
-    const WidePiece p0 = convert_piece(x0, t, d);
-    const WidePiece p1 = convert_piece(x1, t + n, d);
-    lds_write4_b128(p0.a0, p0.v0, p0.a1, p0.v1, p1.a0, p1.v0, p1.a1, p1.v1);
+  lds_read2_b128(a, a + 16 * n, x0, x1);
+  const WidePiece p0 = convert_piece(x0, tid, d);
+  const WidePiece p1 = convert_piece(x1, tid + n, d);
+  lds_write4_b128(p0.a0, p0.v0, p0.a1, p0.v1, p1.a0, p1.v0, p1.a1, p1.v1);
+  if (tid + 2 * n < kTK2 * kPieces8) {
+    const WidePiece p2 = convert_piece(lds_read_b128(a + 2 * 16 * n), tid + 2 * n, d);
+    lds_write2_b128(p2.a0, p2.v0, p2.a1, p2.v1);
   }
-}
-template <bool BATCH = true>
-__device__ __forceinline__ void convert_tile(const uint8_t* src, uint8_t* dst, int tid) {
-  static_assert(kTK2 * kPieces8 > 2 * 64 * kNW2 && kTK2 * kPieces8 <= 3 * 64 * kNW2, "three rounds");
-  convert_tile<BATCH>(src, dst, tid, 64 * kNW2);
 }
 
 // Token range of work item c (internal chunk or explicit split) of request b;
@@ -1150,7 +1101,7 @@ __device__ __forceinline__ void mla_rows_range(const AttnParams& p, int b, int g
     dma(NEXT3, tile_at((K) + 3));                                                           \
     const uint8_t* src = CUR;                                                               \
     if constexpr (FP8) {                                                                    \
-      convert_tile<false>(CUR, s_wide, tid);                                                \
+      convert_tile(CUR, s_wide, tid);                                                       \
       __syncthreads();                                                                       \
       src = s_wide;                                                                         \
     }                                                                                       \

@@ -749,7 +749,7 @@ constexpr int kDma8 = kTK2 * kPieces8 / 64;        // 1-KB direct loads per fp8 
 constexpr int kStage8 = kDma8 * 1024;
 static_assert(kTK2 * kPieces8 % 64 == 0, "an fp8 tile is a whole number of 1-KB wave loads");
 
-// fp8 stage layout read in place by the narrow kernel: piece p of row r at slot
+// fp8 stage layout read in place by the narrow and mid kernels: piece p of row r at slot
 // p ^ swz8(r), within p's aligned group of four (36 pieces per row), so that the
 // 16 rows of an 8-byte operand read and the 8 rows of a transposed read fall on
 // distinct banks.
@@ -1207,10 +1207,13 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_rows_kernel(AttnParams p, in
 // Per 32-token tile (LDS stages fed by direct loads, as above):
 //   S^T = K Q^T is split over the 576 dims: waves 0..5 each take three 32-dim
 //   k-steps (one 16x16x32 MFMA per k-step and 16-token block) and leave their
-//   partial scores in LDS; after a barrier every wave adds the six partials for
-//   all 16 rows x 32 tokens and runs the same online softmax (identical state in
-//   every wave);
+//   partial scores in LDS; wave 6 adds the six partials for all 16 rows x 32
+//   tokens, runs the online softmax and publishes P^T and the rows' rescale
+//   factors;
 //   O^T += V^T P^T is split over the 512 V dims: wave w owns dims [64w, 64w+64).
+// bf16 tiles are read in place from four stages, two barriers per tile; fp8
+// tiles too (codes widened in registers), pipelined one tile deep over double-
+// buffered partial scores and P^T with one barrier per tile (mla_narrow_range).
 constexpr int kNS = kDqk / 32 / 3;  // waves that compute partial scores (6); wave kNS reduces
 static_assert(kNS < kNW2, "a wave beyond the partial-score waves does the softmax");
 // exchange from the reducing wave to the others
@@ -1639,7 +1642,8 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_narrow_kernel(AttnParams p, 
 // 0..NRB-1 then each sum one row block's partials and run its online softmax;
 // every wave does PV for its 64 V dims over all row blocks.  The KV stream is
 // the narrow kernel's (direct loads, bare barriers, stage reads in asm); three
-// bf16 stages or five fp8 raw stages fit next to the 16 KB of partial scores.
+// bf16 stages fit next to the 16 KB of partial scores, and fp8 is read in place
+// from six stages next to double-buffered partial scores and P^T.
 template <int NRB>
 struct MidX {
   i16x8_t pb[NRB][64];    // P^T of each row block in the PV B-operand layout

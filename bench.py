@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the paged-attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c3|c5|c4_h16_q1_bf16|...]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c3|c5|c4_h16_q1_bf16|sparse_mla_h16_bf16|...]
 
 Default workload: the Llama-70B-like GQA decode (64 requests, q_len 1, 64 query
 / 8 KV heads, head_dim 128, bf16, page 16, KV lengths uniform in [512, 8192]).
@@ -43,6 +43,11 @@ def make_workload(name: str):
         return W.config3(poison=False)
     if name == "c5":
         return W.config5(poison=False)
+    if name.startswith("sparse"):
+        # sparse_<mla|gqa>_h<heads>_<bf16|fp8>: top-2048 selected rows per query
+        _, kind, h, dt = name.split("_")
+        return W.config_sparse(num_heads=int(h[1:]), kv_dtype=W.DT_FP8 if dt == "fp8" else W.DT_BF16,
+                               mla=kind == "mla", poison=False)
     if name.startswith("c4"):
         _, h, q, dt = name.split("_")
         return W.config4(num_heads=int(h[1:]), q_len=int(q[1:]),

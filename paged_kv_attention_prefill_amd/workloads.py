@@ -300,6 +300,41 @@ def config4(num_heads: int = 16, q_len: int = 1, kv_dtype: int = DT_BF16, batch:
                  poison=poison, **kw)
 
 
+def config_sparse(num_heads: int = 16, kv_dtype: int = DT_BF16, batch: int = 128,
+                  topk: int = 2048, pool_factor: int = 4, mla: bool = True,
+                  poison: bool = True, sub: int = 0, **kw) -> Workload:
+    """Sparse-selected KV decode: every query (q_len 1, one request each) attends
+    only the ``topk`` token rows a sparse indexer picked for it, given as an
+    index list into a token pool (page size 1, so kv_indices are token slots).
+    The pool holds ``pool_factor`` times the selected rows; the selection of
+    each query is a uniformly random set of distinct slots, in ascending slot
+    order; rows nobody selected are poisoned (NaN) unless ``poison`` is off.
+    MLA shape by default (576/512 shared latent rows, one KV head, scale
+    1/sqrt(192), bf16 or fp8-e4m3 KV); ``mla=False`` gives a GQA shape (32 query
+    / 8 KV heads, head_dim 128, bf16)."""
+    seed = 6000 + sub
+    rng = np.random.default_rng(seed)
+    kv_lens = np.full(batch, topk, dtype=np.int64)
+    if "kv_lens" in kw:
+        kv_lens = np.asarray(kw.pop("kv_lens"), dtype=np.int64)
+    pool = max(1, int(kv_lens.sum()) * pool_factor)
+    if mla:
+        w = build(rng, seed, f"sparse_mla_h{num_heads}_{DT_NAMES[kv_dtype]}", q_lens=[1] * len(kv_lens),
+                  kv_lens=kv_lens, num_qo_heads=num_heads, num_kv_heads=1, head_dim_qk=576,
+                  head_dim_vo=512, page_size=1, q_dtype=DT_BF16, kv_dtype=kv_dtype, shared_kv=True,
+                  sm_scale=1.0 / math.sqrt(192.0), pool_pages=pool, poison=poison, **kw)
+    else:
+        w = build(rng, seed, "sparse_gqa", q_lens=[1] * len(kv_lens), kv_lens=kv_lens,
+                  num_qo_heads=kw.pop("num_qo_heads", 32), num_kv_heads=kw.pop("num_kv_heads", 8),
+                  head_dim_qk=128, head_dim_vo=128, page_size=1, q_dtype=kv_dtype,
+                  kv_dtype=kv_dtype, pool_pages=pool, poison=poison, **kw)
+    # an indexer emits its picks in position order
+    for b in range(len(kv_lens)):
+        seg = slice(int(w.kv_indptr[b]), int(w.kv_indptr[b + 1]))
+        w.kv_indices[seg] = np.sort(w.kv_indices[seg])
+    return w
+
+
 def config5(num_queries: int = 128, kv_len: int = 131072, num_kv_splits: int = 16,
             poison: bool = True, **kw) -> Workload:
     """Shared-prefix split-KV decode with KV broadcast: 128 query batches

@@ -49,3 +49,9 @@ def test_c5_broadcast_split_decode_full():
 def test_c4_mla_decode_full(h, ql, dt):
     run_sampled(W.config4(num_heads=h, q_len=ql, kv_dtype=dt), f"c4 full h{h} q{ql} {W.DT_NAMES[dt]}",
                 n=96)
+
+
+@pytest.mark.parametrize("dt", [W.DT_BF16, W.DT_FP8])
+def test_sparse_mla_decode_full(dt):
+    """128 queries x top-2048 selected latent rows from a 4x larger poisoned pool."""
+    run_sampled(W.config_sparse(num_heads=16, kv_dtype=dt), f"sparse full h16 {W.DT_NAMES[dt]}", n=96)

@@ -342,3 +342,42 @@ def test_decode_takes_mfma_path_with_and_without_internal_chunks():
 def test_plan_names(name, prefix):
     step = R.prepare(R.upload(small(name)))
     assert step.attention_kernel_name.startswith(prefix), step.attention_kernel_name
+
+
+def sparse_cases():
+    """Sparse-selected KV (page size 1: kv_indices are each query's selected
+    token slots in a larger, NaN-poisoned pool), through every decode kernel
+    family: MLA narrow (16 rows), mid (64 rows), many-rows (128 rows), GQA."""
+    lens = [1, 31, 32, 33, 700, 2048]
+    return {
+        "mla_h16_bf16": lambda: W.config_sparse(num_heads=16, kv_lens=lens, pool_factor=3),
+        "mla_h16_fp8": lambda: W.config_sparse(num_heads=16, kv_dtype=W.DT_FP8, kv_lens=lens,
+                                               pool_factor=3),
+        "mla_h64_fp8": lambda: W.config_sparse(num_heads=64, kv_dtype=W.DT_FP8,
+                                               kv_lens=[17, 500, 1500], pool_factor=2),
+        "mla_h128_bf16": lambda: W.config_sparse(num_heads=128, kv_lens=[5, 300, 1000],
+                                                 pool_factor=2),
+        "gqa": lambda: W.config_sparse(mla=False, kv_lens=[1, 64, 65, 999, 2048], pool_factor=3),
+    }
+
+
+@pytest.mark.parametrize("name", list(sparse_cases()))
+def test_sparse_selected_kv(name):
+    run_and_check(sparse_cases()[name](), f"sparse {name}")
+
+
+@pytest.mark.parametrize("name", ["mla_h16_bf16", "gqa"])
+def test_sparse_selection_routed_halves_merge_on_gpu(name):
+    """Two holders each see an interleaved half of every query's selection: the
+    two partial calls (fp32 O and LSE) merged by merge_states match the oracle
+    over the whole selection."""
+    from test_oracle import select_subset
+    w = sparse_cases()[name]()
+    o, lse, _ = OR.attention(w)
+    parts = [R.run(R.upload(select_subset(w, lambda b, i, r=r: i % 2 == r)), out_dtype=torch.float32)
+             for r in (0, 1)]
+    mo, ml = B.merge_states(torch.stack([p["o"] for p in parts]).contiguous(),
+                            torch.stack([p["lse"] for p in parts]).contiguous(),
+                            out_dtype=parts[0]["o"].dtype)
+    torch.cuda.synchronize()
+    check_rows(w, to64(mo), to64(ml), o, lse, label=f"routed halves {name}")

@@ -43,6 +43,11 @@ def small_cases():
         "c4_small_fp8": lambda: W.config4(num_heads=16, q_len=4, kv_dtype=W.DT_FP8, batch=3,
                                           min_len=1, max_len=150),
         "c5_small": lambda: W.config5(num_queries=3, kv_len=300, num_kv_splits=4),
+        "sparse_mla_bf16": lambda: W.config_sparse(num_heads=16, kv_lens=[1, 40, 129], pool_factor=3),
+        "sparse_mla_fp8": lambda: W.config_sparse(num_heads=8, kv_dtype=W.DT_FP8, kv_lens=[3, 77],
+                                                  pool_factor=2),
+        "sparse_gqa": lambda: W.config_sparse(mla=False, num_qo_heads=8, num_kv_heads=2,
+                                              kv_lens=[5, 70, 33], pool_factor=4),
     }
 
 
@@ -240,6 +245,44 @@ def test_split_then_merge_equals_unsplit(name, S):
     po, pl, _ = OR.attention(w, num_kv_splits=S)
     rows = o.shape[0] * o.shape[1]
     mo, ml = OR.merge_states(po.reshape(S, rows, -1), pl.reshape(S, rows))
+    close(mo, o.reshape(rows, -1))
+    close(ml, lse.reshape(rows))
+
+
+def select_subset(w, keep):
+    """The same queries over a subset of each query's selected token slots
+    (page size 1): ``keep(b, i)`` says whether the i-th selected slot of query
+    batch b stays."""
+    assert w.page_size == 1
+    idx, indptr = [], [0]
+    for b in range(w.batch):
+        sel = w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]]
+        part = [int(x) for i, x in enumerate(sel) if keep(b, i)]
+        idx += part
+        indptr.append(len(idx))
+    n = np.diff(indptr)
+    return dataclasses.replace(w, kv_indices=np.asarray(idx, dtype=np.int32),
+                               kv_indptr=np.asarray(indptr, dtype=np.int32),
+                               kv_last_page_len=np.where(n > 0, 1, 0).astype(np.int32),
+                               kv_lens=n.astype(np.int64))
+
+
+@pytest.mark.parametrize("name", ["sparse_mla_bf16", "sparse_mla_fp8", "sparse_gqa"])
+def test_sparse_selection_routed_halves_merge_to_whole(name):
+    """Partial attention over two disjoint halves of every query's selected rows
+    (interleaved, as two holders of a sparsely selected cache would see them),
+    merged through their LSE, equals attention over the whole selection; a
+    query whose half is empty contributes a -inf state."""
+    w = small_cases()[name]()
+    o, lse, _ = OR.attention(w)
+    halves = [select_subset(w, lambda b, i, r=r: i % 2 == r) for r in (0, 1)]
+    parts = [OR.attention(h) for h in halves]
+    rows = o.shape[0] * o.shape[1]
+    po = np.stack([p[0].reshape(rows, -1) for p in parts])
+    pl = np.stack([p[1].reshape(rows) for p in parts])
+    if (w.kv_lens == 1).any():
+        assert np.isneginf(pl[1]).any()  # a one-row selection leaves half 1 empty
+    mo, ml = OR.merge_states(po, pl)
     close(mo, o.reshape(rows, -1))
     close(ml, lse.reshape(rows))
 

@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the paged-attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c3|c5|c4_h16_q1_bf16|sparse_mla_h16_bf16|...]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c3|c5|c4_h16_q1_bf16|sparse_mla_h16_bf16|long_decode_b1|...]
 
 Default workload: the Llama-70B-like GQA decode (64 requests, q_len 1, 64 query
 / 8 KV heads, head_dim 128, bf16, page 16, KV lengths uniform in [512, 8192]).
@@ -43,6 +43,10 @@ def make_workload(name: str):
         return W.config3(poison=False)
     if name == "c5":
         return W.config5(poison=False)
+    if name == "long_decode_b1":
+        # one request, 131072 KV tokens: all parallelism comes from splitting the KV
+        return W.config2(batch=1, min_len=131072, max_len=131072, dtype=W.DT_F16, page_size=128,
+                         num_qo_heads=32, num_kv_heads=8, poison=False)
     if name.startswith("sparse"):
         # sparse_<mla|gqa>_h<heads>_<bf16|fp8>: top-2048 selected rows per query
         _, kind, h, dt = name.split("_")

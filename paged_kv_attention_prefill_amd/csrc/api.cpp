@@ -358,7 +358,13 @@ int run_plan(const Plan& pl, AttnParams p, void* ws, size_t ws_bytes, void* cons
   if (e != hipSuccess) return PA_ERR_HIP;
   if (timed && hipEventRecord(static_cast<hipEvent_t>(events[1]), stream) != hipSuccess)
     return PA_ERR_HIP;
-  if (pl.chunk_tokens > 0 || pl.bal_blocks > 0) e = pa::launch_chunk_merge(p, stream);
+  if (pl.chunk_tokens > 0 || pl.bal_blocks > 0) {
+    // many states per row (few long items over many workgroups): split each
+    // row's states over the lane groups of a workgroup
+    const int64_t items = (int64_t)p.batch * p.num_kv_heads;
+    const bool wide = (pl.bal_blocks > 0 && pl.bal_blocks >= 32 * items) || pl.max_chunks >= 32;
+    e = pa::launch_chunk_merge(p, wide, stream);
+  }
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

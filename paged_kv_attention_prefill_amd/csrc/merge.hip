@@ -116,6 +116,97 @@ hipError_t launch_vt(const void* v, const float* s, int S, int64_t rows, int D, 
   return hipGetLastError();
 }
 
+// Where the partial states of folded row (b, KV head g, r) sit: the number of
+// states and the workspace row of the first (the next ones are WR rows apart).
+__device__ __forceinline__ int row_states(const AttnParams& p, int b, int g, int r,
+                                          int64_t& wrow0) {
+  const int WR = p.ws_rows;
+  const int item = b * p.num_kv_heads + g;
+  if (p.bal_blocks > 0) {
+    // balanced split: the item's partial states sit in slots item + i for its
+    // workgroups i = first..last
+    const int i0 = p.ws_seg[2 * item], i1 = p.ws_seg[2 * item + 1];
+    wrow0 = ((int64_t)item + i0) * WR + r;
+    return i1 - i0 + 1;
+  }
+  const int kb = p.broadcast ? 0 : b;
+  const int n = p.kv_indptr[kb + 1] - p.kv_indptr[kb];
+  const int L = n ? (n - 1) * p.page_size + p.kv_last[kb] : 0;
+  wrow0 = (int64_t)item * p.max_chunks * WR + r;
+  return num_chunks(L, p.chunk_tokens, p.max_chunks);
+}
+
+// Running merge state of one lane: LSE maximum M, weight sum, the lane's four
+// output dims, and the row maximum MX.
+struct Fold {
+  float M = -INFINITY, MX = -INFINITY, wsum = 0.f;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+};
+
+// Folds states [c0, c1) of a row: the LSE, max and O of a block of 8 partial
+// states are loaded together and folded into the running state, which is
+// rescaled when M grows, so a block costs a single memory round trip.
+__device__ __forceinline__ void fold_states(const AttnParams& p, int64_t wrow0, int c0, int c1,
+                                            int d0, Fold& f) {
+  const int WR = p.ws_rows;
+  const int D = p.dvo;
+  constexpr int BLK = 8;
+  for (int cb = c0; cb < c1; cb += BLK) {
+    float ls[BLK], ms[BLK];
+    float4 x[BLK];
+#pragma unroll
+    for (int k = 0; k < BLK; ++k) {
+      const bool ok = cb + k < c1;
+      const int64_t wr = wrow0 + (int64_t)(cb + k) * WR;
+      ls[k] = ok ? p.ws_lse[wr] : -INFINITY;
+      ms[k] = ok ? p.ws_mx[wr] : -INFINITY;
+      x[k] = ok ? *reinterpret_cast<const float4*>(p.ws_o + wr * D + d0) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < BLK; ++k) {
+      bm = fmaxf(bm, ls[k]);
+      f.MX = fmaxf(f.MX, ms[k]);
+    }
+    const float Mn = fmaxf(f.M, bm);
+    if (Mn == -INFINITY) continue;  // every state so far is empty
+    const float a = f.M == -INFINITY ? 0.f : fast_exp2((f.M - Mn) * kLog2e);
+    f.wsum *= a;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.acc[i] *= a;
+#pragma unroll
+    for (int k = 0; k < BLK; ++k) {
+      const float w = ls[k] == -INFINITY ? 0.f : fast_exp2((ls[k] - Mn) * kLog2e);
+      f.wsum += w;
+      f.acc[0] = fmaf(w, x[k].x, f.acc[0]);
+      f.acc[1] = fmaf(w, x[k].y, f.acc[1]);
+      f.acc[2] = fmaf(w, x[k].z, f.acc[2]);
+      f.acc[3] = fmaf(w, x[k].w, f.acc[3]);
+    }
+    f.M = Mn;
+  }
+}
+
+// Normalises a row's merged state and writes O (four dims per lane), LSE and max.
+__device__ __forceinline__ void store_row(const AttnParams& p, int b, int g, int r, int d0, int li,
+                                          Fold& f) {
+  if (f.M != -INFINITY) {
+    const float inv = 1.f / f.wsum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.acc[i] *= inv;
+  }
+  const int D = p.dvo;
+  const int qi = r / p.group, qh = r % p.group;
+  const int64_t rid = (int64_t)(b * p.q_len + qi) * p.num_qo_heads + (int64_t)g * p.group + qh;
+  if (p.o_dtype == F32) store4<F32>(p.o, rid * D + d0, f.acc);
+  else if (p.o_dtype == F16) store4<F16>(p.o, rid * D + d0, f.acc);
+  else store4<BF16>(p.o, rid * D + d0, f.acc);
+  if (li == 0) {
+    if (p.lse) p.lse[rid] = f.M == -INFINITY ? -INFINITY : f.M + fast_log2(f.wsum) * kLn2;
+    if (p.mx) p.mx[rid] = f.MX;
+  }
+}
+
 // Merge of internal KV chunks or balanced-split segments (the same LSE formula):
 // one group of D/4 lanes per folded row (b, KV head g, row r < q_len*G); rows
 // whose item was done in one piece were written directly by the attention kernel
@@ -132,86 +223,73 @@ __global__ __launch_bounds__(256) void chunk_merge_kernel(AttnParams p, int tpr)
   const int g = (int)((rho / WR) % p.num_kv_heads);
   const int b = (int)(rho / ((int64_t)WR * p.num_kv_heads));
   if (r >= R) return;
-  const int item = b * p.num_kv_heads + g;
-  int nch;
   int64_t wrow0;
-  if (p.bal_blocks > 0) {
-    // balanced split: the item's partial states sit in slots item + i for its
-    // workgroups i = first..last
-    const int i0 = p.ws_seg[2 * item], i1 = p.ws_seg[2 * item + 1];
-    nch = i1 - i0 + 1;
-    wrow0 = ((int64_t)item + i0) * WR + r;
-  } else {
-    const int kb = p.broadcast ? 0 : b;
-    const int n = p.kv_indptr[kb + 1] - p.kv_indptr[kb];
-    const int L = n ? (n - 1) * p.page_size + p.kv_last[kb] : 0;
-    nch = num_chunks(L, p.chunk_tokens, p.max_chunks);
-    wrow0 = (int64_t)item * p.max_chunks * WR + r;
-  }
+  const int nch = row_states(p, b, g, r, wrow0);
   if (nch <= 1) return;
-  const int D = p.dvo;
   const int d0 = li * 4;
-  // one pass: the LSE, max and O of a block of 8 partial states are loaded
-  // together and folded into a running (M, weight sum, acc) that is rescaled
-  // when M grows, so the loads of a row need a single round trip
-  constexpr int BLK = 8;
-  float M = -INFINITY, MX = -INFINITY;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  for (int c0 = 0; c0 < nch; c0 += BLK) {
-    float ls[BLK], ms[BLK];
-    float4 x[BLK];
-#pragma unroll
-    for (int k = 0; k < BLK; ++k) {
-      const bool ok = c0 + k < nch;
-      const int64_t wr = wrow0 + (int64_t)(c0 + k) * WR;
-      ls[k] = ok ? p.ws_lse[wr] : -INFINITY;
-      ms[k] = ok ? p.ws_mx[wr] : -INFINITY;
-      x[k] = ok ? *reinterpret_cast<const float4*>(p.ws_o + wr * D + d0) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    float bm = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < BLK; ++k) {
-      bm = fmaxf(bm, ls[k]);
-      MX = fmaxf(MX, ms[k]);
-    }
-    const float Mn = fmaxf(M, bm);
-    if (Mn == -INFINITY) continue;  // every state so far is empty
-    const float a = M == -INFINITY ? 0.f : fast_exp2((M - Mn) * kLog2e);
-    wsum *= a;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] *= a;
-#pragma unroll
-    for (int k = 0; k < BLK; ++k) {
-      const float w = ls[k] == -INFINITY ? 0.f : fast_exp2((ls[k] - Mn) * kLog2e);
-      wsum += w;
-      acc[0] = fmaf(w, x[k].x, acc[0]);
-      acc[1] = fmaf(w, x[k].y, acc[1]);
-      acc[2] = fmaf(w, x[k].z, acc[2]);
-      acc[3] = fmaf(w, x[k].w, acc[3]);
-    }
-    M = Mn;
+  Fold f;
+  fold_states(p, wrow0, 0, nch, d0, f);
+  store_row(p, b, g, r, d0, li, f);
+}
+
+// The same merge for rows with many states (few long items split over many
+// workgroups): one workgroup per folded row, its NG = 256 / (D/4) lane groups
+// each folding an equal contiguous share of the states, then lane group 0
+// combining the NG shares in group order through LDS (a fixed order, so the
+// result does not depend on timing).
+__global__ __launch_bounds__(256) void chunk_merge_wide_kernel(AttnParams p, int tpr) {
+  __shared__ float4 s_acc[256];
+  __shared__ float s_m[256], s_w[256], s_x[256];
+  const int NG = blockDim.x / tpr;
+  const int R = p.q_len * p.group;
+  const int64_t rho = blockIdx.x;  // (b, g, r < R)
+  const int r = (int)(rho % R);
+  const int g = (int)((rho / R) % p.num_kv_heads);
+  const int b = (int)(rho / ((int64_t)R * p.num_kv_heads));
+  const int k = threadIdx.x / tpr, li = threadIdx.x % tpr;
+  int64_t wrow0;
+  const int nch = row_states(p, b, g, r, wrow0);
+  if (nch <= 1) return;  // uniform over the workgroup
+  const int d0 = li * 4;
+  const int per = (nch + NG - 1) / NG;
+  Fold f;
+  if (k < NG) fold_states(p, wrow0, min(nch, k * per), min(nch, (k + 1) * per), d0, f);
+  s_acc[threadIdx.x] = make_float4(f.acc[0], f.acc[1], f.acc[2], f.acc[3]);
+  if (li == 0 && k < NG) {
+    s_m[k] = f.M;
+    s_w[k] = f.wsum;
+    s_x[k] = f.MX;
   }
-  if (M != -INFINITY) {
-    const float inv = 1.f / wsum;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] *= inv;
+  __syncthreads();
+  if (k != 0) return;
+  Fold t;
+  for (int j = 0; j < NG; ++j) t.M = fmaxf(t.M, s_m[j]);
+  if (t.M != -INFINITY) {
+    for (int j = 0; j < NG; ++j) {
+      const float mj = s_m[j];
+      const float a = mj == -INFINITY ? 0.f : fast_exp2((mj - t.M) * kLog2e);
+      const float4 v = s_acc[j * tpr + li];
+      t.wsum = fmaf(a, s_w[j], t.wsum);
+      t.acc[0] = fmaf(a, v.x, t.acc[0]);
+      t.acc[1] = fmaf(a, v.y, t.acc[1]);
+      t.acc[2] = fmaf(a, v.z, t.acc[2]);
+      t.acc[3] = fmaf(a, v.w, t.acc[3]);
+    }
   }
-  const int qi = r / p.group, qh = r % p.group;
-  const int64_t rid = (int64_t)(b * p.q_len + qi) * p.num_qo_heads + (int64_t)g * p.group + qh;
-  if (p.o_dtype == F32) store4<F32>(p.o, rid * D + d0, acc);
-  else if (p.o_dtype == F16) store4<F16>(p.o, rid * D + d0, acc);
-  else store4<BF16>(p.o, rid * D + d0, acc);
-  if (li == 0) {
-    if (p.lse) p.lse[rid] = M == -INFINITY ? -INFINITY : M + fast_log2(wsum) * kLn2;
-    if (p.mx) p.mx[rid] = MX;
-  }
+  for (int j = 0; j < NG; ++j) t.MX = fmaxf(t.MX, s_x[j]);
+  store_row(p, b, g, r, d0, li, t);
 }
 
 }  // namespace
 
-hipError_t launch_chunk_merge(const AttnParams& p, hipStream_t stream) {
+hipError_t launch_chunk_merge(const AttnParams& p, bool wide, hipStream_t stream) {
   const int tpr = p.dvo / 4;
+  if (wide) {
+    const int64_t rows = (int64_t)p.batch * p.num_kv_heads * p.q_len * p.group;
+    if (rows == 0) return hipSuccess;
+    chunk_merge_wide_kernel<<<(unsigned)rows, 256 / tpr * tpr, 0, stream>>>(p, tpr);
+    return hipGetLastError();
+  }
   const int rpb = 256 / tpr;
   const int64_t total = (int64_t)p.batch * p.num_kv_heads * p.ws_rows;
   const dim3 grid((unsigned)((total + rpb - 1) / rpb));

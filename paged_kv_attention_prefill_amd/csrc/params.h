@@ -77,7 +77,8 @@ int mla_blocks_per_cu(const AttnParams& p);
 hipError_t launch_mla_decode(const AttnParams& p, hipStream_t stream);
 bool flash_attn_supported(const AttnParams& p);
 hipError_t launch_flash_attn(const AttnParams& p, bool same_strides, hipStream_t stream);
-hipError_t launch_chunk_merge(const AttnParams& p, hipStream_t stream);
+// Merge of internal splits; `wide`: one workgroup per row (rows with many states).
+hipError_t launch_chunk_merge(const AttnParams& p, bool wide, hipStream_t stream);
 hipError_t launch_merge(const void* v, int v_dtype, const float* s, int num_states, int64_t rows,
                         int head_dim, int64_t v_state_stride, int64_t s_state_stride, void* out,
                         int out_dtype, float* s_out, hipStream_t stream);

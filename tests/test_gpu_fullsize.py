@@ -55,3 +55,11 @@ def test_c4_mla_decode_full(h, ql, dt):
 def test_sparse_mla_decode_full(dt):
     """128 queries x top-2048 selected latent rows from a 4x larger poisoned pool."""
     run_sampled(W.config_sparse(num_heads=16, kv_dtype=dt), f"sparse full h16 {W.DT_NAMES[dt]}", n=96)
+
+
+def test_long_single_request_decode_full():
+    """Batch 1, 131072 fp16 KV tokens, 32/8 heads, page 128: the balanced split
+    spreads one request's KV over every co-resident workgroup."""
+    w = W.config2(batch=1, min_len=131072, max_len=131072, dtype=W.DT_F16, page_size=128,
+                  num_qo_heads=32, num_kv_heads=8)
+    run_sampled(w, "long decode b1", n=32)

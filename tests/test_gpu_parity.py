@@ -381,3 +381,24 @@ def test_sparse_selection_routed_halves_merge_on_gpu(name):
                             out_dtype=parts[0]["o"].dtype)
     torch.cuda.synchronize()
     check_rows(w, to64(mo), to64(ml), o, lse, label=f"routed halves {name}")
+
+
+@pytest.mark.parametrize("name", ["gqa_b1", "gqa_b2_d64_f16", "mla_b1_bf16", "mla_b1_fp8_q2"])
+def test_few_long_requests_wide_merge(name):
+    """Few long requests: the balanced split gives each row dozens of partial
+    states, merged by a workgroup per row (lane groups over fixed shares of the
+    states, combined in a fixed order): oracle parity and bitwise repeats."""
+    w = {
+        "gqa_b1": lambda: W.config2(batch=1, min_len=60000, max_len=60000),
+        "gqa_b2_d64_f16": lambda: W.build(np.random.default_rng(41), 41, "few_long_d64",
+                                          q_lens=[1, 1], kv_lens=[50000, 1], num_qo_heads=16,
+                                          num_kv_heads=4, head_dim_qk=64, head_dim_vo=64,
+                                          page_size=32, q_dtype=W.DT_F16, kv_dtype=W.DT_F16),
+        "mla_b1_bf16": lambda: W.config4(num_heads=16, q_len=1, batch=1, min_len=30000, max_len=30000),
+        "mla_b1_fp8_q2": lambda: W.config4(num_heads=16, q_len=2, kv_dtype=W.DT_FP8, batch=1,
+                                           min_len=25000, max_len=25000),
+    }[name]()
+    _, res = run_and_check(w, f"wide merge {name}")
+    again = R.run(R.upload(w))
+    torch.cuda.synchronize()
+    assert torch.equal(again["o"], res["o"]) and torch.equal(again["lse"], res["lse"])

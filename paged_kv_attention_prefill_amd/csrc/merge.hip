@@ -208,21 +208,19 @@ __device__ __forceinline__ void store_row(const AttnParams& p, int b, int g, int
 }
 
 // Merge of internal KV chunks or balanced-split segments (the same LSE formula):
-// one group of D/4 lanes per folded row (b, KV head g, row r < q_len*G); rows
-// whose item was done in one piece were written directly by the attention kernel
-// and are skipped here.
+// one group of D/4 lanes per folded row (b, KV head g, row r < q_len*G; the
+// workspace's padding row slots get no lanes); rows whose item was done in one
+// piece were written directly by the attention kernel and are skipped here.
 __global__ __launch_bounds__(256) void chunk_merge_kernel(AttnParams p, int tpr) {
   const int rpb = blockDim.x / tpr;
   const int64_t rho = (int64_t)blockIdx.x * rpb + threadIdx.x / tpr;
   const int li = threadIdx.x % tpr;
   const int R = p.q_len * p.group;
-  const int WR = p.ws_rows;
-  const int64_t total = (int64_t)p.batch * p.num_kv_heads * WR;
+  const int64_t total = (int64_t)p.batch * p.num_kv_heads * R;
   if (threadIdx.x >= rpb * tpr || rho >= total) return;
-  const int r = (int)(rho % WR);
-  const int g = (int)((rho / WR) % p.num_kv_heads);
-  const int b = (int)(rho / ((int64_t)WR * p.num_kv_heads));
-  if (r >= R) return;
+  const int r = (int)(rho % R);
+  const int g = (int)((rho / R) % p.num_kv_heads);
+  const int b = (int)(rho / ((int64_t)R * p.num_kv_heads));
   int64_t wrow0;
   const int nch = row_states(p, b, g, r, wrow0);
   if (nch <= 1) return;
@@ -291,7 +289,8 @@ hipError_t launch_chunk_merge(const AttnParams& p, bool wide, hipStream_t stream
     return hipGetLastError();
   }
   const int rpb = 256 / tpr;
-  const int64_t total = (int64_t)p.batch * p.num_kv_heads * p.ws_rows;
+  const int64_t total = (int64_t)p.batch * p.num_kv_heads * p.q_len * p.group;
+  if (total == 0) return hipSuccess;
   const dim3 grid((unsigned)((total + rpb - 1) / rpb));
   chunk_merge_kernel<<<grid, dim3(rpb * tpr), 0, stream>>>(p, tpr);
   return hipGetLastError();

@@ -864,9 +864,14 @@ __device__ __forceinline__ WidePiece convert_piece(i32x4_t x, int q, uint32_t ds
 
 // Widening of a whole tile by the workgroup's threads (three rounds at most: two
 // pieces, then a third for the first threads).
-__device__ __forceinline__ void convert_tile(const uint8_t* src, uint8_t* dst, int tid) {
+__device__ __forceinline__ void convert_tile(const uint8_t* src, uint8_t* dst, int tid_in) {
   constexpr int n = 64 * kNW2;
   static_assert(kTK2 * kPieces8 > 2 * n && kTK2 * kPieces8 <= 3 * n, "three rounds");
+  // the per-thread addresses are recomputed per call (cheap) rather than hoisted
+  // out of the tile loop, where they were spilled and reloaded behind a wait
+  // that also drained the tiles in flight
+  int tid = tid_in;
+  asm volatile("" : "+v"(tid));
   const uint32_t a = lds_off(src) + 16 * tid;
   const uint32_t d = lds_off(dst);
   i32x4_t x0, x1;

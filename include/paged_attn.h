@@ -27,6 +27,10 @@
  *       k + page*k_stride[0] + slot*k_stride[1] + g*k_stride[2] + d
  *     (likewise V with v_stride).  kv_len = (n-1)*page_size + last_page_len
  *     for n >= 1 pages, 0 for n == 0.
+ *   - A sparse selection of token rows per query (the "Move the Query, Not the
+ *     Cache" summary, problem statement: KV picked by a sparse indexer) is a
+ *     KV batch per query with page_size 1: kv_indices then lists the selected
+ *     token slots, last_page_len is 1, and no causal mask is needed.
  *   - Query head h reads KV head h / (num_qo_heads / num_kv_heads).
  *   - causal: query i of a batch with q_b queries sits at position
  *     kv_len - q_b + i and sees KV tokens j <= that position.

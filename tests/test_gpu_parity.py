@@ -383,17 +383,23 @@ def test_sparse_selection_routed_halves_merge_on_gpu(name):
     check_rows(w, to64(mo), to64(ml), o, lse, label=f"routed halves {name}")
 
 
-@pytest.mark.parametrize("name", ["gqa_b1", "gqa_b2_d64_f16", "mla_b1_bf16", "mla_b1_fp8_q2"])
+@pytest.mark.parametrize("name", ["gqa_b1", "gqa_b2_d64_f16", "gqa_b1_d256", "mla_b1_bf16",
+                                  "mla_b1_fp8_q2"])
 def test_few_long_requests_wide_merge(name):
     """Few long requests: the balanced split gives each row dozens of partial
     states, merged by a workgroup per row (lane groups over fixed shares of the
-    states, combined in a fixed order): oracle parity and bitwise repeats."""
+    states, combined in a fixed order; 16, 8, 4 and 2 lane groups for head dims
+    64, 128, 256 and 512): oracle parity and bitwise repeats."""
     w = {
         "gqa_b1": lambda: W.config2(batch=1, min_len=60000, max_len=60000),
         "gqa_b2_d64_f16": lambda: W.build(np.random.default_rng(41), 41, "few_long_d64",
                                           q_lens=[1, 1], kv_lens=[50000, 1], num_qo_heads=16,
                                           num_kv_heads=4, head_dim_qk=64, head_dim_vo=64,
                                           page_size=32, q_dtype=W.DT_F16, kv_dtype=W.DT_F16),
+        "gqa_b1_d256": lambda: W.build(np.random.default_rng(42), 42, "few_long_d256", q_lens=[1],
+                                       kv_lens=[40000], num_qo_heads=16, num_kv_heads=4,
+                                       head_dim_qk=256, head_dim_vo=256, page_size=16,
+                                       q_dtype=W.DT_BF16, kv_dtype=W.DT_BF16),
         "mla_b1_bf16": lambda: W.config4(num_heads=16, q_len=1, batch=1, min_len=30000, max_len=30000),
         "mla_b1_fp8_q2": lambda: W.config4(num_heads=16, q_len=2, kv_dtype=W.DT_FP8, batch=1,
                                            min_len=25000, max_len=25000),

@@ -95,10 +95,21 @@ def algorithmic_counts(w, num_states: int = 1):
     return attn, merge, flops
 
 
-def cpu_baseline(w, target_s: float = 15.0):
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(w, target_s: float = 15.0, threads: int = 0):
     """Time the oracle on a bounded sample of query batches (whole batches, all heads),
-    scaled to the whole workload by the sample's share of (row x allowed token) work."""
-    import dataclasses
+    scaled to the whole workload by the sample's share of (row x allowed token) work.
+    threads = 0: every host core (OpenMP default); otherwise that many threads."""
     from oracle import oracle as OR
     work = allowed_tokens(w) * w.num_qo_heads
     per_batch = np.array([work[w.qo_indptr[b]:w.qo_indptr[b + 1]].sum() for b in range(w.batch)],
@@ -109,7 +120,7 @@ def cpu_baseline(w, target_s: float = 15.0):
                                   w.qo_indptr[b + 1] * w.num_qo_heads, dtype=np.int64)
     t0 = time.perf_counter()
     b_small = int(order[-1])
-    OR.attention(w, rows=rows_of(b_small), num_kv_splits=1)
+    OR.attention(w, rows=rows_of(b_small), num_kv_splits=1, num_threads=threads)
     t_small = time.perf_counter() - t0
     rate = per_batch[b_small] / max(t_small, 1e-6)
     budget = rate * target_s
@@ -124,13 +135,13 @@ def cpu_baseline(w, target_s: float = 15.0):
     reps, elapsed = 0, 0.0
     while reps == 0 or (elapsed < min(10.0, target_s) and reps < 20):
         t0 = time.perf_counter()
-        OR.attention(w, rows=rows, num_kv_splits=1)
+        OR.attention(w, rows=rows, num_kv_splits=1, num_threads=threads)
         elapsed += time.perf_counter() - t0
         reps += 1
     frac = acc / per_batch.sum()
     return elapsed / reps / frac, dict(batches=len(chosen), rows=int(rows.size),
                                        seconds=elapsed, reps=reps, fraction=frac,
-                                       threads=OR.num_threads())
+                                       threads=threads if threads > 0 else OR.num_threads())
 
 
 COPY_BYTES = 1 << 30  # calibration copy: reads and writes this many bytes per launch
@@ -161,6 +172,76 @@ def recorded_traffic(workload: str, kernel: str):
     return int(rec["traffic_bytes"])
 
 
+FLUSH_BYTES = 1 << 30  # read before every cold iteration: 4x the 256 MB MALL
+
+
+def pct(xs):
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2)}
+
+
+def step_distribution(call, stream, iters: int):
+    """Per-step µs over `iters` iterations, warm (back to back) and cold (an untimed
+    read of a 1 GiB scratch buffer before every step, so KV, tables and Q come
+    from HBM; a read rather than a write, so that no dirty lines of the flush are
+    written back during the timed step).  Each step is bracketed by its own
+    event pair on the stream it runs on."""
+    import torch
+    scratch = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda:0")
+    out = {}
+    for mode in ("warm", "cold"):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(iters)]
+        torch.cuda.synchronize()
+        for i, (e0, e1) in enumerate(evs):
+            if mode == "cold":
+                scratch.sum()
+            e0.record(stream)
+            call()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        out[mode + "_us"] = pct([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+    del scratch
+    out["iters"] = iters
+    out["flush_bytes"] = FLUSH_BYTES
+    return out
+
+
+def side_workload(name: str, steps: int, warmup: int, iters: int):
+    """Timing of a second workload in the same run (same protocol as the main one):
+    step µs, the attention kernel's µs, and its rate against its binding roof."""
+    import torch
+    from paged_kv_attention_prefill_amd import runner as R
+    w = make_workload(name)
+    d = R.upload(w, "cuda:0")
+    stream = torch.cuda.current_stream()
+    call = R.prepare(d)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        call()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    attn_ms = call.time_attention_kernel(steps)
+    attn_bytes, merge_bytes, flops = algorithmic_counts(w, call.num_states)
+    rec = {"workload": w.name, "kernel": call.attention_kernel_name,
+           "us_per_step": round(ms * 1e3, 2), "kernel_us": round(attn_ms * 1e3, 2),
+           "tflops": round(flops / (attn_ms * 1e-3) / 1e12, 2),
+           "mfma_frac": round(flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "hbm_gbs": round(attn_bytes / (attn_ms * 1e-3) / 1e9, 1),
+           "hbm_frac": round(attn_bytes / (attn_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+           "flops_per_launch": flops, "bytes_per_launch": attn_bytes}
+    rec["timing"] = step_distribution(call, stream, iters)
+    del call, d
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +250,10 @@ def main(argv=None):
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--iters", type=int, default=100,
+                    help="iterations of the cold/warm per-step distribution")
+    ap.add_argument("--no-side", action="store_true",
+                    help="skip the prefill (c3) and tiny-decode (c1) side measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the HBM-counter calibration copy kernel")
     a = ap.parse_args(argv)
@@ -252,16 +337,29 @@ def main(argv=None):
         "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": roof,
     }
+    line["timing"] = step_distribution(call, stream, a.iters)
+    if not a.no_side and a.workload == "c2":
+        # the prefill half of the metric (causal GPT-OSS-like prefill) and the
+        # launch-latency-bound tiny decode, in the same run
+        line["prefill_c3"] = side_workload("c3", max(5, a.steps // 2), a.warmup, a.iters)
+        line["tiny_c1"] = side_workload("c1", a.steps, a.warmup, a.iters)
     if not a.no_cpu_baseline:
         full_s, info = cpu_baseline(w, a.cpu_seconds)
-        cpu_val = (step_bytes / full_s / 1e9) if decode_like else (flops / full_s / 1e12)
-        line["cpu_baseline"] = {"value": round(cpu_val, 6), "unit": unit,
+        one_s, info1 = cpu_baseline(w, a.cpu_seconds * 2 / 3, threads=1)
+        rate = lambda s: (step_bytes / s / 1e9) if decode_like else (flops / s / 1e12)
+        line["cpu_baseline"] = {"value": round(rate(full_s), 6), "unit": unit,
                                 "cores": info["threads"], "kind": "oracle",
                                 "sample": (f"{info['batches']} whole query batches "
                                            f"({info['rows']} rows, {info['fraction']:.3f} of the "
                                            f"work), {info['reps']} run(s) in "
                                            f"{info['seconds']:.1f} s, scaled to the full workload"),
-                                "seconds_full_workload": round(full_s, 2)}
+                                "seconds_full_workload": round(full_s, 2),
+                                "one_thread": {"value": round(rate(one_s), 6),
+                                               "seconds_full_workload": round(one_s, 2),
+                                               "sample": (f"{info1['batches']} whole query "
+                                                          f"batches, {info1['fraction']:.3f} of "
+                                                          f"the work, {info1['reps']} run(s)")},
+                                "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count()}
     print(json.dumps(line), flush=True)
     return 0
 

@@ -182,8 +182,8 @@ class PreparedCall:
         self.stream = _stream_handle(stream)
         self._ref = ctypes.byref(args)
         self._ws = _ptr(workspace) if ws_bytes else None
-        plan = "paged_attn_decode_plan_name" if fn_name == "paged_attn_decode" \
-            else "paged_attn_prefill_plan_name"
+        plan = "paged_attn_prefill_plan_name" if fn_name == "paged_attn_prefill" \
+            else "paged_attn_decode_plan_name"
         name = getattr(self.lib, plan)(self._ref)
         self.plan_name = name.decode() if name else None
 
@@ -197,9 +197,9 @@ def _workspace(lib, size_fn, args, device, workspace):
     _check(size_fn, getattr(lib, size_fn)(ctypes.byref(args), ctypes.byref(ws_bytes)))
     n = ws_bytes.value
     if n > 0 and (workspace is None or workspace.numel() < n):
-        # zero-filled: kernels that count arrivals in the workspace expect zeros
-        # on first use and leave them zero when they finish
-        workspace = torch.zeros(n, dtype=torch.uint8, device=device)
+        # every workspace byte a kernel reads was written earlier in the same
+        # call, so the buffer needs no initial contents
+        workspace = torch.empty(n, dtype=torch.uint8, device=device)
     return workspace, n
 
 
@@ -246,9 +246,9 @@ def prepare_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[tor
     a.lse = _ptr(lse)
     a.row_max = _ptr(mx)
     a.flags = flags
-    workspace, n = _workspace(lib, "paged_attn_decode_workspace_size", a, q.device, workspace)
     keep = dict(o=out, lse=lse, mx=mx, _q=q, _k=k_cache, _v=v_cache, _ip=kv_indptr,
                 _ix=kv_indices, _lp=kv_last_page_len)
+    workspace, n = _workspace(lib, "paged_attn_decode_workspace_size", a, q.device, workspace)
     return PreparedCall("paged_attn_decode", a, keep, workspace, n, stream)
 
 

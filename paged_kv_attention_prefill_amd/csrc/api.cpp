@@ -4,6 +4,7 @@
 // section), workspace planning, launch on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -94,11 +95,17 @@ void fill_kv(AttnParams& p, const pa_paged_kv& kv) {
   p.max_kv_len = kv.max_kv_len_hint;
 }
 
+// The kernels scale scores by sm_scale * k_scale * log2(e) in fp32; that
+// product must be finite (a scale that overflows it has no fp32 result).
+bool finite_score_scale(float sm_scale, float k_scale) {
+  return std::isfinite(sm_scale) && std::isfinite(sm_scale * k_scale * 1.4426950408889634f);
+}
+
 int check_decode(const pa_decode_args* a) {
   if (!a) return PA_ERR_NULL;
   if (a->batch < 1 || a->q_len < 1) return PA_ERR_SHAPE;
   if (a->num_kv_splits < 1 || a->num_kv_splits > 1024) return PA_ERR_SHAPE;
-  if (!std::isfinite(a->sm_scale)) return PA_ERR_SHAPE;
+  if (!finite_score_scale(a->sm_scale, a->kv.k_scale)) return PA_ERR_SHAPE;
   int st = check_common(a->q, a->q_dtype, a->num_qo_heads, a->kv, a->kv_broadcast, a->batch, a->o,
                         a->o_dtype);
   if (st != PA_OK) return st;
@@ -114,7 +121,7 @@ int check_prefill(const pa_prefill_args* a) {
   if (!a) return PA_ERR_NULL;
   if (!a->qo_indptr) return PA_ERR_NULL;
   if (a->batch < 1 || a->total_q < 0 || a->max_q_len_hint < 0) return PA_ERR_SHAPE;
-  if (!std::isfinite(a->sm_scale)) return PA_ERR_SHAPE;
+  if (!finite_score_scale(a->sm_scale, a->kv.k_scale)) return PA_ERR_SHAPE;
   return check_common(a->q, a->q_dtype, a->num_qo_heads, a->kv, a->kv_broadcast, a->batch, a->o,
                       a->o_dtype);
 }
@@ -208,23 +215,45 @@ int decode_chunk_tokens(const AttnParams& p, uint32_t flags) {
   return c;
 }
 
-// Compute units of the current device (MI355X: 256), cached per device.
-int device_cus() {
-  static int cache[64] = {};
+// Per-device values read once with HIP device queries (compute-unit count,
+// kernel occupancies).  Slots are atomics: concurrent first calls may both run
+// the query, and both store the same value.
+constexpr int kMaxDevices = 64;
+
+int current_device() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
     (void)hipGetLastError();
-    return 256;
+    return -1;
   }
-  if (cache[dev] <= 0) {
+  return dev;
+}
+
+// Cached per-device value: slot[dev] once `query()` has been called there.
+template <typename Query>
+int per_device(std::atomic<int>* slot, int fallback, Query query) {
+  const int dev = current_device();
+  if (dev < 0) return fallback;
+  int v = slot[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    v = query(dev);
+    if (v <= 0) v = fallback;
+    slot[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// Compute units of the current device (MI355X: 256).
+int device_cus() {
+  static std::atomic<int> cache[kMaxDevices];
+  return per_device(cache, 256, [](int dev) {
     int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
       (void)hipGetLastError();
-      n = 256;
+      n = 0;
     }
-    cache[dev] = n;
-  }
-  return cache[dev];
+    return n;
+  });
 }
 
 // Workspace of a balanced split: partial states in slots item + workgroup, then
@@ -250,6 +279,21 @@ int mla_chunk_tokens(const AttnParams& p, uint32_t flags) {
   return c;
 }
 
+// Workgroups per CU of the balanced GQA decode kernel variant, per device.
+int gqa_occupancy(const AttnParams& p, bool same) {
+  static std::atomic<int> occ[2][3][2][kMaxDevices];
+  return per_device(occ[p.q_dtype == PA_BF16][p.dqk == 64 ? 0 : p.dqk == 128 ? 1 : 2][same], 1,
+                    [&](int) { return pa::gqa_decode_blocks_per_cu(p, same); });
+}
+
+// Workgroups per CU of the MLA decode kernel for this row count, per device.
+int mla_occupancy(const AttnParams& p) {
+  static std::atomic<int> occ[2][4][kMaxDevices];
+  const int R = p.q_len * p.group;
+  return per_device(occ[p.kv_dtype == PA_FP8_E4M3][R <= 16 ? 0 : R <= 32 ? 1 : R <= 64 ? 2 : 3], 1,
+                    [&](int) { return pa::mla_blocks_per_cu(p); });
+}
+
 Plan make_plan(const AttnParams& p, uint32_t flags) {
   Plan pl;
   const bool same = equal_kv_strides(p) && !(flags & PA_FLAG_FORCE_GENERAL_STRIDES);
@@ -265,27 +309,25 @@ Plan make_plan(const AttnParams& p, uint32_t flags) {
     // co-resident workgroups (every workgroup streams the same number of
     // 32-token tiles, so none idles at the end)
     if (decode_chunk_tokens(p, flags) > 0) {
-      static int occ[2][3][2] = {};
-      int& o = occ[p.q_dtype == PA_BF16][p.dqk == 64 ? 0 : p.dqk == 128 ? 1 : 2][same];
-      if (o <= 0) o = pa::gqa_decode_blocks_per_cu(p, same);
       pl.bal_unit = 32;
-      pl.bal_blocks = o * device_cus();
+      pl.bal_blocks = gqa_occupancy(p, same) * device_cus();
       pl.workspace = balanced_workspace(p, pl.bal_blocks, 16);
     }
     return pl;
   }
-  if (pa::mla_decode_supported(p)) {
+  // The flash and MLA kernels take the running max of raw scores and apply the
+  // score scale afterwards, which orders scores correctly only for a positive
+  // scale; a zero or negative scale goes to the generic kernel (it scales
+  // every score first).
+  const bool positive_scale = p.sm_scale * p.k_scale * 1.4426950408889634f > 0.f;
+  if (positive_scale && pa::mla_decode_supported(p)) {
     pl.kind = Plan::MLA_DECODE;
     pl.name = p.kv_dtype == PA_FP8_E4M3 ? "mla_decode_mfma_fp8" : "mla_decode_mfma";
     const int ct = mla_chunk_tokens(p, flags);
     if (ct > 0 && pa::mla_balanced_ok(p)) {
       // one row tile per request: balanced split over one wave of workgroups
-      static int occ[2][4] = {};
-      const int R = p.q_len * p.group;
-      int& o = occ[p.kv_dtype == PA_FP8_E4M3][R <= 16 ? 0 : R <= 32 ? 1 : R <= 64 ? 2 : 3];
-      if (o <= 0) o = pa::mla_blocks_per_cu(p);
       pl.bal_unit = 32;
-      pl.bal_blocks = o * device_cus();
+      pl.bal_blocks = mla_occupancy(p) * device_cus();
       pl.ws_rows = p.q_len * p.group;
       pl.workspace = balanced_workspace(p, pl.bal_blocks, pl.ws_rows);
       return pl;
@@ -299,7 +341,7 @@ Plan make_plan(const AttnParams& p, uint32_t flags) {
     }
     return pl;
   }
-  if (pa::flash_attn_supported(p)) {
+  if (positive_scale && pa::flash_attn_supported(p)) {
     pl.kind = Plan::FLASH;
     pl.same_strides = same;
     pl.name = same ? "flash_attn_mfma_same_strides" : "flash_attn_mfma";

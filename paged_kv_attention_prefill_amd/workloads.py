@@ -147,9 +147,17 @@ def build(rng: np.random.Generator, seed: int, name: str, *, q_lens: Sequence[in
           shared_kv: bool = False, kv_broadcast: bool = False, causal: bool = False,
           sm_scale: Optional[float] = None, num_kv_splits: int = 1,
           pool_pages: Optional[int] = None, poison: bool = True, k_layout: str = "NHD",
-          v_layout: str = "NHD", uniform_q_len: bool = True) -> Workload:
+          v_layout: str = "NHD", uniform_q_len: bool = True,
+          k_late_gain: Optional[tuple] = None) -> Workload:
     """Lay out one paged workload.  ``rng`` has already drawn the lengths; this
-    draws, in order, the page permutation, Q, K and V."""
+    draws, in order, the page permutation, Q, K and V.
+
+    ``k_late_gain = (gain, d0, d1)`` multiplies dims [d0, d1) of the K rows of
+    the second half of every KV batch (tokens j >= ceil(L/2)) by ``gain`` before
+    any fp8 scale is taken, so the scores of those tokens spread ``gain`` times
+    wider: a row's running maximum then jumps far above its first tiles' maximum
+    part-way through the KV (for a shared latent cache, dims past head_dim_vo
+    leave V untouched)."""
     q_lens = np.asarray(q_lens, dtype=np.int64)
     kv_lens = np.asarray(kv_lens, dtype=np.int64)
     P = page_size
@@ -173,6 +181,14 @@ def build(rng: np.random.Generator, seed: int, name: str, *, q_lens: Sequence[in
     v32 = None
     if not shared_kv:
         v32 = rng.standard_normal((pool, P, num_kv_heads, head_dim_vo), dtype=np.float32)
+
+    if k_late_gain is not None:
+        gain, d0, d1 = k_late_gain
+        for b in range(len(kv_lens)):
+            L = int(kv_lens[b])
+            js = np.arange((L + 1) // 2, L)
+            pages = kv_indices[kv_indptr[b] + js // P]
+            k32[pages, js % P, :, d0:d1] *= np.float32(gain)
 
     k_scale = v_scale = 1.0
     if kv_dtype == DT_FP8:

@@ -194,3 +194,63 @@ def test_workloads_pass_table_check(lib):
         assert lib.paged_attn_check_tables(w.kv_indptr.ctypes.data, w.kv_indices.ctypes.data,
                                            w.kv_last_page_len.ctypes.data, w.num_kv_batches,
                                            w.num_pool_pages, w.page_size) == 0
+
+
+@pytest.mark.parametrize("which", ["decode", "prefill"])
+def test_overflowing_score_scale_rejected(lib, which):
+    # sm_scale * k_scale * log2(e) must be finite in fp32
+    for sm, ks in ((3e38, 1.0), (1e10, 1e30), (-3e38, 1.0)):
+        a = good_decode() if which == "decode" else good_prefill()
+        a.sm_scale, a.kv.k_scale = sm, ks
+        st = dsize(lib, a)[0] if which == "decode" else psize(lib, a)[0]
+        assert st == -2, (sm, ks, st)
+
+
+def mla_decode_args(sm=0.072, dt=B.PA_BF16, P=64, k_scale=1.0, heads=16):
+    a = good_decode()
+    a.num_qo_heads = heads
+    a.kv = good_kv(dqk=576, dvo=512, hkv=1, P=P, dt=dt)
+    a.kv.v = a.kv.k  # shared latent rows
+    a.kv.k_scale = k_scale
+    a.sm_scale = sm
+    return a
+
+
+def plan(lib, a):
+    fn = lib.paged_attn_decode_plan_name if isinstance(a, B.DecodeArgs) else \
+        lib.paged_attn_prefill_plan_name
+    name = fn(ctypes.byref(a))
+    return name.decode() if name else None
+
+
+def test_plans_for_non_positive_scales(lib):
+    # the flash and MLA kernels order raw scores, valid for a positive scale only
+    assert plan(lib, mla_decode_args()).startswith("mla_decode_mfma")
+    assert plan(lib, mla_decode_args(heads=128)).startswith("mla_decode_mfma")
+    assert plan(lib, mla_decode_args(sm=0.0)) == "generic"
+    assert plan(lib, mla_decode_args(sm=-0.072)) == "generic"
+    assert plan(lib, mla_decode_args(dt=B.PA_FP8_E4M3)) == "mla_decode_mfma_fp8"
+    assert plan(lib, mla_decode_args(dt=B.PA_FP8_E4M3, k_scale=0.0)) == "generic"
+    p = good_prefill()
+    assert plan(lib, p).startswith("flash_attn_mfma")
+    for sm in (0.0, -0.088):
+        p.sm_scale = sm
+        assert plan(lib, p) == "generic"
+    d = good_decode()  # the GQA decode scales every score before it is compared
+    for sm in (0.088, 0.0, -0.088):
+        d.sm_scale = sm
+        assert plan(lib, d).startswith("gqa_decode_mfma")
+
+
+def test_plans_for_generic_only_combinations(lib):
+    assert plan(lib, mla_decode_args(P=8192)) == "generic"
+    assert plan(lib, mla_decode_args(P=4096)).startswith("mla_decode_mfma")
+    a = mla_decode_args(dt=B.PA_FP8_E4M3)
+    a.q_dtype = B.PA_F16
+    assert plan(lib, a) == "generic"
+    p = good_prefill()
+    p.kv.kv_dtype = B.PA_FP8_E4M3
+    for i in range(3):
+        p.kv.k_stride[i] //= 2
+        p.kv.v_stride[i] //= 2
+    assert plan(lib, p) == "generic"

@@ -44,9 +44,11 @@ def test_c5_broadcast_split_decode_full():
     run_sampled(W.config5(), "c5 full", n=96)
 
 
-@pytest.mark.parametrize("h,ql,dt", [(16, 1, W.DT_BF16), (128, 4, W.DT_FP8), (128, 1, W.DT_BF16),
-                                     (16, 4, W.DT_FP8), (16, 1, W.DT_FP8), (16, 4, W.DT_BF16)])
+@pytest.mark.parametrize("dt", [W.DT_BF16, W.DT_FP8])
+@pytest.mark.parametrize("ql", W.C4_QLENS)
+@pytest.mark.parametrize("h", W.C4_HEADS)
 def test_c4_mla_decode_full(h, ql, dt):
+    """All twelve MLA sub-configurations (heads x q_len x KV dtype) at full size."""
     run_sampled(W.config4(num_heads=h, q_len=ql, kv_dtype=dt), f"c4 full h{h} q{ql} {W.DT_NAMES[dt]}",
                 n=96)
 

@@ -373,3 +373,63 @@ def test_merge_special_cases():
     vo, so = OR.merge_states(v4, s4)
     assert vo[0, 0] == pytest.approx(1.0 / (1.0 + math.exp(-2.0)), rel=1e-15)
     assert so[0] == pytest.approx(2.0 + math.log1p(math.exp(-2.0)), rel=1e-15)
+
+
+# ------------------------------------------- score jumps and non-positive scales
+
+def _mla_small(seed, heads, q_len, kv_lens, dt=W.DT_BF16, **kw):
+    rng = np.random.default_rng(seed)
+    return W.build(rng, seed, "mla_small", q_lens=[q_len] * len(kv_lens), kv_lens=kv_lens,
+                   num_qo_heads=heads, num_kv_heads=1, head_dim_qk=576, head_dim_vo=512,
+                   page_size=16, q_dtype=W.DT_BF16, kv_dtype=dt, shared_kv=True, causal=True,
+                   sm_scale=1.0 / math.sqrt(192.0), **kw)
+
+
+def edge_cases():
+    return {
+        "jump_gqa": lambda: W.config2(batch=3, min_len=1, max_len=90, k_late_gain=(32.0, 0, 128)),
+        "jump_prefill": lambda: W.config3(batch=2, min_q=1, max_q=40, max_prefix=60,
+                                          k_late_gain=(32.0, 0, 128)),
+        "jump_mla_fp8": lambda: _mla_small(61, 8, 2, [1, 50, 130], dt=W.DT_FP8,
+                                           k_late_gain=(32.0, 512, 576)),
+        "zero_scale": lambda: dataclasses.replace(W.config2(batch=3, min_len=1, max_len=70),
+                                                  sm_scale=0.0),
+        "negative_scale": lambda: dataclasses.replace(
+            W.config3(batch=2, min_q=1, max_q=30, max_prefix=40), sm_scale=-0.3),
+        "zero_k_scale_fp8": lambda: dataclasses.replace(
+            _mla_small(62, 4, 2, [2, 70], dt=W.DT_FP8), k_scale=0.0),
+        "f16_q_fp8_kv": lambda: W.build(np.random.default_rng(63), 63, "f16xfp8", q_lens=[1, 1],
+                                        kv_lens=[9, 40], num_qo_heads=4, num_kv_heads=2,
+                                        head_dim_qk=64, head_dim_vo=64, page_size=16,
+                                        q_dtype=W.DT_F16, kv_dtype=W.DT_FP8),
+    }
+
+
+@pytest.mark.parametrize("name", list(edge_cases()))
+def test_oracle_matches_dense_edge_cases(name):
+    """Large late score jumps (scores spanning far beyond +-60), zero and negative
+    score scales, a zero fp8 K scale and f16 queries over fp8 KV: the oracle's
+    two-pass softmax against the dense torch reference."""
+    w = edge_cases()[name]()
+    o, lse, mx = OR.attention(w, num_kv_splits=1)
+    ro, rl, rm = dense_attention(w)
+    close(o, ro)
+    close(lse, rl)
+    close(mx, rm)
+    assert np.isfinite(o).all()
+
+
+def test_zero_scale_closed_form():
+    """sm_scale = 0: every allowed score is 0, so O is the plain mean of V over the
+    allowed set, LSE = ln|J| and max = 0."""
+    w = edge_cases()["zero_scale"]()
+    o, lse, mx = OR.attention(w)
+    Hq, G = w.num_qo_heads, w.num_qo_heads // w.num_kv_heads
+    v = OR.decode(w.v, w.kv_dtype).reshape(w.num_pool_pages, w.page_size, w.num_kv_heads, -1)
+    for b in range(w.batch):
+        L = int(w.kv_lens[b])
+        pages = w.kv_indices[w.kv_indptr[b]:w.kv_indptr[b + 1]]
+        rows = v[pages].reshape(-1, w.num_kv_heads, w.head_dim_vo)[:L]
+        for h in range(Hq):
+            close(o[b, h], rows[:, h // G].mean(axis=0))
+            assert abs(lse[b, h] - math.log(L)) < 1e-12 and mx[b, h] == 0.0

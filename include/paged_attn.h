@@ -39,13 +39,16 @@
  *
  * Ownership and concurrency
  *   - The caller owns every buffer.  The library allocates nothing on the
- *     compute path and keeps no pointer after a call returns.
+ *     compute path and keeps no pointer after a call returns (the one array it
+ *     owns, the per-GPU scratch of paged_attn_decode_noalloc, is allocated when
+ *     the library loads).
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *     null stream).  Buffers must stay alive until the stream passes the call.
  *   - A workspace belongs to one in-flight call; two calls that overlap in
  *     time must not share one (the PR #3309 analysis traces a multi-token
  *     mismatch to exactly such sharing, reviewer-feedback section).
- *   - All entry points are reentrant.
+ *   - All entry points are reentrant; calls of paged_attn_decode_noalloc that
+ *     overlap in time on one GPU share its scratch array and race (see there).
  *
  * Errors
  *   - Arguments are validated on the host first; a failed check returns a
@@ -187,6 +190,23 @@ int paged_attn_decode(const pa_decode_args* args, void* workspace, size_t worksp
                       pa_stream_t stream);
 int paged_attn_prefill(const pa_prefill_args* args, void* workspace, size_t workspace_bytes,
                        pa_stream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): paged_attn_decode with
+ * the same arguments, kernels and results, whose workspace is a device array
+ * owned by the library instead of a caller buffer.  The caller still passes
+ * every input and output.  The array holds PA_NOALLOC_SCRATCH_BYTES per GPU;
+ * each GPU the library runs on holds its copy from the time the library loads
+ * until the process ends.  A call whose workspace (paged_attn_decode_workspace_
+ * size) exceeds that returns PA_ERR_WORKSPACE and enqueues nothing.  The call
+ * allocates nothing (no hipMalloc, no allocating library routine).  Every call
+ * on one GPU shares that GPU's array, and no kernel expects it to hold anything
+ * on entry (each workspace byte read is written earlier in the same call), so
+ * calls that overlap in time on one GPU (two streams, two threads) race and
+ * must be serialised by the caller.  Returns PA_ERR_HIP if the array's device
+ * address cannot be read. */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int paged_attn_decode_noalloc(const pa_decode_args* args, pa_stream_t stream);
 
 /* Merge S partial attention states per row through their LSE:
  *   m = max_c s_c, w_c = exp(s_c - m), out = sum_c w_c v_c / sum_c w_c,

@@ -24,6 +24,7 @@ PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 FLAG_FORCE_GENERAL_STRIDES = 0x1
 FLAG_FORCE_GENERIC = 0x2
 FLAG_NO_INTERNAL_SPLIT = 0x4
+NOALLOC_SCRATCH_BYTES = 128 << 20  # PA_NOALLOC_SCRATCH_BYTES
 
 _TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
                 torch.float8_e4m3fn: PA_FP8_E4M3}
@@ -95,6 +96,8 @@ def load_library(path: str = LIB_PATH):
     lib.paged_attn_decode.argtypes = [ctypes.POINTER(DecodeArgs), c_vp, ctypes.c_size_t, c_vp]
     lib.paged_attn_prefill.restype = ctypes.c_int
     lib.paged_attn_prefill.argtypes = [ctypes.POINTER(PrefillArgs), c_vp, ctypes.c_size_t, c_vp]
+    lib.paged_attn_decode_noalloc.restype = ctypes.c_int
+    lib.paged_attn_decode_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), c_vp]
     lib.merge_states.restype = ctypes.c_int
     lib.merge_states.argtypes = [c_vp, ctypes.c_int, c_vp, c_i32, c_i64, c_i32, c_vp,
                                  ctypes.c_int, c_vp, c_vp]
@@ -188,7 +191,10 @@ class PreparedCall:
         self.plan_name = name.decode() if name else None
 
     def __call__(self):
-        _check(self.fn_name, self.fn(self._ref, self._ws, self.ws_bytes, self.stream))
+        if self.fn_name == "paged_attn_decode_noalloc":
+            _check(self.fn_name, self.fn(self._ref, self.stream))
+        else:
+            _check(self.fn_name, self.fn(self._ref, self._ws, self.ws_bytes, self.stream))
         return self.outputs
 
 
@@ -212,8 +218,9 @@ def prepare_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[tor
                    k_scale: float = 1.0, v_scale: float = 1.0, return_max: bool = False,
                    max_kv_len: int = 0, flags: int = 0, out: Optional[torch.Tensor] = None,
                    lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                   stream=None) -> PreparedCall:
-    """Validate and marshal one paged decode; see ``decode``."""
+                   stream=None, noalloc: bool = False) -> PreparedCall:
+    """Validate and marshal one paged decode; see ``decode``.  ``noalloc``: call
+    paged_attn_decode_noalloc (the library's own scratch array is the workspace)."""
     lib = load_library()
     if q.dim() != 4 or not q.is_contiguous():
         raise ValueError("q must be a contiguous [batch, q_len, heads, head_dim] tensor")
@@ -248,6 +255,8 @@ def prepare_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[tor
     a.flags = flags
     keep = dict(o=out, lse=lse, mx=mx, _q=q, _k=k_cache, _v=v_cache, _ip=kv_indptr,
                 _ix=kv_indices, _lp=kv_last_page_len)
+    if noalloc:
+        return PreparedCall("paged_attn_decode_noalloc", a, keep, None, 0, stream)
     workspace, n = _workspace(lib, "paged_attn_decode_workspace_size", a, q.device, workspace)
     return PreparedCall("paged_attn_decode", a, keep, workspace, n, stream)
 

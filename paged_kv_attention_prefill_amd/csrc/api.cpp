@@ -465,6 +465,21 @@ int paged_attn_decode(const pa_decode_args* args, void* workspace, size_t worksp
                   static_cast<hipStream_t>(stream));
 }
 
+int paged_attn_decode_noalloc(const pa_decode_args* args, pa_stream_t stream) {
+  const int st = check_decode(args);
+  if (st != PA_OK) return st;
+  const AttnParams p = params_decode(args);
+  const Plan pl = make_plan(p, args->flags);
+  if (pl.workspace > pa::kNoAllocScratchBytes) return PA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (pl.workspace > 0 && pa::noalloc_scratch(&ws) != hipSuccess) {
+    (void)hipGetLastError();
+    return PA_ERR_HIP;
+  }
+  return run_plan(pl, p, ws, pl.workspace > 0 ? pa::kNoAllocScratchBytes : 0, args->timing_events,
+                  static_cast<hipStream_t>(stream));
+}
+
 int paged_attn_prefill(const pa_prefill_args* args, void* workspace, size_t workspace_bytes,
                        pa_stream_t stream) {
   const int st = check_prefill(args);

@@ -64,6 +64,12 @@ __host__ __device__ inline int num_chunks(int L, int chunk_tokens, int max_chunk
   return n < max_chunks ? n : max_chunks;
 }
 
+// Size of the library-owned scratch array of the allocation-free decode entry
+// point (one per GPU); noalloc_scratch() returns its device address on the
+// current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Launchers (one per kernel family).  Return hipSuccess or the launch error.
 hipError_t launch_generic(const AttnParams& p, hipStream_t stream);
 bool gqa_decode_supported(const AttnParams& p);

@@ -254,3 +254,25 @@ def test_plans_for_generic_only_combinations(lib):
         p.kv.k_stride[i] //= 2
         p.kv.v_stride[i] //= 2
     assert plan(lib, p) == "generic"
+
+
+def test_noalloc_rejects_oversized_workspace(lib):
+    """paged_attn_decode_noalloc: a call whose workspace exceeds the library's
+    scratch array (PA_NOALLOC_SCRATCH_BYTES) is refused before any GPU work;
+    argument errors come back as for paged_attn_decode."""
+    text = open(B.HEADER).read()
+    assert "#define PA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)" in text
+    assert B.NOALLOC_SCRATCH_BYTES == 128 << 20
+    # MLA, 32 requests x 512 rows, KV up to 32768 tokens: fixed chunks of 4096
+    # tokens, 8 chunks x 512 rows x 512 fp32 dims per request = 268 MB
+    a = mla_decode_args(heads=128)
+    a.batch, a.q_len, a.causal = 32, 4, 1
+    a.kv.num_kv_batches = 32
+    a.kv.max_kv_len_hint = 32768
+    st, n = dsize(lib, a)
+    assert st == 0 and n > B.NOALLOC_SCRATCH_BYTES
+    assert lib.paged_attn_decode_noalloc(ctypes.byref(a), None) == -6
+    for path, value, status in DECODE_BAD[:4]:
+        bad = mutate(good_decode(), path, value)
+        assert lib.paged_attn_decode_noalloc(ctypes.byref(bad), None) == status
+    assert lib.paged_attn_decode_noalloc(None, None) == -1

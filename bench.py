@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the paged-attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c3|c5|c4_h16_q1_bf16|sparse_mla_h16_bf16|long_decode_b1|...]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c3|c5|c4_h16_q1_bf16|c4_h128_q4_fp8q|sparse_mla_h16_bf16|long_decode_b1|...]
 
 Default workload: the Llama-70B-like GQA decode (64 requests, q_len 1, 64 query
 / 8 KV heads, head_dim 128, bf16, page 16, KV lengths uniform in [512, 8192]).
@@ -53,9 +53,11 @@ def make_workload(name: str):
         return W.config_sparse(num_heads=int(h[1:]), kv_dtype=W.DT_FP8 if dt == "fp8" else W.DT_BF16,
                                mla=kind == "mla", poison=False)
     if name.startswith("c4"):
+        # c4_h<heads>_q<q_len>_<bf16|fp8|fp8q>; fp8q: fp8 queries over the fp8 cache
         _, h, q, dt = name.split("_")
         return W.config4(num_heads=int(h[1:]), q_len=int(q[1:]),
-                         kv_dtype=W.DT_FP8 if dt == "fp8" else W.DT_BF16, poison=False)
+                         kv_dtype=W.DT_FP8 if dt.startswith("fp8") else W.DT_BF16,
+                         q_dtype=W.DT_FP8 if dt == "fp8q" else W.DT_BF16, poison=False)
     raise SystemExit(f"unknown workload {name}")
 
 

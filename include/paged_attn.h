@@ -36,6 +36,12 @@
  *     kv_len - q_b + i and sees KV tokens j <= that position.
  *   - A row that sees no token gets O = 0, LSE = -inf, max = -inf.
  *   - LSE is the natural log of sum_j exp(sm_scale * q.k_j) (k_scale folded in).
+ *   - fp8 queries (e4m3 codes with a per-tensor q_scale, over an fp8 cache): the
+ *     MLA shapes with more than 64 rows per request multiply fp8 Q by fp8 K on
+ *     the fp8 matrix cores (the FP8 MLA decode target of the PR #3309
+ *     analysis, introduction); every e4m3 code is exact in the kernels'
+ *     arithmetic, so results match the real-valued definition on those codes
+ *     up to fp32 accumulation and 16-bit rounding of P, as for 16-bit queries.
  *
  * Ownership and concurrency
  *   - The caller owns every buffer.  The library allocates nothing on the
@@ -70,7 +76,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 typedef void* pa_stream_t; /* a hipStream_t */
 
@@ -124,7 +130,7 @@ typedef struct {
 /* Decode: every query batch has the same number of queries, q_len. */
 typedef struct {
   const void* q;            /* [batch, q_len, num_qo_heads, head_dim_qk], contiguous */
-  pa_dtype q_dtype;         /* F32, F16 or BF16 */
+  pa_dtype q_dtype;         /* F32, F16, BF16, or FP8_E4M3 with an FP8_E4M3 cache (q_scale) */
   int32_t batch;
   int32_t q_len;
   int32_t num_qo_heads;     /* multiple of kv.num_kv_heads */
@@ -143,6 +149,8 @@ typedef struct {
   void* timing_events[2];   /* optional hipEvent_t pair recorded on `stream` right before and
                                right after the attention kernel (not around a merge launch);
                                NULL to skip */
+  float q_scale;            /* FP8_E4M3 queries only: real Q = q_scale * stored Q (a per-tensor
+                               scale, as k_scale); ignored for other query dtypes */
 } pa_decode_args;
 
 /* Prefill: ragged query batches; the new tokens' K/V are already in the cache
@@ -165,6 +173,7 @@ typedef struct {
   float* row_max;           /* NULL to skip */
   uint32_t flags;
   void* timing_events[2];   /* as in pa_decode_args */
+  float q_scale;            /* as in pa_decode_args */
 } pa_prefill_args;
 
 int pa_abi_version(void);

@@ -21,7 +21,8 @@
  *   For query token i of query batch b (q_b tokens), query head h,
  *   KV head g = h / (Hq/Hkv), allowed set
  *       J = { j : 0 <= j < L  and  (!causal or j <= L - q_b + i) }
- *   s_j = sm_scale * sum_{d<Dqk} q[d] * k_scale * K_j[d]
+ *   s_j = sm_scale * sum_{d<Dqk} q_scale * Q[d] * k_scale * K_j[d]
+ *   (q_scale and k_scale: per-tensor scales of fp8 codes, 1 otherwise)
  *   m   = max_j s_j,  Z = sum_j exp(s_j - m)
  *   O   = sum_j exp(s_j - m) * v_scale * V_j[:Dvo] / Z,  LSE = m + ln Z,  max = m
  *   Empty J: O = 0, LSE = -inf, max = -inf.
@@ -41,7 +42,8 @@
  *   O = sum_c w_c O_c / sum_c w_c, LSE = m + ln sum_c w_c; states with
  *   LSE = -inf carry no weight; all -inf gives O = 0, LSE = -inf.
  *
- * fp8 is OCP e4m3fn: sign, 4-bit exponent (bias 7), 3-bit mantissa,
+ * fp8 (KV caches, and queries with their own scale) is OCP e4m3fn: sign,
+ * 4-bit exponent (bias 7), 3-bit mantissa,
  * subnormals (m/8)*2^-6, S.1111.111 is NaN, no infinities.
  */
 #include <math.h>
@@ -109,7 +111,7 @@ static int batch_of(const int32_t* qo_indptr, int batch, int64_t t) {
  * computes every row, in id order.  Outputs o[S][nrows][Dvo], lse[S][nrows],
  * mx[S][nrows] (mx may be NULL).  Returns 0, or -1 on a bad argument.
  */
-int oracle_paged_attn(const void* q, int q_dtype, const int32_t* qo_indptr, int batch,
+int oracle_paged_attn(const void* q, int q_dtype, double q_scale, const int32_t* qo_indptr, int batch,
                       int num_qo_heads, const void* k, const void* v, int kv_dtype,
                       const int64_t* k_stride, const int64_t* v_stride, int num_kv_heads,
                       int page_size, int head_dim_qk, int head_dim_vo, double k_scale,
@@ -160,7 +162,7 @@ int oracle_paged_attn(const void* q, int q_dtype, const int32_t* qo_indptr, int 
                 const int64_t kbase = page * k_stride[0] + (j % page_size) * k_stride[1] + g * k_stride[2];
                 double acc = 0.0;
                 for (int d = 0; d < head_dim_qk; ++d)
-                    acc += elem(q, q_dtype, qoff + d) * (k_scale * elem(k, kv_dtype, kbase + d));
+                    acc += (q_scale * elem(q, q_dtype, qoff + d)) * (k_scale * elem(k, kv_dtype, kbase + d));
                 s[j - j0] = sm_scale * acc;
                 if (s[j - j0] > m) m = s[j - j0];
             }

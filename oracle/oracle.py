@@ -47,7 +47,7 @@ def declare(lib):
     P = ctypes.c_void_p
     i32, i64, dbl = ctypes.c_int, ctypes.c_int64, ctypes.c_double
     lib.oracle_paged_attn.restype = i32
-    lib.oracle_paged_attn.argtypes = [P, i32, P, i32, i32, P, P, i32, P, P, i32, i32, i32, i32,
+    lib.oracle_paged_attn.argtypes = [P, i32, dbl, P, i32, i32, P, P, i32, P, P, i32, i32, i32, i32,
                                       dbl, dbl, P, P, P, i32, i32, i32, dbl, i32, P, i64, P, P,
                                       P, i32]
     lib.oracle_merge_states.restype = i32
@@ -104,7 +104,7 @@ def attention(w, rows: Optional[Sequence[int]] = None, num_kv_splits: Optional[i
     o = np.empty((S, nrows, w.head_dim_vo), dtype=np.float64)
     lse = np.empty((S, nrows), dtype=np.float64)
     mx = np.empty((S, nrows), dtype=np.float64)
-    rc = lib.oracle_paged_attn(_ptr(q), w.q_dtype, _ptr(qo), w.batch, w.num_qo_heads, _ptr(k),
+    rc = lib.oracle_paged_attn(_ptr(q), w.q_dtype, w.q_scale, _ptr(qo), w.batch, w.num_qo_heads, _ptr(k),
                                _ptr(v), w.kv_dtype, _ptr(ks), _ptr(vs), w.num_kv_heads,
                                w.page_size, w.head_dim_qk, w.head_dim_vo, w.k_scale, w.v_scale,
                                _ptr(ip), _ptr(ix), _ptr(lp), w.num_kv_batches,

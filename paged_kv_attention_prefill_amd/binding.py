@@ -47,7 +47,7 @@ class DecodeArgs(ctypes.Structure):
                 ("num_qo_heads", c_i32), ("kv", PagedKV), ("kv_broadcast", c_i32),
                 ("causal", c_i32), ("sm_scale", c_f32), ("num_kv_splits", c_i32), ("o", c_vp),
                 ("o_dtype", ctypes.c_int), ("lse", c_vp), ("row_max", c_vp),
-                ("flags", ctypes.c_uint32), ("timing_events", c_vp * 2)]
+                ("flags", ctypes.c_uint32), ("timing_events", c_vp * 2), ("q_scale", c_f32)]
 
 
 class PrefillArgs(ctypes.Structure):
@@ -55,7 +55,8 @@ class PrefillArgs(ctypes.Structure):
                 ("total_q", c_i32), ("max_q_len_hint", c_i32), ("num_qo_heads", c_i32),
                 ("kv", PagedKV), ("kv_broadcast", c_i32), ("causal", c_i32),
                 ("sm_scale", c_f32), ("o", c_vp), ("o_dtype", ctypes.c_int), ("lse", c_vp),
-                ("row_max", c_vp), ("flags", ctypes.c_uint32), ("timing_events", c_vp * 2)]
+                ("row_max", c_vp), ("flags", ctypes.c_uint32), ("timing_events", c_vp * 2),
+                ("q_scale", c_f32)]
 
 
 class PagedAttnError(RuntimeError):
@@ -215,7 +216,8 @@ def prepare_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[tor
                    sm_scale: Optional[float] = None, kv_broadcast: bool = False,
                    num_kv_splits: int = 1, out_dtype: Optional[torch.dtype] = None,
                    head_dim_vo: Optional[int] = None, kv_dtype: Optional[int] = None,
-                   k_scale: float = 1.0, v_scale: float = 1.0, return_max: bool = False,
+                   k_scale: float = 1.0, v_scale: float = 1.0, q_scale: float = 1.0,
+                   return_max: bool = False,
                    max_kv_len: int = 0, flags: int = 0, out: Optional[torch.Tensor] = None,
                    lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                    stream=None, noalloc: bool = False) -> PreparedCall:
@@ -253,6 +255,7 @@ def prepare_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[tor
     a.lse = _ptr(lse)
     a.row_max = _ptr(mx)
     a.flags = flags
+    a.q_scale = q_scale
     keep = dict(o=out, lse=lse, mx=mx, _q=q, _k=k_cache, _v=v_cache, _ip=kv_indptr,
                 _ix=kv_indices, _lp=kv_last_page_len)
     if noalloc:
@@ -275,7 +278,8 @@ def prepare_prefill(q: torch.Tensor, qo_indptr: torch.Tensor, k_cache: torch.Ten
                     causal: bool = True, sm_scale: Optional[float] = None,
                     kv_broadcast: bool = False, out_dtype: Optional[torch.dtype] = None,
                     head_dim_vo: Optional[int] = None, kv_dtype: Optional[int] = None,
-                    k_scale: float = 1.0, v_scale: float = 1.0, return_max: bool = False,
+                    k_scale: float = 1.0, v_scale: float = 1.0, q_scale: float = 1.0,
+                    return_max: bool = False,
                     max_q_len: int = 0, max_kv_len: int = 0, flags: int = 0,
                     workspace: Optional[torch.Tensor] = None, stream=None) -> PreparedCall:
     """Validate and marshal one paged prefill; see ``prefill``."""
@@ -309,6 +313,7 @@ def prepare_prefill(q: torch.Tensor, qo_indptr: torch.Tensor, k_cache: torch.Ten
     a.lse = lse.data_ptr()
     a.row_max = _ptr(mx)
     a.flags = flags
+    a.q_scale = q_scale
     workspace, n = _workspace(lib, "paged_attn_prefill_workspace_size", a, q.device, workspace)
     keep = dict(o=out, lse=lse, mx=mx, _q=q, _qo=qo_indptr, _k=k_cache, _v=v_cache,
                 _ip=kv_indptr, _ix=kv_indices, _lp=kv_last_page_len)

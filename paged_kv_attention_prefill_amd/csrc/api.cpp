@@ -37,7 +37,7 @@ bool supported_dims(int dqk, int dvo) {
 bool supported_combo(int qdt, int kvdt) {
   return (qdt == PA_F32 && kvdt == PA_F32) || (qdt == PA_F16 && kvdt == PA_F16) ||
          (qdt == PA_BF16 && kvdt == PA_BF16) || (qdt == PA_BF16 && kvdt == PA_FP8_E4M3) ||
-         (qdt == PA_F16 && kvdt == PA_FP8_E4M3);
+         (qdt == PA_F16 && kvdt == PA_FP8_E4M3) || (qdt == PA_FP8_E4M3 && kvdt == PA_FP8_E4M3);
 }
 
 // Checks shared by decode and prefill.  Returns PA_OK or the first failure.
@@ -47,7 +47,7 @@ int check_common(const void* q, int q_dtype, int num_qo_heads, const pa_paged_kv
     return PA_ERR_NULL;
   if (!known_dtype(q_dtype) || !known_dtype(kv.kv_dtype) || !known_dtype(o_dtype))
     return PA_ERR_DTYPE;
-  if (q_dtype == PA_FP8_E4M3 || o_dtype == PA_FP8_E4M3) return PA_ERR_DTYPE;
+  if (o_dtype == PA_FP8_E4M3) return PA_ERR_DTYPE;
   if (num_qo_heads < 1 || kv.num_kv_heads < 1 || kv.page_size < 1) return PA_ERR_SHAPE;
   if (num_qo_heads % kv.num_kv_heads != 0) return PA_ERR_SHAPE;
   if (kv.num_kv_batches < 1) return PA_ERR_SHAPE;
@@ -95,17 +95,22 @@ void fill_kv(AttnParams& p, const pa_paged_kv& kv) {
   p.max_kv_len = kv.max_kv_len_hint;
 }
 
-// The kernels scale scores by sm_scale * k_scale * log2(e) in fp32; that
-// product must be finite (a scale that overflows it has no fp32 result).
-bool finite_score_scale(float sm_scale, float k_scale) {
-  return std::isfinite(sm_scale) && std::isfinite(sm_scale * k_scale * 1.4426950408889634f);
+// Query scale folded into the score scale: q_scale for fp8 queries, 1 otherwise.
+float query_scale(int q_dtype, float q_scale) { return q_dtype == PA_FP8_E4M3 ? q_scale : 1.f; }
+
+// The kernels scale scores by sm_scale * q_scale * k_scale * log2(e) in fp32;
+// that product must be finite (a scale that overflows it has no fp32 result).
+bool finite_score_scale(float sm_scale, float q_scale, float k_scale) {
+  return std::isfinite(sm_scale) && std::isfinite(q_scale) &&
+         std::isfinite(sm_scale * q_scale * k_scale * 1.4426950408889634f);
 }
 
 int check_decode(const pa_decode_args* a) {
   if (!a) return PA_ERR_NULL;
   if (a->batch < 1 || a->q_len < 1) return PA_ERR_SHAPE;
   if (a->num_kv_splits < 1 || a->num_kv_splits > 1024) return PA_ERR_SHAPE;
-  if (!finite_score_scale(a->sm_scale, a->kv.k_scale)) return PA_ERR_SHAPE;
+  if (!finite_score_scale(a->sm_scale, query_scale(a->q_dtype, a->q_scale), a->kv.k_scale))
+    return PA_ERR_SHAPE;
   int st = check_common(a->q, a->q_dtype, a->num_qo_heads, a->kv, a->kv_broadcast, a->batch, a->o,
                         a->o_dtype);
   if (st != PA_OK) return st;
@@ -121,7 +126,8 @@ int check_prefill(const pa_prefill_args* a) {
   if (!a) return PA_ERR_NULL;
   if (!a->qo_indptr) return PA_ERR_NULL;
   if (a->batch < 1 || a->total_q < 0 || a->max_q_len_hint < 0) return PA_ERR_SHAPE;
-  if (!finite_score_scale(a->sm_scale, a->kv.k_scale)) return PA_ERR_SHAPE;
+  if (!finite_score_scale(a->sm_scale, query_scale(a->q_dtype, a->q_scale), a->kv.k_scale))
+    return PA_ERR_SHAPE;
   return check_common(a->q, a->q_dtype, a->num_qo_heads, a->kv, a->kv_broadcast, a->batch, a->o,
                       a->o_dtype);
 }
@@ -138,7 +144,7 @@ AttnParams params_decode(const pa_decode_args* a) {
   fill_kv(p, a->kv);
   p.num_kv_heads = a->kv.num_kv_heads;
   p.group = a->num_qo_heads / a->kv.num_kv_heads;
-  p.sm_scale = a->sm_scale;
+  p.sm_scale = a->sm_scale * query_scale(a->q_dtype, a->q_scale);  // real Q = q_scale * codes
   p.broadcast = a->kv_broadcast ? 1 : 0;
   p.causal = a->causal ? 1 : 0;
   p.num_splits = a->num_kv_splits;
@@ -165,7 +171,7 @@ AttnParams params_prefill(const pa_prefill_args* a) {
   fill_kv(p, a->kv);
   p.num_kv_heads = a->kv.num_kv_heads;
   p.group = a->num_qo_heads / a->kv.num_kv_heads;
-  p.sm_scale = a->sm_scale;
+  p.sm_scale = a->sm_scale * query_scale(a->q_dtype, a->q_scale);
   p.broadcast = a->kv_broadcast ? 1 : 0;
   p.causal = a->causal ? 1 : 0;
   p.num_splits = 1;
@@ -288,9 +294,10 @@ int gqa_occupancy(const AttnParams& p, bool same) {
 
 // Workgroups per CU of the MLA decode kernel for this row count, per device.
 int mla_occupancy(const AttnParams& p) {
-  static std::atomic<int> occ[2][4][kMaxDevices];
+  static std::atomic<int> occ[3][4][kMaxDevices];
   const int R = p.q_len * p.group;
-  return per_device(occ[p.kv_dtype == PA_FP8_E4M3][R <= 16 ? 0 : R <= 32 ? 1 : R <= 64 ? 2 : 3], 1,
+  const int dt = p.q_dtype == PA_FP8_E4M3 ? 2 : p.kv_dtype == PA_FP8_E4M3 ? 1 : 0;
+  return per_device(occ[dt][R <= 16 ? 0 : R <= 32 ? 1 : R <= 64 ? 2 : 3], 1,
                     [&](int) { return pa::mla_blocks_per_cu(p); });
 }
 
@@ -322,7 +329,9 @@ Plan make_plan(const AttnParams& p, uint32_t flags) {
   const bool positive_scale = p.sm_scale * p.k_scale * 1.4426950408889634f > 0.f;
   if (positive_scale && pa::mla_decode_supported(p)) {
     pl.kind = Plan::MLA_DECODE;
-    pl.name = p.kv_dtype == PA_FP8_E4M3 ? "mla_decode_mfma_fp8" : "mla_decode_mfma";
+    pl.name = p.q_dtype == PA_FP8_E4M3    ? "mla_decode_mfma_fp8q"
+              : p.kv_dtype == PA_FP8_E4M3 ? "mla_decode_mfma_fp8"
+                                          : "mla_decode_mfma";
     const int ct = mla_chunk_tokens(p, flags);
     if (ct > 0 && pa::mla_balanced_ok(p)) {
       // one row tile per request: balanced split over one wave of workgroups

@@ -67,10 +67,24 @@ __device__ __forceinline__ void store_elem(void* base, int64_t idx, float v) {
   }
 }
 
+// Sum over the 64 lanes, every lane receiving the total, in VALU cross-lane
+// steps: DPP quad permutations (lanes l ^ 1, l ^ 2), row half-mirror and row
+// mirror (pairing the quads of each 8 and the halves of each 16 lanes), then the
+// gfx950 permlane swaps of 16-lane rows and 32-lane halves.  Each step adds a
+// lane's value to its partner's, so partners hold identical sums at every step.
+template <int CTRL>
+__device__ __forceinline__ float dpp_partner(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float wave_allreduce_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  v += dpp_partner<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_partner<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_partner<0x141>(v);  // row_half_mirror
+  v += dpp_partner<0x140>(v);  // row_mirror
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float wave_allreduce_max(float v) {

@@ -68,36 +68,51 @@ __global__ __launch_bounds__(256) void generic_attn_kernel(AttnParams p, int n_h
   }
   const float qk_scale = p.sm_scale * p.k_scale * kLog2e;
 
-  for (int64_t j = j0; j < j1; ++j) {
-    const int64_t page = p.kv_indices[pbeg + (int)(j / p.page_size)];
-    const int64_t slot = j % p.page_size;
-    const int64_t kbase = page * p.ks0 + slot * p.ks1 + (int64_t)g * p.ks2;
-    const int64_t vbase = page * p.vs0 + slot * p.vs1 + (int64_t)g * p.vs2;
-    float kf[DQC], vf[DVC];
+  // U tokens per step: their page ids, K and V rows are loaded together (no
+  // load waits on another), then folded in token order
+  constexpr int U = DQC + DVC <= 4 ? 8 : DQC + DVC <= 8 ? 4 : 1;
+  for (int64_t j = j0; j < j1; j += U) {
+    float kf[U][DQC], vf[U][DVC];
 #pragma unroll
-    for (int cc = 0; cc < DQC; ++cc) {
-      const int d = lane + 64 * cc;
-      kf[cc] = d < p.dqk ? load_elem<KT>(p.k, kbase + d) : 0.f;
-    }
+    for (int u = 0; u < U; ++u) {
+      const int64_t jj = j + u < j1 ? j + u : j1 - 1;  // a valid token
+      const int64_t page = p.kv_indices[pbeg + (int)(jj / p.page_size)];
+      const int64_t slot = jj % p.page_size;
+      const int64_t kbase = page * p.ks0 + slot * p.ks1 + (int64_t)g * p.ks2;
+      const int64_t vbase = page * p.vs0 + slot * p.vs1 + (int64_t)g * p.vs2;
 #pragma unroll
-    for (int cc = 0; cc < DVC; ++cc) {
-      const int d = lane + 64 * cc;
-      vf[cc] = d < p.dvo ? load_elem<KT>(p.v, vbase + d) : 0.f;
+      for (int cc = 0; cc < DQC; ++cc) {
+        const int d = lane + 64 * cc;
+        kf[u][cc] = d < p.dqk ? load_elem<KT>(p.k, kbase + d) : 0.f;
+      }
+#pragma unroll
+      for (int cc = 0; cc < DVC; ++cc) {
+        const int d = lane + 64 * cc;
+        vf[u][cc] = d < p.dvo ? load_elem<KT>(p.v, vbase + d) : 0.f;
+      }
     }
 #pragma unroll
     for (int r = 0; r < kHB; ++r) {
       if (r >= nh) break;
-      float part = 0.f;
+      float s[U];
 #pragma unroll
-      for (int cc = 0; cc < DQC; ++cc) part = fmaf(qf[r][cc], kf[cc], part);
-      const float s = wave_allreduce_sum(part) * qk_scale;
-      const float mn = fmaxf(m[r], s);
-      const float a = fast_exp2(m[r] - mn);
-      const float pr = fast_exp2(s - mn);
-      l[r] = fmaf(l[r], a, pr);
+      for (int u = 0; u < U; ++u) {
+        float part = 0.f;
 #pragma unroll
-      for (int cc = 0; cc < DVC; ++cc) of[r][cc] = fmaf(of[r][cc], a, pr * vf[cc]);
-      m[r] = mn;
+        for (int cc = 0; cc < DQC; ++cc) part = fmaf(qf[r][cc], kf[u][cc], part);
+        s[u] = wave_allreduce_sum(part) * qk_scale;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (j + u >= j1) break;
+        const float mn = fmaxf(m[r], s[u]);
+        const float a = fast_exp2(m[r] - mn);
+        const float pr = fast_exp2(s[u] - mn);
+        l[r] = fmaf(l[r], a, pr);
+#pragma unroll
+        for (int cc = 0; cc < DVC; ++cc) of[r][cc] = fmaf(of[r][cc], a, pr * vf[u][cc]);
+        m[r] = mn;
+      }
     }
   }
 
@@ -154,6 +169,7 @@ hipError_t launch_generic(const AttnParams& p, hipStream_t stream) {
   if (p.q_dtype == BF16 && p.kv_dtype == BF16) return launch_dims<BF16, BF16>(p, stream);
   if (p.q_dtype == BF16 && p.kv_dtype == FP8) return launch_dims<BF16, FP8>(p, stream);
   if (p.q_dtype == F16 && p.kv_dtype == FP8) return launch_dims<F16, FP8>(p, stream);
+  if (p.q_dtype == FP8 && p.kv_dtype == FP8) return launch_dims<FP8, FP8>(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -344,6 +344,13 @@ __device__ __forceinline__ i16x8_t fp8x8_to_bf16(i32x2_t x) {
   asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0 op_sel:[1,0,0]" : "=v"(o3) : "v"(x.y));
   return as_i16x8(make_uint4(o0, o1, o2, o3));
 }
+// Eight query elements at element offset e of Q as bf16 bits: bf16 queries, or
+// fp8 codes widened exactly (the query scale is in the score scale).
+__device__ __forceinline__ i16x8_t load_q8(const AttnParams& p, int64_t e) {
+  if (p.q_dtype == FP8)
+    return fp8x8_to_bf16(*reinterpret_cast<const i32x2_t*>(static_cast<const uint8_t*>(p.q) + e));
+  return *reinterpret_cast<const i16x8_t*>(static_cast<const uint16_t*>(p.q) + e);
+}
 // Two 16-byte reads.
 __device__ __forceinline__ void lds_read2_b128(uint32_t a0, uint32_t a1, i32x4_t& r0, i32x4_t& r1) {
   asm volatile(
@@ -366,15 +373,15 @@ __device__ __forceinline__ i32x4_t lds_read_b128(uint32_t a0) {
 }
 
 // LDS swizzle: piece p of row r sits at slot p ^ swz(r) of the row (the XOR stays
-// within p's aligned group of 8 pieces).  With the 1152-byte pitch, even rows
-// start at bank 0 and odd rows at bank 32; swz(r) = g(r/2 mod 8) with
-// g(x) = 2 (x mod 4) + x / 4 makes the 16-lane K operand reads (16 rows, one
-// piece) and the 32-lane transposed V reads (8 rows, a pair of pieces) hit 64
-// distinct banks.
-__device__ __forceinline__ int mla_swz(int r) {
-  const int x = (r >> 1) & 7;
-  return 2 * (x & 3) + (x >> 2);
-}
+// within p's aligned group of 8 pieces).  gfx950's LDS has 128 four-byte banks
+// and serves a 16-byte read 32 lanes per cycle and an 8-byte read 64 lanes per
+// cycle (this model predicts the bank-conflict counts measured on this kernel
+// and on the padded-pitch prefill kernel).  With the 1152-byte pitch, row r
+// starts at bank 32 (r mod 4).  swz(r) = 2 r1 ^ 4 r2 ^ 3 r3 (r_i: bit i of r)
+// makes the K operand reads (16 rows x two pieces per 32 lanes) and the
+// transposed V reads (16 rows x two pieces x two halves per 64 lanes) hit
+// distinct banks; it depends on bits 1..3 only, so rows r and r + 16 share it.
+__device__ __forceinline__ int mla_swz(int r) { return (r & 6) ^ (3 * ((r >> 3) & 1)); }
 
 // Direct HBM -> LDS load of tile rows [jb, jb + kTK2) (clamped into [.., we)):
 // instruction i of the tile fills LDS bytes [1024 i, 1024 i + 1024); lane l
@@ -419,7 +426,23 @@ static_assert(kTK2 * kPieces8 % 64 == 0, "an fp8 tile is a whole number of 1-KB 
 // distinct banks.
 __device__ __forceinline__ int swz8(int r) { return (r >> 2) & 3; }
 
-template <bool SWZ = false>
+// Stage layout of the many-rows kernel for fp8 queries: piece p of row r at slot
+// p ^ swzq(r) within p's aligned group of four.  Rows are 576 bytes, so row r
+// starts at 16-byte unit 4 r mod 32 of the 128 banks; swzq(r) = (r >> 3) & 3
+// puts the K operand reads (per 32 lanes: 16 rows x two lane groups, 16 bytes
+// each) and the transposed 8-bit V reads (per 64 lanes: 32 rows x two 8-byte
+// halves) on distinct banks.
+__device__ __forceinline__ int swzq(int r) { return (r >> 3) & 3; }
+
+// fp8 stage swizzle by layout: 0 linear, 1 swz8, 2 swzq
+template <int SW>
+__device__ __forceinline__ int fp8_swz(int r) {
+  if constexpr (SW == 1) return swz8(r);
+  else if constexpr (SW == 2) return swzq(r);
+  else return 0;
+}
+
+template <int SW = 0>
 __device__ __forceinline__ void dma_tile8(const AttnParams& p, const int* s_pages, uint8_t* stage,
                                           int jb, int we, int wbP, int g, int w, int lane) {
   const uint8_t* kbase = static_cast<const uint8_t*>(p.k);
@@ -437,7 +460,7 @@ __device__ __forceinline__ void dma_tile8(const AttnParams& p, const int* s_page
     const uint32_t pi = div_by_magic(jj, p.page_magic);
     const uint32_t pslot = jj - pi * (uint32_t)p.page_size;
     const uint32_t page = s_pages[pi];
-    const uint64_t off = (uint64_t)page * ks0 + (pslot * ks1 + kc + 16 * (SWZ ? piece ^ swz8(row) : piece));
+    const uint64_t off = (uint64_t)page * ks0 + (pslot * ks1 + kc + 16 * (piece ^ fp8_swz<SW>(row)));
     if (i < kDma8)
       __builtin_amdgcn_global_load_lds(kbase + off, (PA_LDS void*)(stage + 1024 * i), 16, 0, 0);
   }
@@ -447,7 +470,7 @@ __device__ __forceinline__ void dma_tile8(const AttnParams& p, const int* s_page
 // page's offset is uniform, and the (row, piece) each lane loads is fixed per
 // load instruction, so the per-lane part is precomputed once (PageLanes) and a
 // load costs a clamp, a multiply-add and the address add.
-template <bool FP8, bool SWZ = false>
+template <bool FP8, int SW = 0>
 struct PageLanes {
   static constexpr int N = ((FP8 ? kDma8 : kDma) + kNW2 - 1) / kNW2;  // load rounds
   int row[N];       // tile row of this lane's piece in round r
@@ -460,7 +483,7 @@ struct PageLanes {
       if constexpr (FP8) {
         row[r] = slot / kPieces8;
         const int q = slot - row[r] * kPieces8;
-        off[r] = (uint32_t)(g * p.ks2) + 16 * (SWZ ? q ^ swz8(row[r]) : q);
+        off[r] = (uint32_t)(g * p.ks2) + 16 * (q ^ fp8_swz<SW>(row[r]));
       } else {
         row[r] = slot / kPieces;
         const int q = slot - row[r] * kPieces;
@@ -494,7 +517,7 @@ __device__ __forceinline__ void dma_page_fp8(const AttnParams& p, int page, uint
                                              int we, int wbP, const PageLanes<true>& pl, int w) {
   PA_DMA_PAGE_BODY(uint8_t, kDma8, PageLanes<true>)
 }
-using PageLanes8S = PageLanes<true, true>;  // swizzled fp8 stages
+using PageLanes8S = PageLanes<true, 1>;  // swizzled fp8 stages
 __device__ __forceinline__ void dma_page_fp8s(const AttnParams& p, int page, uint8_t* stage, int jb,
                                               int we, int wbP, const PageLanes8S& pl, int w) {
   PA_DMA_PAGE_BODY(uint8_t, kDma8, PageLanes8S)
@@ -717,12 +740,11 @@ __device__ __forceinline__ void mla_rows_range(const AttnParams& p, int b, int g
   i16x8_t qreg[KK];
   {
     const int qi = row_ok ? row / p.group : 0, qh = row_ok ? row % p.group : 0;
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q) +
-                         ((int64_t)(b * p.q_len + qi) * p.num_qo_heads + (int64_t)g * p.group + qh) * kDqk +
-                         8 * lg;
+    const int64_t qe =
+        ((int64_t)(b * p.q_len + qi) * p.num_qo_heads + (int64_t)g * p.group + qh) * kDqk + 8 * lg;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      qreg[kk] = row_ok ? *reinterpret_cast<const i16x8_t*>(qp + 32 * kk) : i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      qreg[kk] = row_ok ? load_q8(p, qe + 32 * kk) : i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
   }
 
   MlaRow st{-INFINITY, 0.f, -INFINITY};
@@ -871,6 +893,320 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_rows_kernel(AttnParams p, in
 }
 
 // ---------------------------------------------------------------------------
+// fp8 queries over an fp8 cache, more than 64 rows per request: Q.K on the fp8
+// matrix cores (the FP8 MLA decode that the FlashInfer PR #3309 analysis
+// targets, introduction).  The workgroup shape and the tile pipeline are those
+// of the many-rows kernel (8 waves x 16 rows, 32-token tiles streamed HBM ->
+// LDS by direct loads, four stages), but the tile stays as fp8 codes in LDS
+// (swzq layout) and nothing is widened in LDS:
+//   S^T = K Q^T on v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales
+//   (the per-tensor query and cache scales are in the score scale): K codes
+//   from LDS as the A operand (32 per lane, two 16-byte reads), the rows' Q^T
+//   codes in registers as the B operand (40 registers instead of 72 for
+//   bf16); the 576 dims are four 128-dim k-steps and one of 64 dims, whose
+//   other half is zero in both operands;
+//   online softmax as in mla_rows_tile;
+//   O^T += V^T P^T on the bf16 16x16x32 MFMA, V^T read by transposed 8-bit
+//   reads (ds_read_b64_tr_b8) in P^T's token order and widened exactly to
+//   bf16 in registers.
+// The two operands of the fp8 MFMA pair their (lane group, byte) positions
+// identically (checked on the device), so a lane group's 32 bytes may hold any
+// 32 dims as long as K and Q^T hold the same dims in the same places.
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+constexpr int kKS8 = 5;  // k-steps of 128 dims (the last one half used)
+
+__device__ __forceinline__ f32x4_t mfma_fp8(const i32x8_t& a, const i32x8_t& b, f32x4_t c) {
+  // format 0 (e4m3) for both operands, block scales 2^0 (E8M0 127)
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// One 32-token tile of math for this wave's 16 rows (lane: row l16, group lg).
+__device__ __forceinline__ void mla_rows8_tile(const uint8_t* kv, int jb, int lim, bool need_mask,
+                                               const i32x8_t (&qreg)[kKS8], float qk_scale,
+                                               MlaRow& st, f32x4_t (&oacc)[kDvo / 16], int lane) {
+  constexpr int NDT = kDvo / 16;
+  constexpr int kPitch = kPieces8 * 16;  // 576-byte fp8 rows
+  int ln = lane;  // per-lane offsets recomputed per tile, not held across the loop
+  asm volatile("" : "+v"(ln));
+  const int l16 = ln & 15, lg = ln >> 4;
+  // K operand of k-step ks, block st: row 16 st + l16, pieces 8 ks + 2 lg + e
+  // (e = 0, 1), i.e. slot 8 ks + 4 (lg >> 1) + ((2 (lg & 1) + e) ^ swzq(row)):
+  // four per-lane bases (st, e), the k-step adding 128 ks bytes; k-step 4 has
+  // pieces 32..35 only (lane groups 0 and 1)
+  const int sw0 = swzq(l16);  // block 1 rows: sw0 ^ 2
+  const uint32_t kvb = lds_off(kv);
+  uint32_t kb[2][2];  // LDS byte addresses
+#pragma unroll
+  for (int stb = 0; stb < 2; ++stb)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      kb[stb][e] = kvb + (16 * stb + l16) * kPitch + 64 * (lg >> 1) +
+                   16 * ((2 * (lg & 1) + e) ^ (sw0 ^ (2 * stb)));
+  // k-step 4 (dims 512..575): lane groups 2 and 3 would address pieces 36..39,
+  // past the row; they read pieces 32..35 of their row instead (in bounds, a
+  // plain read for every lane) and their operand is zeroed by a select
+  const uint32_t tail_back = lg >= 2 ? 64u : 0u;
+  auto kfrag = [&](int f) __attribute__((always_inline)) {
+    const int ks = f >> 1, stb = f & 1;
+    const uint32_t back = ks == kKS8 - 1 ? tail_back : 0u;
+    const i32x4_t lo = *(const PA_LDS i32x4_t*)(uintptr_t)(kb[stb][0] + 128 * ks - back);
+    const i32x4_t hi = *(const PA_LDS i32x4_t*)(uintptr_t)(kb[stb][1] + 128 * ks - back);
+    return i32x8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  };
+  constexpr int kPF = 2;  // K operands in flight
+  f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  i32x8_t ring[kPF];
+#pragma unroll
+  for (int f = 0; f < kPF; ++f) ring[f] = kfrag(f);
+#pragma unroll
+  for (int f = 0; f < 2 * kKS8; ++f) {
+    i32x8_t a = ring[f % kPF];
+    if (f + kPF < 2 * kKS8) ring[f % kPF] = kfrag(f + kPF);
+    if (f >= 2 * (kKS8 - 1)) {
+      const i32x8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
+      a = tail_back ? z : a;
+    }
+    sacc[f & 1] = mfma_fp8(a, qreg[f >> 1], sacc[f & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // lane holds row l16, tokens jb + 16st + 4lg + i
+  float sv[2][4];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = jb + 16 * st2 + 4 * lg + i;
+      sv[st2][i] = (!need_mask || j < lim) ? sacc[st2][i] : -INFINITY;
+      tmax = fmaxf(tmax, sv[st2][i]);
+    }
+  tmax = xor32_max(xor16_max(tmax)) * qk_scale;
+  st.true_max = fmaxf(st.true_max, tmax);
+  // lazily re-based reference max (as in mla_rows_tile)
+  const bool grow = tmax > st.m + 8.f;
+  if (__ballot(grow)) {
+    const float mnew = grow ? tmax : st.m;
+    const float alpha =
+        fast_exp2((st.m == -INFINITY ? -INFINITY : st.m) - (mnew == -INFINITY ? 0.f : mnew));
+    const float a = grow ? alpha : 1.f;
+    st.lsum *= a;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) oacc[t] *= a;
+    st.m = mnew;
+  }
+  const float nmref = -(st.m == -INFINITY ? 0.f : st.m);
+  float e[8];
+#pragma unroll
+  for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e[4 * st2 + i] = fast_exp2(fmaf(sv[st2][i], qk_scale, nmref));
+  const uint4 bits = make_uint4(pack2<BF16>(e[0], e[1]), pack2<BF16>(e[2], e[3]),
+                                pack2<BF16>(e[4], e[5]), pack2<BF16>(e[6], e[7]));
+  const i16x8_t pb = as_i16x8(bits);
+  st.lsum = sum2<BF16>(bits.x, sum2<BF16>(bits.y, sum2<BF16>(bits.z, sum2<BF16>(bits.w, st.lsum))));
+  // O^T += V^T P^T: in each 16-lane group q, lane 2j + h addresses bytes 8h..8h+7
+  // of the dim block's piece in token row trow(q, j), and lane c receives dim c of
+  // the group's eight rows: tokens 4q + j (j < 4) and 16 + 4q + (j - 4), the
+  // token order of P^T above
+  const int q = ln >> 4, jr = (ln & 15) >> 1, h = ln & 1;
+  const int trow = jr < 4 ? 4 * q + jr : 12 + 4 * q + jr;
+  const int tsw = swzq(trow);
+  // dim block d sits at slot 4 (d >> 2) + ((d & 3) ^ tsw): four per-lane bases
+  // (d mod 4), the block group adding 64 (d >> 2) bytes
+  uint32_t vb[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) vb[u] = kvb + trow * kPitch + 8 * h + 16 * (u ^ tsw);
+  auto vfrag = [&](int d) __attribute__((always_inline)) {
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2_t*)(uintptr_t)(vb[d & 3] + 64 * (d >> 2)));
+  };
+  constexpr int kPV = 4;  // V^T operands in flight
+  i32x2_t vring[kPV];
+#pragma unroll
+  for (int d = 0; d < kPV; ++d) vring[d] = vfrag(d);
+#pragma unroll
+  for (int d = 0; d < NDT; ++d) {
+    const i16x8_t va = fp8x8_to_bf16(vring[d % kPV]);
+    if (d + kPV < NDT) vring[d % kPV] = vfrag(d + kPV);
+    oacc[d] = mfma16<BF16>(va, pb, oacc[d]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One (request b, KV head g, row tile rt) token range [j0, j1) of the fp8-query
+// many-rows kernel; output as for the narrow kernel.  Called by every thread.
+__device__ __forceinline__ void mla_rows8_range(const AttnParams& p, int b, int g, int rt, int L, int j0,
+                                                int j1, bool to_ws, int64_t wslot, int c, uint8_t* s_kv0,
+                                                uint8_t* s_kv1, uint8_t* s_kv2, uint8_t* s_kv3,
+                                                int* s_pages) {
+  constexpr int NDT = kDvo / 16;  // 32 16-dim tiles of O
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
+  const int l16 = lane & 15, lg = lane >> 4;
+  b = uni(b);
+  g = uni(g);
+  L = uni(L);
+  j0 = uni(j0);
+  j1 = uni(j1);
+  const int kb = p.broadcast ? 0 : b;
+  const int pbeg = p.kv_indptr[kb];
+  const int R = p.q_len * p.group;
+  const int row0 = rt * kRT2;
+
+  const int row = row0 + kRW * w + l16;
+  const bool row_ok = row < R;
+  int lim = j1;
+  if (row_ok && p.causal) lim = min(lim, L - p.q_len + row / p.group + 1);
+  if (!row_ok) lim = INT_MIN;
+  int lo = row_ok ? lim : INT_MAX;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) lo = min(lo, __shfl_xor(lo, off, 64));
+  const int wave_lim_min = __builtin_amdgcn_readfirstlane(lo);
+  const bool wave_live = wave_lim_min != INT_MAX;
+  int jhi = j1;
+  if (p.causal) jhi = min(j1, L - p.q_len + (min(row0 + kRT2, R) - 1) / p.group + 1);
+
+  // Q^T codes: k-step ks, lane group lg holds dims 128 ks + 32 lg .. + 31 of row
+  i32x8_t qreg[kKS8];
+  {
+    const int qi = row_ok ? row / p.group : 0, qh = row_ok ? row % p.group : 0;
+    const uint8_t* qp = static_cast<const uint8_t*>(p.q) +
+                        ((int64_t)(b * p.q_len + qi) * p.num_qo_heads + (int64_t)g * p.group + qh) * kDqk +
+                        32 * lg;
+#pragma unroll
+    for (int ks = 0; ks < kKS8; ++ks) {
+      const bool ok = row_ok && (ks < kKS8 - 1 || lg < 2);
+      const i32x4_t z = {0, 0, 0, 0};
+      const i32x4_t a = ok ? *reinterpret_cast<const i32x4_t*>(qp + 128 * ks) : z;
+      const i32x4_t bq = ok ? *reinterpret_cast<const i32x4_t*>(qp + 128 * ks + 16) : z;
+      qreg[ks] = i32x8_t{a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
+    }
+  }
+
+  MlaRow st{-INFINITY, 0.f, -INFINITY};
+  f32x4_t oacc[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) oacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const float qk_scale = p.sm_scale * p.k_scale * kLog2e;
+  const int P = p.page_size;
+
+  if (jhi > j0) {
+    const int pfirst = j0 / P, plast = (jhi - 1) / P;
+    for (int wb = pfirst; wb <= plast; wb += kPageWinM) {
+      const int npw = min(kPageWinM, plast - wb + 1);
+      __syncthreads();  // the previous window's readers are done
+      for (int i = tid; i < npw; i += 64 * kNW2) s_pages[i] = p.kv_indices[pbeg + wb + i];
+      __syncthreads();
+      const int ws = max(j0, wb * P), we = min(jhi, (wb + npw) * P);
+      const int nk = (we - ws + kTK2 - 1) / kTK2;
+      // tile k in stage k % 4, tiles k+1..k+3 in flight during its math (as in
+      // the many-rows kernel)
+      constexpr int kMinDma = kDma8 / kNW2;  // direct loads per wave per tile
+      constexpr int kWait = 2 * kMinDma;     // vmcnt that leaves only tiles k+1, k+2 in flight
+      static_assert(kWait < 64, "vmcnt field");
+      constexpr int kWaitImm = (kWait & 0xF) | ((kWait >> 4) << 14) | 0x70 | 0xF00;
+      const int wbP = wb * P;
+      auto tile_at = [&](int k) { return ws + min(k, nk - 1) * kTK2; };
+      auto dma = [&](uint8_t* stage, int jb) __attribute__((always_inline)) {
+        dma_tile8<2>(p, s_pages, stage, jb, we, wbP, g, w, lane);
+      };
+      dma(s_kv0, tile_at(0));
+      dma(s_kv1, tile_at(1));
+      dma(s_kv2, tile_at(2));
+#define PA_MLA8_STEP(K, CUR, NEXT3)                                                             \
+  {                                                                                           \
+    __builtin_amdgcn_s_waitcnt(kWaitImm); /* tile K's direct loads are done */                \
+    __syncthreads();                                                                           \
+    dma(NEXT3, tile_at((K) + 3));                                                             \
+    const int jb = ws + (K) * kTK2;                                                           \
+    if (wave_live)                                                                            \
+      mla_rows8_tile(CUR, jb, lim, jb + kTK2 > wave_lim_min, qreg, qk_scale, st, oacc, lane); \
+  }
+      for (int k = 0; k < nk; k += 4) {
+        PA_MLA8_STEP(k, s_kv0, s_kv3);
+        if (k + 1 >= nk) break;
+        PA_MLA8_STEP(k + 1, s_kv1, s_kv0);
+        if (k + 2 >= nk) break;
+        PA_MLA8_STEP(k + 2, s_kv2, s_kv1);
+        if (k + 3 >= nk) break;
+        PA_MLA8_STEP(k + 3, s_kv3, s_kv2);
+      }
+#undef PA_MLA8_STEP
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no loads in flight into the stages
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: lane (row l16, group lg) holds dims 16d + 4lg + (0..3)
+  const float ltot = xor32_sum(xor16_sum(st.lsum));
+  if (!row_ok) return;
+  const bool empty = !(ltot > 0.f);
+  const float scale = empty ? 0.f : p.v_scale / ltot;
+  const int64_t rid = (int64_t)(b * p.q_len + row / p.group) * p.num_qo_heads + (int64_t)g * p.group +
+                      row % p.group;
+  const int64_t wrow = wslot * p.ws_rows + row;
+#pragma unroll
+  for (int d = 0; d < NDT; ++d) {
+    const int dim = 16 * d + 4 * lg;
+    const float x0 = oacc[d][0] * scale, x1 = oacc[d][1] * scale;
+    const float x2 = oacc[d][2] * scale, x3 = oacc[d][3] * scale;
+    if (to_ws) {
+      *reinterpret_cast<float4*>(p.ws_o + wrow * kDvo + dim) = make_float4(x0, x1, x2, x3);
+    } else if (p.o_dtype == F32) {
+      *reinterpret_cast<float4*>(static_cast<float*>(p.o) + c * p.o_split_stride + rid * kDvo + dim) =
+          make_float4(x0, x1, x2, x3);
+    } else {
+      const uint2 v = p.o_dtype == F16 ? make_uint2(pack2<F16>(x0, x1), pack2<F16>(x2, x3))
+                                       : make_uint2(pack2<BF16>(x0, x1), pack2<BF16>(x2, x3));
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + c * p.o_split_stride + rid * kDvo + dim) = v;
+    }
+  }
+  if (lg == 0) {
+    const float lse = empty ? -INFINITY : (st.m + fast_log2(ltot)) * kLn2;
+    const float mx = empty ? -INFINITY : st.true_max * kLn2;
+    if (to_ws) {
+      p.ws_lse[wrow] = lse;
+      p.ws_mx[wrow] = mx;
+    } else {
+      const int64_t sidx = c * p.s_split_stride + rid;
+      if (p.lse) p.lse[sidx] = lse;
+      if (p.mx) p.mx[sidx] = mx;
+    }
+  }
+}
+
+// Workgroups as for the many-rows kernel.
+__global__ __launch_bounds__(64 * kNW2, 1) void mla_rows8_kernel(AttnParams p, int nrt, int ngroups) {
+  __shared__ __align__(16) uint8_t s_kv0[kStage8];
+  __shared__ __align__(16) uint8_t s_kv1[kStage8];
+  __shared__ __align__(16) uint8_t s_kv2[kStage8];
+  __shared__ __align__(16) uint8_t s_kv3[kStage8];
+  __shared__ int s_pages[kPageWinM];
+  if (p.bal_blocks > 0) {
+    BalCursor cur;
+    if (!cur.start(p, blockIdx.x)) return;
+    do {
+      mla_rows8_range(p, cur.b, cur.g, 0, cur.L, cur.j0(p), cur.j1(p), !cur.whole(), cur.slot(p), 0,
+                      s_kv0, s_kv1, s_kv2, s_kv3, s_pages);
+    } while (cur.next(p));
+    return;
+  }
+  const int lam = blockIdx.x;
+  const int xcd = lam % 8, k8 = lam / 8;
+  const int rt = k8 % nrt;
+  const int gi = (k8 / nrt) * 8 + xcd;
+  if (gi >= ngroups) return;
+  const int b = gi / (p.num_kv_heads * p.max_chunks);
+  const int g = (gi / p.max_chunks) % p.num_kv_heads;
+  const int c = gi % p.max_chunks;
+  int L, j0, j1;
+  bool to_ws;
+  if (!mla_item_range(p, b, c, L, j0, j1, to_ws)) return;
+  mla_rows8_range(p, b, g, rt, L, j0, j1, to_ws, (int64_t)(b * p.num_kv_heads + g) * p.max_chunks + c, c,
+                  s_kv0, s_kv1, s_kv2, s_kv3, s_pages);
+}
+
+// ---------------------------------------------------------------------------
 // Up to 16 rows per request (q_len x H <= 16): one row block is too little MFMA
 // work for one wave to keep up with HBM, so the tile is shared out by dims.
 // Per 32-token tile (LDS stages fed by direct loads, as above):
@@ -929,13 +1265,11 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
   i16x8_t qreg[3];
   {
     const int qi = row_ok ? row / p.group : 0, qh = row_ok ? row % p.group : 0;
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q) +
-                         ((int64_t)(b * p.q_len + qi) * p.num_qo_heads + (int64_t)g * p.group + qh) * kDqk +
-                         8 * lg;
+    const int64_t qe =
+        ((int64_t)(b * p.q_len + qi) * p.num_qo_heads + (int64_t)g * p.group + qh) * kDqk + 8 * lg;
 #pragma unroll
     for (int u = 0; u < 3; ++u)
-      qreg[u] = row_ok && w < kNS ? *reinterpret_cast<const i16x8_t*>(qp + 32 * (3 * w + u))
-                                  : i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      qreg[u] = row_ok && w < kNS ? load_q8(p, qe + 32 * (3 * w + u)) : i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
   }
 
   // softmax state: kept by the reducing wave (kNS) only
@@ -1106,7 +1440,7 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
   // tiles never straddle a page when the page size is a multiple of the tile
   // (range starts are multiples of the tile or of the page)
   const bool page_tiles = P % kTK2 == 0 && j0 % kTK2 == 0;
-  PageLanes<FP8, FP8> plane;
+  PageLanes<FP8, FP8 ? 1 : 0> plane;
   if (page_tiles) plane.init(p, g, w, lane);
   if (jhi > j0) {
     const int pfirst = j0 / P, plast = (jhi - 1) / P;
@@ -1141,7 +1475,7 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
             dma_page_bf16(p, page, stage, jb, we, wbP, plane, w);
         } else {
           if constexpr (FP8)
-            dma_tile8<true>(p, s_pages, stage, jb, we, wbP, g, w, lane);
+            dma_tile8<1>(p, s_pages, stage, jb, we, wbP, g, w, lane);
           else
             dma_tile(p, s_pages, stage, jb, we, wbP, g, w, lane);
         }
@@ -1359,13 +1693,11 @@ __device__ __forceinline__ void mla_mid_range(const AttnParams& p, int b, int g,
   i16x8_t qreg[KMAX];
   {
     const int qi = row_ok ? row / p.group : 0, qh = row_ok ? row % p.group : 0;
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q) +
-                         ((int64_t)(b * p.q_len + qi) * p.num_qo_heads + (int64_t)g * p.group + qh) * kDqk +
-                         8 * lg;
+    const int64_t qe =
+        ((int64_t)(b * p.q_len + qi) * p.num_qo_heads + (int64_t)g * p.group + qh) * kDqk + 8 * lg;
 #pragma unroll
     for (int u = 0; u < KMAX; ++u)
-      qreg[u] = row_ok && u < nks ? *reinterpret_cast<const i16x8_t*>(qp + 32 * (k0 + u))
-                                  : i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      qreg[u] = row_ok && u < nks ? load_q8(p, qe + 32 * (k0 + u)) : i16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
   }
 
   // softmax state of row block w, kept by wave w < NRB
@@ -1573,7 +1905,7 @@ __device__ __forceinline__ void mla_mid_range(const AttnParams& p, int b, int g,
   };
 
   const bool page_tiles = P % kTK2 == 0 && j0 % kTK2 == 0;
-  PageLanes<FP8, FP8> plane;
+  PageLanes<FP8, FP8 ? 1 : 0> plane;
   if (page_tiles) plane.init(p, g, w, lane);
   if (jhi > j0) {
     const int pfirst = j0 / P, plast = (jhi - 1) / P;
@@ -1607,7 +1939,7 @@ __device__ __forceinline__ void mla_mid_range(const AttnParams& p, int b, int g,
             dma_page_bf16(p, page, stage, jb, we, wbP, plane, w);
         } else {
           if constexpr (FP8)
-            dma_tile8<true>(p, s_pages, stage, jb, we, wbP, g, w, lane);
+            dma_tile8<1>(p, s_pages, stage, jb, we, wbP, g, w, lane);
           else
             dma_tile(p, s_pages, stage, jb, we, wbP, g, w, lane);
         }
@@ -1785,6 +2117,8 @@ hipError_t launch_rows(const AttnParams& p, hipStream_t stream) {
       mla_mid_kernel<true, 4><<<blocks, 64 * kNW2, 0, stream>>>(q, ngroups);
     else
       mla_mid_kernel<false, 4><<<blocks, 64 * kNW2, 0, stream>>>(q, ngroups);
+  } else if (p.q_dtype == FP8) {
+    mla_rows8_kernel<<<blocks, 64 * kNW2, 0, stream>>>(q, nrt, ngroups);
   } else if (p.kv_dtype == FP8) {
     mla_rows_kernel<true><<<blocks, 64 * kNW2, 0, stream>>>(q, nrt, ngroups);
   } else {
@@ -1806,7 +2140,9 @@ bool mla_rows_path(const AttnParams& p) {
 
 bool mla_decode_supported(const AttnParams& p) {
   // other page sizes and strides go to the generic kernel
-  return mla_rows_path(p) && p.qo_indptr == nullptr && p.q_dtype == BF16 && (p.kv_dtype == BF16 || p.kv_dtype == FP8) &&
+  return mla_rows_path(p) && p.qo_indptr == nullptr &&
+         ((p.q_dtype == BF16 && (p.kv_dtype == BF16 || p.kv_dtype == FP8)) ||
+          (p.q_dtype == FP8 && p.kv_dtype == FP8)) &&
          p.dqk == kDqk && p.dvo == kDvo && p.ks0 == p.vs0 && p.ks1 == p.vs1 && p.ks2 == p.vs2 &&
          p.k == p.v;
 }
@@ -1824,6 +2160,7 @@ int mla_blocks_per_cu(const AttnParams& p) {
                                         : reinterpret_cast<const void*>(&mla_mid_kernel<false, 2>))
                   : R <= 4 * kRW ? (fp8 ? reinterpret_cast<const void*>(&mla_mid_kernel<true, 4>)
                                         : reinterpret_cast<const void*>(&mla_mid_kernel<false, 4>))
+                  : p.q_dtype == FP8 ? reinterpret_cast<const void*>(&mla_rows8_kernel)
                                  : (fp8 ? reinterpret_cast<const void*>(&mla_rows_kernel<true>)
                                         : reinterpret_cast<const void*>(&mla_rows_kernel<false>));
   int n = 0;

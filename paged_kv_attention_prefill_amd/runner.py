@@ -71,7 +71,7 @@ def run(d: DeviceWorkload, *, num_kv_splits: Optional[int] = None, merge: bool =
     kvdt = w.kv_dtype
     hint = int(w.kv_lens.max()) if max_kv_len is None else max_kv_len
     common = dict(head_dim_vo=w.head_dim_vo, kv_dtype=kvdt, k_scale=w.k_scale,
-                  v_scale=w.v_scale, max_kv_len=hint, flags=flags, stream=stream,
+                  v_scale=w.v_scale, q_scale=w.q_scale, max_kv_len=hint, flags=flags, stream=stream,
                   sm_scale=w.sm_scale, causal=w.causal, kv_broadcast=w.kv_broadcast)
     res = {}
     if d.is_decode and not force_prefill:
@@ -82,7 +82,9 @@ def run(d: DeviceWorkload, *, num_kv_splits: Optional[int] = None, merge: bool =
         if S > 1:
             res["po"], res["plse"], res["pmx"] = o, lse, mx
             if merge:
-                odt = out_dtype or (d.q.dtype if d.q.dtype != torch.float32 else torch.float32)
+                odt = out_dtype or (d.q.dtype if d.q.dtype in (torch.float16, torch.bfloat16)
+                                    else torch.bfloat16 if d.q.dtype != torch.float32
+                                    else torch.float32)
                 o, lse = B.merge_states(o, lse, out_dtype=odt, stream=stream)
                 mx = None
         res["o"], res["lse"], res["mx"] = o, lse, mx
@@ -116,7 +118,8 @@ class Step:
         S = w.num_kv_splits
         self.num_states = S
         common = dict(head_dim_vo=w.head_dim_vo, kv_dtype=w.kv_dtype, k_scale=w.k_scale,
-                      v_scale=w.v_scale, max_kv_len=int(w.kv_lens.max()), flags=flags,
+                      v_scale=w.v_scale, q_scale=w.q_scale, max_kv_len=int(w.kv_lens.max()),
+                      flags=flags,
                       stream=self.stream, sm_scale=w.sm_scale, causal=w.causal,
                       kv_broadcast=w.kv_broadcast)
         self.merge = None
@@ -126,7 +129,7 @@ class Step:
                                          num_kv_splits=S, **common)
             if S > 1:
                 po, pl = self.attn.outputs["o"], self.attn.outputs["lse"]
-                odt = d.q.dtype
+                odt = d.q.dtype if d.q.dtype != torch.float8_e4m3fn else torch.bfloat16
                 self.final_o = torch.empty(po.shape[1:], dtype=odt, device=po.device)
                 self.final_lse = torch.empty(pl.shape[1:], dtype=torch.float32, device=po.device)
                 lib = B.load_library()

@@ -94,6 +94,7 @@ class Workload:
     num_kv_splits: int = 1
     k_layout: str = "NHD"
     v_layout: str = "NHD"
+    q_scale: float = 1.0          # real Q = q_scale * stored Q (fp8 queries; 1 otherwise)
     meta: dict = field(default_factory=dict)
 
     @property
@@ -128,7 +129,8 @@ class Workload:
                     kv_batches=self.num_kv_batches, sum_kv_len=int(self.kv_lens.sum()),
                     pages=int(self.kv_indptr[-1]), pool_pages=self.num_pool_pages,
                     broadcast=self.kv_broadcast, causal=self.causal, splits=self.num_kv_splits,
-                    k_scale=self.k_scale, v_scale=self.v_scale, sm_scale=self.sm_scale)
+                    k_scale=self.k_scale, v_scale=self.v_scale, q_scale=self.q_scale,
+                    sm_scale=self.sm_scale)
 
 
 def _layout_array(x: np.ndarray, layout: str):
@@ -201,6 +203,11 @@ def build(rng: np.random.Generator, seed: int, name: str, *, q_lens: Sequence[in
             v_scale = float(np.float32(np.abs(v32).max()) / np.float32(FP8_MAX))
             v32 = v32 / np.float32(v_scale)
 
+    q_scale = 1.0
+    if q_dtype == DT_FP8:
+        # fp8 queries: one per-tensor scale, s = amax/448 (as for the caches)
+        q_scale = float(np.float32(np.abs(q32).max()) / np.float32(FP8_MAX))
+        q32 = q32 / np.float32(q_scale)
     q = round_to_storage(q32, q_dtype)
     del q32
     k = round_to_storage(k32, kv_dtype).reshape(k32.shape)
@@ -241,7 +248,7 @@ def build(rng: np.random.Generator, seed: int, name: str, *, q_lens: Sequence[in
                     kv_indptr=kv_indptr, kv_indices=kv_indices, kv_last_page_len=last,
                     kv_lens=kv_lens, num_pool_pages=pool, kv_broadcast=kv_broadcast,
                     causal=causal, sm_scale=float(sm_scale), num_kv_splits=num_kv_splits,
-                    k_layout=k_layout, v_layout=v_layout)
+                    k_layout=k_layout, v_layout=v_layout, q_scale=q_scale)
 
 
 # ---------------------------------------------------------------------------
@@ -298,20 +305,23 @@ C4_QLENS = (1, 2, 4)
 
 
 def config4(num_heads: int = 16, q_len: int = 1, kv_dtype: int = DT_BF16, batch: int = 32,
-            min_len: int = 4096, max_len: int = 32768, poison: bool = True, **kw) -> Workload:
+            min_len: int = 4096, max_len: int = 32768, poison: bool = True,
+            q_dtype: int = DT_BF16, **kw) -> Workload:
     """MLA latent decode: q_len in {1,2,4} folded into heads, 16 or 128 query
     heads, one shared KV head of 576 dims (V = first 512), page 64, KV lengths
     uniform in [4096, 32768], bf16 or fp8-e4m3 KV with a per-tensor scale,
     scale 1/sqrt(192).  One draw per (heads, q_len); the fp8 variant is
-    quantised from the same fp32 values."""
+    quantised from the same fp32 values.  ``q_dtype=DT_FP8`` (with fp8 KV):
+    the queries are fp8-e4m3 codes with their own per-tensor scale too."""
     sub = C4_HEADS.index(num_heads) * len(C4_QLENS) + C4_QLENS.index(q_len)
     seed = 4000 + sub
     rng = np.random.default_rng(seed)
     kv_lens = rng.integers(min_len, max_len, endpoint=True, size=batch)
-    return build(rng, seed, f"c4_mla_decode_h{num_heads}_q{q_len}_{DT_NAMES[kv_dtype]}",
+    qtag = "_fp8q" if q_dtype == DT_FP8 else ""
+    return build(rng, seed, f"c4_mla_decode_h{num_heads}_q{q_len}_{DT_NAMES[kv_dtype]}{qtag}",
                  q_lens=[q_len] * batch, kv_lens=kv_lens, num_qo_heads=num_heads,
                  num_kv_heads=1, head_dim_qk=576, head_dim_vo=512, page_size=64,
-                 q_dtype=DT_BF16, kv_dtype=kv_dtype, shared_kv=True,
+                 q_dtype=q_dtype, kv_dtype=kv_dtype, shared_kv=True,
                  causal=kw.pop("causal", True), sm_scale=1.0 / math.sqrt(192.0),
                  poison=poison, **kw)
 

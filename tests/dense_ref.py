@@ -28,7 +28,7 @@ def dense_attention(w: W.Workload, split=None, causal=None):
     [floor(c*n/S), floor((c+1)*n/S)) of its KV batch.
     """
     caus = w.causal if causal is None else causal
-    q = decoded(w.q, w.q_dtype).reshape(w.total_q, w.num_qo_heads, w.head_dim_qk)
+    q = decoded(w.q, w.q_dtype).reshape(w.total_q, w.num_qo_heads, w.head_dim_qk) * w.q_scale
     kflat = decoded(w.k, w.kv_dtype)
     kc = logical_cache(kflat, w.k_stride, w.num_pool_pages, w.page_size, w.num_kv_heads,
                        w.head_dim_qk)

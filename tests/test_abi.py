@@ -27,7 +27,7 @@ def test_exports_every_header_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pa_abi_version() == 1
+    assert lib.pa_abi_version() == 2
     for st in range(0, -8, -1):
         assert B.status_string(st) != "unknown status"
     assert B.status_string(-99) == "unknown status"
@@ -109,7 +109,7 @@ DECODE_BAD = [
     ("num_kv_splits", 2000, -2), ("kv.max_kv_len_hint", -1, -2), ("kv.k_stride[1]", -8, -2),
     ("sm_scale", float("nan"), -2), ("kv.k_scale", float("inf"), -2),
     ("q_dtype", 7, -3), ("kv.kv_dtype", -1, -3), ("o_dtype", B.PA_FP8_E4M3, -3),
-    ("q_dtype", B.PA_FP8_E4M3, -3),
+    ("q_dtype", B.PA_FP8_E4M3, -5),
     ("kv.head_dim_qk", 96, -5), ("kv.head_dim_vo", 64, -5), ("q_dtype", B.PA_F32, -5),
     ("q", FAKE + 8, -4), ("kv.k", FAKE + 2, -4), ("o", FAKE + 4, -4),
     ("kv.v_stride[2]", 132, -4),

@@ -46,11 +46,12 @@ def run_and_check(w, label, flags=0, expect_plan=None, **kw):
                       None if res.get("mx") is None else to64(res["mx"]), mx, label=label)
 
 
-def mla(seed, heads, q_len, kv_lens, page_size=64, dt=W.DT_BF16, gain=None, **kw):
+def mla(seed, heads, q_len, kv_lens, page_size=64, dt=W.DT_BF16, gain=None, q_dtype=W.DT_BF16,
+        **kw):
     rng = np.random.default_rng(seed)
     return W.build(rng, seed, f"mla h{heads} q{q_len} p{page_size}", q_lens=[q_len] * len(kv_lens),
                    kv_lens=kv_lens, num_qo_heads=heads, num_kv_heads=1, head_dim_qk=576,
-                   head_dim_vo=512, page_size=page_size, q_dtype=W.DT_BF16, kv_dtype=dt,
+                   head_dim_vo=512, page_size=page_size, q_dtype=q_dtype, kv_dtype=dt,
                    shared_kv=True, causal=True, sm_scale=MLA_SCALE,
                    k_late_gain=None if gain is None else (gain, 512, 576), **kw)
 
@@ -77,6 +78,12 @@ def jump_cases():
         "mla_rows_fp8": lambda g: mla(406, 128, 1, [5, 1000, 3000], dt=W.DT_FP8, gain=g),
         "mla_rows2_bf16": lambda g: mla(407, 128, 2, [5, 1500], gain=g),
         "mla_rows2_fp8": lambda g: mla(408, 128, 2, [5, 1500], dt=W.DT_FP8, gain=g),
+        "mla_rows_fp8q": lambda g: mla(409, 128, 1, [5, 1000, 3000], dt=W.DT_FP8, gain=g,
+                                       q_dtype=W.DT_FP8),
+        "mla_rows4_fp8q": lambda g: mla(410, 128, 4, [5, 1500], dt=W.DT_FP8, gain=g,
+                                        q_dtype=W.DT_FP8),
+        "mla_narrow_fp8q": lambda g: mla(411, 16, 1, [1, 700, 3000, 4100], dt=W.DT_FP8, gain=g,
+                                         q_dtype=W.DT_FP8),
     }
 
 
@@ -173,6 +180,18 @@ def test_prefill_over_fp8_cache():
                 num_qo_heads=16, num_kv_heads=4, head_dim_qk=128, head_dim_vo=128, page_size=16,
                 q_dtype=W.DT_BF16, kv_dtype=W.DT_FP8, causal=True, uniform_q_len=False)
     run_and_check(w, "ragged causal prefill, bf16 Q x fp8 KV", expect_plan="generic")
+
+
+def test_fp8_queries_generic_kernel():
+    """fp8 queries outside the MLA kernels (GQA shape, and MLA forced onto the
+    generic kernel): the generic kernel decodes the codes and applies q_scale."""
+    rng = np.random.default_rng(435)
+    w = W.build(rng, 435, "fp8q gqa", q_lens=[1] * 4, kv_lens=[1, 90, 700, 1300],
+                num_qo_heads=16, num_kv_heads=4, head_dim_qk=128, head_dim_vo=128, page_size=16,
+                q_dtype=W.DT_FP8, kv_dtype=W.DT_FP8)
+    run_and_check(w, "fp8 Q x fp8 KV, d128", expect_plan="generic")
+    w2 = mla(436, 128, 2, [1, 333, 900], dt=W.DT_FP8, q_dtype=W.DT_FP8)
+    run_and_check(w2, "MLA fp8 Q forced generic", flags=B.FLAG_FORCE_GENERIC, expect_plan="generic")
 
 
 def test_mla_forced_generic():

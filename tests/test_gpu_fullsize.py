@@ -44,6 +44,14 @@ def test_c5_broadcast_split_decode_full():
     run_sampled(W.config5(), "c5 full", n=96)
 
 
+@pytest.mark.parametrize("ql", W.C4_QLENS)
+@pytest.mark.parametrize("h", W.C4_HEADS)
+def test_c4_mla_decode_fp8_queries_full(h, ql):
+    """fp8 queries over the fp8 cache, every (heads, q_len) at full size."""
+    run_sampled(W.config4(num_heads=h, q_len=ql, kv_dtype=W.DT_FP8, q_dtype=W.DT_FP8),
+                f"c4 full h{h} q{ql} fp8 KV fp8 Q", n=96)
+
+
 @pytest.mark.parametrize("dt", [W.DT_BF16, W.DT_FP8])
 @pytest.mark.parametrize("ql", W.C4_QLENS)
 @pytest.mark.parametrize("h", W.C4_HEADS)

@@ -101,6 +101,47 @@ def test_parity_mla_small(h, ql, dt):
     run_and_check(c4_small(h, ql, dt), label)
 
 
+@pytest.mark.parametrize("h", W.C4_HEADS)
+@pytest.mark.parametrize("ql", W.C4_QLENS)
+def test_parity_mla_fp8_queries(h, ql):
+    """fp8 queries over an fp8 cache: Q.K on the fp8 matrix cores for more than
+    64 rows per request; the narrow and mid kernels widen the query codes."""
+    w = W.config4(num_heads=h, q_len=ql, kv_dtype=W.DT_FP8, q_dtype=W.DT_FP8, batch=3, min_len=1,
+                  max_len=900)
+    label = f"c4 h{h} q{ql} fp8 KV, fp8 Q"
+    print(label, flush=True)
+    step = R.prepare(R.upload(w))
+    assert step.attention_kernel_name == "mla_decode_mfma_fp8q", step.attention_kernel_name
+    run_and_check(w, label)
+
+
+@pytest.mark.parametrize("heads,q_len,page_size", [(128, 1, 24), (128, 2, 1), (96, 2, 64),
+                                                   (144, 1, 7), (128, 4, 96)])
+def test_mla_fp8_queries_row_tiles_and_page_sizes(heads, q_len, page_size):
+    """The fp8-query many-rows kernel over partial and multiple row tiles and
+    page sizes that do not hold whole tiles, with and without internal splits."""
+    label = f"MLA fp8 Q h{heads} q{q_len} page {page_size}"
+    print(label, flush=True)
+    w = mla_build(1100 + heads + page_size + q_len, heads, q_len, [1, 45, 700, 1333, 2100], page_size,
+                  dt=W.DT_FP8, q_dtype=W.DT_FP8)
+    run_and_check(w, label)
+    run_and_check(w, label + " unsplit", flags=B.FLAG_NO_INTERNAL_SPLIT)
+
+
+def test_mla_fp8_queries_explicit_splits():
+    w = mla_build(1191, 128, 2, [0, 5, 640, 999], 64, dt=W.DT_FP8, q_dtype=W.DT_FP8)
+    d = R.upload(w)
+    S = 3
+    res = R.run(d, num_kv_splits=S)
+    torch.cuda.synchronize()
+    po, pl, pm = OR.attention(w, num_kv_splits=S)
+    for c in range(S):
+        check_rows(w, to64(res["po"][c]), to64(res["plse"][c]), po[c], pl[c],
+                   to64(res["pmx"][c]), pm[c], label=f"MLA fp8 Q partial {c}")
+    o, lse, _ = OR.attention(w, num_kv_splits=1)
+    check_rows(w, to64(res["o"]), to64(res["lse"]), o, lse, label="MLA fp8 Q merged")
+
+
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5"])
 def test_parity_generic_kernel(name):
     print(f"generic {name}", flush=True)
@@ -253,11 +294,11 @@ def test_causal_rows_that_see_nothing():
     run_and_check(w2, "MLA fp8 empty causal rows")
 
 
-def mla_build(seed, heads, q_len, kv_lens, page_size, dt=W.DT_BF16, **kw):
+def mla_build(seed, heads, q_len, kv_lens, page_size, dt=W.DT_BF16, q_dtype=W.DT_BF16, **kw):
     rng = np.random.default_rng(seed)
     return W.build(rng, seed, f"mla h{heads} q{q_len} p{page_size}", q_lens=[q_len] * len(kv_lens),
                    kv_lens=kv_lens, num_qo_heads=heads, num_kv_heads=1, head_dim_qk=576,
-                   head_dim_vo=512, page_size=page_size, q_dtype=W.DT_BF16, kv_dtype=dt,
+                   head_dim_vo=512, page_size=page_size, q_dtype=q_dtype, kv_dtype=dt,
                    shared_kv=True, causal=True, sm_scale=1.0 / np.sqrt(192.0), **kw)
 
 

@@ -42,6 +42,8 @@ def small_cases():
         "c4_small_bf16": lambda: W.config4(num_heads=16, q_len=2, batch=2, min_len=1, max_len=150),
         "c4_small_fp8": lambda: W.config4(num_heads=16, q_len=4, kv_dtype=W.DT_FP8, batch=3,
                                           min_len=1, max_len=150),
+        "c4_small_fp8q": lambda: W.config4(num_heads=16, q_len=2, kv_dtype=W.DT_FP8,
+                                           q_dtype=W.DT_FP8, batch=3, min_len=1, max_len=120),
         "c5_small": lambda: W.config5(num_queries=3, kv_len=300, num_kv_splits=4),
         "sparse_mla_bf16": lambda: W.config_sparse(num_heads=16, kv_lens=[1, 40, 129], pool_factor=3),
         "sparse_mla_fp8": lambda: W.config_sparse(num_heads=8, kv_dtype=W.DT_FP8, kv_lens=[3, 77],

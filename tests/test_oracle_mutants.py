@@ -19,6 +19,7 @@ SRC = os.path.join(os.path.dirname(OR.__file__), "oracle.c")
 
 MUTANTS = {
     "drop_k_scale": ("(k_scale * elem(k, kv_dtype, kbase + d))", "(elem(k, kv_dtype, kbase + d))"),
+    "drop_q_scale": ("(q_scale * elem(q, q_dtype, qoff + d))", "(elem(q, q_dtype, qoff + d))"),
     "drop_v_scale": ("(v_scale * elem(v, kv_dtype, vbase + d))", "(elem(v, kv_dtype, vbase + d))"),
     "drop_sm_scale": ("s[j - j0] = sm_scale * acc;", "s[j - j0] = acc;"),
     "gqa_map_modulo": ("const int g = h / group;", "const int g = h % num_kv_heads;"),

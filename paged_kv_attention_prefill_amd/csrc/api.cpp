@@ -195,6 +195,8 @@ struct Plan {
   int ws_rows = 16;           // workspace row slots per (batch, KV head, chunk)
   int bal_blocks = 0;         // balanced split over this many workgroups (0: none)
   int bal_unit = 0;           // its unit of work in KV tokens
+  int bal_rt = 1;             // row tiles per (batch, KV head) item of the balanced split
+  int bal_xcd = 0;            // consecutive shares on one XCD
   size_t workspace = 0;
   const char* name = "generic";
 };
@@ -263,9 +265,9 @@ int device_cus() {
 }
 
 // Workspace of a balanced split: partial states in slots item + workgroup, then
-// the first/last workgroup of every item.
-size_t balanced_workspace(const AttnParams& p, int blocks, int ws_rows) {
-  const int64_t items = (int64_t)p.batch * p.num_kv_heads;
+// the first/last workgroup of every item ((batch, KV head, row tile)).
+size_t balanced_workspace(const AttnParams& p, int blocks, int ws_rows, int bal_rt) {
+  const int64_t items = (int64_t)p.batch * p.num_kv_heads * bal_rt;
   const size_t rows = (size_t)pa::bal_slots(items, blocks) * ws_rows;
   return align256(rows * p.dvo * 4) + 2 * align256(rows * 4) + align256((size_t)items * 8);
 }
@@ -318,7 +320,7 @@ Plan make_plan(const AttnParams& p, uint32_t flags) {
     if (decode_chunk_tokens(p, flags) > 0) {
       pl.bal_unit = 32;
       pl.bal_blocks = gqa_occupancy(p, same) * device_cus();
-      pl.workspace = balanced_workspace(p, pl.bal_blocks, 16);
+      pl.workspace = balanced_workspace(p, pl.bal_blocks, 16, 1);
     }
     return pl;
   }
@@ -333,12 +335,18 @@ Plan make_plan(const AttnParams& p, uint32_t flags) {
               : p.kv_dtype == PA_FP8_E4M3 ? "mla_decode_mfma_fp8"
                                           : "mla_decode_mfma";
     const int ct = mla_chunk_tokens(p, flags);
-    if (ct > 0 && pa::mla_balanced_ok(p)) {
-      // one row tile per request: balanced split over one wave of workgroups
+    if (ct > 0) {
+      // balanced split over one wave of workgroups; items are (request, KV head,
+      // 128-row tile), and with several row tiles the consecutive shares (the
+      // row tiles of one token range) run on one XCD, sharing its L2
+      const int R = p.q_len * p.group;
+      const int rt = pa::mla_rows_per_tile(p);
+      pl.bal_rt = (R + rt - 1) / rt;
       pl.bal_unit = 32;
       pl.bal_blocks = mla_occupancy(p) * device_cus();
-      pl.ws_rows = p.q_len * p.group;
-      pl.workspace = balanced_workspace(p, pl.bal_blocks, pl.ws_rows);
+      pl.bal_xcd = pl.bal_rt > 1 && pl.bal_blocks % 8 == 0;
+      pl.ws_rows = pl.bal_rt > 1 ? rt : R;
+      pl.workspace = balanced_workspace(p, pl.bal_blocks, pl.ws_rows, pl.bal_rt);
       return pl;
     }
     pl.chunk_tokens = ct;
@@ -373,8 +381,11 @@ int run_plan(const Plan& pl, AttnParams p, void* ws, size_t ws_bytes, void* cons
   p.ws_rows = pl.ws_rows;
   p.bal_blocks = pl.bal_blocks;
   p.bal_unit = pl.bal_unit;
+  p.bal_rt = pl.bal_rt;
+  p.bal_rows = pl.ws_rows;
+  p.bal_xcd = pl.bal_xcd;
   if (pl.bal_blocks > 0) {
-    const int64_t items = (int64_t)p.batch * p.num_kv_heads;
+    const int64_t items = pa::bal_items(p);
     const size_t rows = (size_t)pa::bal_slots(items, pl.bal_blocks) * pl.ws_rows;
     char* w = static_cast<char*>(ws);
     p.ws_o = reinterpret_cast<float*>(w);
@@ -412,7 +423,7 @@ int run_plan(const Plan& pl, AttnParams p, void* ws, size_t ws_bytes, void* cons
   if (pl.chunk_tokens > 0 || pl.bal_blocks > 0) {
     // many states per row (few long items over many workgroups): split each
     // row's states over the lane groups of a workgroup
-    const int64_t items = (int64_t)p.batch * p.num_kv_heads;
+    const int64_t items = (int64_t)p.batch * p.num_kv_heads * pl.bal_rt;
     const bool wide = (pl.bal_blocks > 0 && pl.bal_blocks >= 32 * items) || pl.max_chunks >= 32;
     e = pa::launch_chunk_merge(p, wide, stream);
   }

@@ -2,9 +2,11 @@
 // pages only fix that split partial states merge through their LSE, which is how
 // the pieces below are recombined).
 //
-// The work is the sequence of items (query batch b, KV head g), b-major; item
-// (b, g) has nu(b) = max(1, ceil(L_b / unit)) units of `unit` KV tokens (an empty
-// KV batch still has one unit, so that some workgroup writes its empty result).
+// The work is the sequence of items (query batch b, KV head g, row tile), b-major
+// (row tiles only for MLA with several 128-row tiles per request; the cursor's g
+// runs over KV heads x row tiles); item (b, g) has nu(b) = max(1, ceil(L_b /
+// unit)) units of `unit` KV tokens (an empty KV batch still has one unit, so
+// that some workgroup writes its empty result).
 // With T units in total and NB workgroups (as many as are co-resident on the
 // device), workgroup i takes units [i Qc, min(T, (i+1) Qc)), Qc = ceil(T / NB):
 // every workgroup streams the same number of KV tokens (up to one unit), so all
@@ -57,20 +59,20 @@ struct BalCursor {
   int64_t pos;   // global unit index of the segment's start
   int64_t left;  // units left for this workgroup, current segment included
   int64_t Qc;    // units per workgroup
-  int i;         // this workgroup
+  int i;         // this workgroup's share
 
   __device__ __forceinline__ int j0(const AttnParams& p) const { return min(L, u * p.bal_unit); }
   __device__ __forceinline__ int j1(const AttnParams& p) const { return min(L, (u + take) * p.bal_unit); }
   __device__ __forceinline__ bool whole() const { return u == 0 && take == nu; }
   __device__ __forceinline__ int64_t slot(const AttnParams& p) const {
-    return (int64_t)(b * p.num_kv_heads + g) + i;
+    return (int64_t)(b * p.num_kv_heads * p.bal_rt + g) + i;
   }
 
   // the item's first workgroup records the item's span for the merge
   __device__ __forceinline__ void open(const AttnParams& p) {
     take = uni(left < nu - u ? (int)left : nu - u);
     if (u == 0 && threadIdx.x == 0) {
-      const int item = b * p.num_kv_heads + g;
+      const int item = b * p.num_kv_heads * p.bal_rt + g;
       p.ws_seg[2 * item] = i;
       p.ws_seg[2 * item + 1] = (int)((pos + nu - 1) / Qc);
     }
@@ -78,8 +80,10 @@ struct BalCursor {
 
   __device__ __forceinline__ bool start(const AttnParams& p, int wg) {
     const int lane = threadIdx.x & 63;
-    const int B = p.batch, H = p.num_kv_heads, unit = p.bal_unit;
-    i = wg;
+    const int B = p.batch, H = p.num_kv_heads * p.bal_rt, unit = p.bal_unit;
+    // workgroups are dealt round-robin to the 8 XCDs: with bal_xcd, the shares
+    // of one XCD are consecutive
+    i = p.bal_xcd ? (wg % 8) * (p.bal_blocks / 8) + wg / 8 : wg;
     int64_t tot = 0;
     for (int base = 0; base < B; base += 64) {
       const int bb = base + lane;
@@ -123,7 +127,7 @@ struct BalCursor {
     u += take;
     if (u == nu) {
       u = 0;
-      if (++g == p.num_kv_heads) {
+      if (++g == p.num_kv_heads * p.bal_rt) {
         g = 0;
         ++b;
         L = uni(kv_len_of(p, b));

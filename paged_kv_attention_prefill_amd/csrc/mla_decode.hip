@@ -787,13 +787,13 @@ __device__ __forceinline__ void mla_rows_range(const AttnParams& p, int b, int g
       // it; the first one also says every wave is done with the previous tile)
 #define PA_MLA_STEP(K, CUR, NEXT3)                                                            \
   {                                                                                         \
-    __builtin_amdgcn_s_waitcnt(kWaitImm); /* tile K's direct loads are done */              \
-    __syncthreads();                                                                         \
+    __builtin_amdgcn_s_waitcnt(kWaitImm); /* this wave's loads of tile K are done */        \
+    lds_barrier(); /* every wave's; no wait for the tiles behind it */                      \
     dma(NEXT3, tile_at((K) + 3));                                                           \
     const uint8_t* src = CUR;                                                               \
     if constexpr (FP8) {                                                                    \
       convert_tile(CUR, s_wide, tid);                                                       \
-      __syncthreads();                                                                       \
+      lds_barrier();                                                                         \
       src = s_wide;                                                                         \
     }                                                                                       \
     const int jb = ws + (K) * kTK2;                                                         \
@@ -822,7 +822,8 @@ __device__ __forceinline__ void mla_rows_range(const AttnParams& p, int b, int g
   const float scale = empty ? 0.f : p.v_scale / ltot;
   const int64_t rid = (int64_t)(b * p.q_len + row / p.group) * p.num_qo_heads + (int64_t)g * p.group +
                       row % p.group;
-  const int64_t wrow = wslot * p.ws_rows + row;
+  // workspace rows: per request (chunks), or per row tile (balanced split with row tiles)
+  const int64_t wrow = wslot * p.ws_rows + (p.bal_rt > 1 ? row - row0 : row);
 #pragma unroll
   for (int d = 0; d < NDT; ++d) {
     const int dim = 16 * d + 4 * lg;
@@ -872,8 +873,8 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_rows_kernel(AttnParams p, in
     BalCursor cur;
     if (!cur.start(p, blockIdx.x)) return;
     do {
-      mla_rows_range<FP8>(p, cur.b, cur.g, 0, cur.L, cur.j0(p), cur.j1(p), !cur.whole(), cur.slot(p), 0,
-                          s_kv0, s_kv1, s_kv2, s_kv3, s_wide, s_pages);
+      mla_rows_range<FP8>(p, cur.b, cur.g / p.bal_rt, cur.g % p.bal_rt, cur.L, cur.j0(p), cur.j1(p),
+                          !cur.whole(), cur.slot(p), 0, s_kv0, s_kv1, s_kv2, s_kv3, s_wide, s_pages);
     } while (cur.next(p));
     return;
   }
@@ -933,24 +934,25 @@ __device__ __forceinline__ void mla_rows8_tile(const uint8_t* kv, int jb, int li
   // (e = 0, 1), i.e. slot 8 ks + 4 (lg >> 1) + ((2 (lg & 1) + e) ^ swzq(row)):
   // four per-lane bases (st, e), the k-step adding 128 ks bytes; k-step 4 has
   // pieces 32..35 only (lane groups 0 and 1)
+  // (addresses stay pointers into the stage, so the compiler's wait counting
+  // sees which stage a read touches and does not wait for the loads in flight
+  // into the other stages)
   const int sw0 = swzq(l16);  // block 1 rows: sw0 ^ 2
-  const uint32_t kvb = lds_off(kv);
-  uint32_t kb[2][2];  // LDS byte addresses
+  int kb[2][2];  // byte offsets in the stage
 #pragma unroll
   for (int stb = 0; stb < 2; ++stb)
 #pragma unroll
     for (int e = 0; e < 2; ++e)
-      kb[stb][e] = kvb + (16 * stb + l16) * kPitch + 64 * (lg >> 1) +
-                   16 * ((2 * (lg & 1) + e) ^ (sw0 ^ (2 * stb)));
+      kb[stb][e] = (16 * stb + l16) * kPitch + 64 * (lg >> 1) + 16 * ((2 * (lg & 1) + e) ^ (sw0 ^ (2 * stb)));
   // k-step 4 (dims 512..575): lane groups 2 and 3 would address pieces 36..39,
   // past the row; they read pieces 32..35 of their row instead (in bounds, a
   // plain read for every lane) and their operand is zeroed by a select
-  const uint32_t tail_back = lg >= 2 ? 64u : 0u;
+  const int tail_back = lg >= 2 ? 64 : 0;
   auto kfrag = [&](int f) __attribute__((always_inline)) {
     const int ks = f >> 1, stb = f & 1;
-    const uint32_t back = ks == kKS8 - 1 ? tail_back : 0u;
-    const i32x4_t lo = *(const PA_LDS i32x4_t*)(uintptr_t)(kb[stb][0] + 128 * ks - back);
-    const i32x4_t hi = *(const PA_LDS i32x4_t*)(uintptr_t)(kb[stb][1] + 128 * ks - back);
+    const int back = ks == kKS8 - 1 ? tail_back : 0;
+    const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(kv + kb[stb][0] + 128 * ks - back);
+    const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(kv + kb[stb][1] + 128 * ks - back);
     return i32x8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   };
   constexpr int kPF = 2;  // K operands in flight
@@ -1013,11 +1015,11 @@ __device__ __forceinline__ void mla_rows8_tile(const uint8_t* kv, int jb, int li
   const int tsw = swzq(trow);
   // dim block d sits at slot 4 (d >> 2) + ((d & 3) ^ tsw): four per-lane bases
   // (d mod 4), the block group adding 64 (d >> 2) bytes
-  uint32_t vb[4];
+  int vb[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) vb[u] = kvb + trow * kPitch + 8 * h + 16 * (u ^ tsw);
+  for (int u = 0; u < 4; ++u) vb[u] = trow * kPitch + 8 * h + 16 * (u ^ tsw);
   auto vfrag = [&](int d) __attribute__((always_inline)) {
-    return __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2_t*)(uintptr_t)(vb[d & 3] + 64 * (d >> 2)));
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2_t*)(kv + vb[d & 3] + 64 * (d >> 2)));
   };
   constexpr int kPV = 4;  // V^T operands in flight
   i32x2_t vring[kPV];
@@ -1115,8 +1117,8 @@ __device__ __forceinline__ void mla_rows8_range(const AttnParams& p, int b, int 
       dma(s_kv2, tile_at(2));
 #define PA_MLA8_STEP(K, CUR, NEXT3)                                                             \
   {                                                                                           \
-    __builtin_amdgcn_s_waitcnt(kWaitImm); /* tile K's direct loads are done */                \
-    __syncthreads();                                                                           \
+    __builtin_amdgcn_s_waitcnt(kWaitImm); /* this wave's loads of tile K are done */          \
+    lds_barrier(); /* every wave's; no wait for the tiles behind it */                        \
     dma(NEXT3, tile_at((K) + 3));                                                             \
     const int jb = ws + (K) * kTK2;                                                           \
     if (wave_live)                                                                            \
@@ -1144,7 +1146,8 @@ __device__ __forceinline__ void mla_rows8_range(const AttnParams& p, int b, int 
   const float scale = empty ? 0.f : p.v_scale / ltot;
   const int64_t rid = (int64_t)(b * p.q_len + row / p.group) * p.num_qo_heads + (int64_t)g * p.group +
                       row % p.group;
-  const int64_t wrow = wslot * p.ws_rows + row;
+  // workspace rows: per request (chunks), or per row tile (balanced split with row tiles)
+  const int64_t wrow = wslot * p.ws_rows + (p.bal_rt > 1 ? row - row0 : row);
 #pragma unroll
   for (int d = 0; d < NDT; ++d) {
     const int dim = 16 * d + 4 * lg;
@@ -1186,8 +1189,8 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_rows8_kernel(AttnParams p, i
     BalCursor cur;
     if (!cur.start(p, blockIdx.x)) return;
     do {
-      mla_rows8_range(p, cur.b, cur.g, 0, cur.L, cur.j0(p), cur.j1(p), !cur.whole(), cur.slot(p), 0,
-                      s_kv0, s_kv1, s_kv2, s_kv3, s_pages);
+      mla_rows8_range(p, cur.b, cur.g / p.bal_rt, cur.g % p.bal_rt, cur.L, cur.j0(p), cur.j1(p),
+                      !cur.whole(), cur.slot(p), 0, s_kv0, s_kv1, s_kv2, s_kv3, s_pages);
     } while (cur.next(p));
     return;
   }
@@ -2149,7 +2152,6 @@ bool mla_decode_supported(const AttnParams& p) {
 
 int mla_rows_per_tile(const AttnParams&) { return kRT2; }
 
-bool mla_balanced_ok(const AttnParams& p) { return mla_rows_path(p) && p.q_len * p.group <= kRT2; }
 
 int mla_blocks_per_cu(const AttnParams& p) {
   const bool fp8 = p.kv_dtype == FP8;

@@ -52,11 +52,21 @@ struct AttnParams {
   // ws_seg[2 item + 1] receive the item's first and last workgroup
   int32_t bal_blocks;
   int32_t bal_unit;
-  int32_t* ws_seg;          // [B * Hkv][2]
+  int32_t* ws_seg;          // [B * Hkv * bal_rt][2]
+  // items of the balanced split are (batch, KV head, row tile): bal_rt row tiles
+  // of bal_rows rows per (batch, KV head) (1 and all rows, except for MLA with
+  // more than one 128-row tile); a slot holds the rows of one row tile
+  int32_t bal_rt;
+  int32_t bal_rows;
+  // 1: workgroup w takes share (w % 8) * (bal_blocks / 8) + w / 8, so that
+  // consecutive shares (the row tiles of one token range) run on one XCD
+  int32_t bal_xcd;
 };
 
 // Workspace slots of a balanced split: item + workgroup < items + blocks - 1.
 inline int64_t bal_slots(int64_t items, int blocks) { return items + blocks - 1; }
+// Items of a balanced split: (batch, KV head, row tile).
+inline int64_t bal_items(const AttnParams& p) { return (int64_t)p.batch * p.num_kv_heads * p.bal_rt; }
 
 // Number of chunks of a KV batch of L tokens under internal chunking.
 __host__ __device__ inline int num_chunks(int L, int chunk_tokens, int max_chunks) {
@@ -78,7 +88,6 @@ int gqa_decode_blocks_per_cu(const AttnParams& p, bool same_strides);
 bool mla_decode_supported(const AttnParams& p);
 bool mla_rows_path(const AttnParams& p);
 int mla_rows_per_tile(const AttnParams& p);
-bool mla_balanced_ok(const AttnParams& p);
 int mla_blocks_per_cu(const AttnParams& p);
 hipError_t launch_mla_decode(const AttnParams& p, hipStream_t stream);
 bool flash_attn_supported(const AttnParams& p);

@@ -263,12 +263,12 @@ def test_noalloc_rejects_oversized_workspace(lib):
     text = open(B.HEADER).read()
     assert "#define PA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)" in text
     assert B.NOALLOC_SCRATCH_BYTES == 128 << 20
-    # MLA, 32 requests x 512 rows, KV up to 32768 tokens: fixed chunks of 4096
-    # tokens, 8 chunks x 512 rows x 512 fp32 dims per request = 268 MB
-    a = mla_decode_args(heads=128)
-    a.batch, a.q_len, a.causal = 32, 4, 1
-    a.kv.num_kv_batches = 32
-    a.kv.max_kv_len_hint = 32768
+    # GQA decode of 20000 requests x 8 KV heads, KV up to 8192 tokens: the
+    # balanced split's partial-state slots (items + workgroups) x 16 rows x 128
+    # fp32 dims exceed 1 GB
+    a = good_decode()
+    a.batch = 20000
+    a.kv.num_kv_batches = 20000
     st, n = dsize(lib, a)
     assert st == 0 and n > B.NOALLOC_SCRATCH_BYTES
     assert lib.paged_attn_decode_noalloc(ctypes.byref(a), None) == -6

@@ -449,3 +449,27 @@ def test_few_long_requests_wide_merge(name):
     again = R.run(R.upload(w))
     torch.cuda.synchronize()
     assert torch.equal(again["o"], res["o"]) and torch.equal(again["lse"], res["lse"])
+
+
+@pytest.mark.parametrize("heads,q_len,dt,qdt", [(128, 2, W.DT_BF16, W.DT_BF16), (128, 3, W.DT_FP8, W.DT_FP8),
+                                                (144, 1, W.DT_FP8, W.DT_BF16), (128, 4, W.DT_FP8, W.DT_FP8)])
+def test_mla_balanced_split_over_row_tiles(heads, q_len, dt, qdt):
+    """More than one 128-row tile per request: the balanced split's items are
+    (request, row tile), consecutive shares run on one XCD, and the merge maps
+    each row to its row tile's states.  Ragged and empty requests, long ones
+    spread over many workgroups; bitwise repeat."""
+    kv_lens = [0, 1, 31, 4000, 700, 9000, 2, 5000]
+    label = f"MLA balanced row tiles h{heads} q{q_len} {W.DT_NAMES[dt]} q {W.DT_NAMES[qdt]}"
+    print(label, flush=True)
+    w = mla_build(1300 + heads + q_len + dt + qdt, heads, q_len, kv_lens, 64, dt=dt, q_dtype=qdt)
+    _, res = run_and_check(w, label)
+    again = R.run(R.upload(w))
+    torch.cuda.synchronize()
+    assert torch.equal(again["o"], res["o"]) and torch.equal(again["lse"], res["lse"])
+
+
+def test_mla_one_long_request_many_row_tiles_wide_merge():
+    """One request, 512 rows (four row tiles), 40000 tokens: every row tile's
+    states are merged by the wide merge."""
+    w = mla_build(1350, 128, 4, [40000], 64, dt=W.DT_FP8, q_dtype=W.DT_FP8)
+    run_and_check(w, "MLA b1 512 rows wide merge")

@@ -3,26 +3,33 @@
 // states.  It is the exact-fp32 path (fp32 caches) and the fallback for shapes
 // the MFMA kernels do not cover.
 //
-// One wavefront owns one (query token t, KV head g, block of up to 8 query
-// heads of g's group) and one KV split.  Lanes own head-dim elements
-// d = lane + 64*c.  Per KV token: page-table walk, K row load, dot products
-// reduced across the wavefront, online softmax (running max m, running sum l,
-// rescale by exp(m_old - m_new)), O accumulation with the V row.
+// One workgroup owns one (query token t, KV head g, block of up to 8 query
+// heads of g's group) and one KV split; its four waves take the item's KV tokens
+// in groups of U, group q going to wave q mod 4, and merge their four states in
+// LDS at the end (the in-workgroup split and merge of the SM110 XQA split
+// kernel, kernel-design section).  Lanes own head-dim elements d = lane + 64*c.
+// Per KV token: page-table walk, K row load, dot products reduced across the
+// wavefront, online softmax (running max m, running sum l, rescale by
+// exp(m_old - m_new)), O accumulation with the V row.
 // Online softmax as merged partial states: "Move the Query, Not the Cache"
-// summary, method section; the SM110 XQA split kernel, kernel-design section.
+// summary, method section.
 #include "device_common.h"
 
 namespace pa {
 namespace {
 
-constexpr int kHB = 8;      // query heads per wavefront
-constexpr int kWaves = 4;   // wavefronts per workgroup
+constexpr int kHB = 8;      // query heads per item
+constexpr int kWaves = 4;   // wavefronts per workgroup, all on one item
 
 template <int QT, int KT, int DQC, int DVC>
 __global__ __launch_bounds__(256) void generic_attn_kernel(AttnParams p, int n_hb, int64_t n_items) {
+  // the waves' states, merged at the end
+  __shared__ float s_o[kWaves][kHB][DVC * 64];
+  __shared__ float s_m[kWaves][kHB], s_l[kWaves][kHB];
   const int lane = threadIdx.x & 63;
-  const int64_t item = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (item >= n_items) return;
+  const int w = threadIdx.x >> 6;
+  const int64_t item = blockIdx.x;
+  if (item >= n_items) return;  // uniform over the workgroup
   const int hb = (int)(item % n_hb);
   const int64_t rest = item / n_hb;
   const int g = (int)(rest % p.num_kv_heads);
@@ -71,7 +78,7 @@ __global__ __launch_bounds__(256) void generic_attn_kernel(AttnParams p, int n_h
   // U tokens per step: their page ids, K and V rows are loaded together (no
   // load waits on another), then folded in token order
   constexpr int U = DQC + DVC <= 4 ? 8 : DQC + DVC <= 8 ? 4 : 1;
-  for (int64_t j = j0; j < j1; j += U) {
+  for (int64_t j = j0 + (int64_t)w * U; j < j1; j += (int64_t)kWaves * U) {
     float kf[U][DQC], vf[U][DVC];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -116,18 +123,42 @@ __global__ __launch_bounds__(256) void generic_attn_kernel(AttnParams p, int n_h
     }
   }
 
+  // merge: wave w finishes heads w, w + 4, ... of the block
 #pragma unroll
   for (int r = 0; r < kHB; ++r) {
-    if (r >= nh) break;
+#pragma unroll
+    for (int cc = 0; cc < DVC; ++cc) s_o[w][r][64 * cc + lane] = of[r][cc];
+    if (lane == 0) {
+      s_m[w][r] = m[r];
+      s_l[w][r] = l[r];
+    }
+  }
+  __syncthreads();
+  for (int r = w; r < nh; r += kWaves) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, s_m[ww][r]);
+    const float Mref = M == -INFINITY ? 0.f : M;
+    float L = 0.f;
+    float acc[DVC];
+#pragma unroll
+    for (int cc = 0; cc < DVC; ++cc) acc[cc] = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float cw = fast_exp2(s_m[ww][r] - Mref);  // 0 for a wave that saw no token
+      L = fmaf(cw, s_l[ww][r], L);
+#pragma unroll
+      for (int cc = 0; cc < DVC; ++cc) acc[cc] = fmaf(cw, s_o[ww][r][64 * cc + lane], acc[cc]);
+    }
     const int64_t row = (int64_t)t * p.num_qo_heads + h0 + r;
-    const bool empty = !(l[r] > 0.f);
-    const float inv = empty ? 0.f : p.v_scale / l[r];
+    const bool empty = !(L > 0.f);
+    const float inv = empty ? 0.f : p.v_scale / L;
 #pragma unroll
     for (int cc = 0; cc < DVC; ++cc) {
       const int d = lane + 64 * cc;
       if (d < p.dvo) {
         const int64_t idx = c * p.o_split_stride + row * p.dvo + d;
-        const float val = of[r][cc] * inv;
+        const float val = acc[cc] * inv;
         if (p.o_dtype == F32) store_elem<F32>(p.o, idx, val);
         else if (p.o_dtype == F16) store_elem<F16>(p.o, idx, val);
         else store_elem<BF16>(p.o, idx, val);
@@ -135,8 +166,8 @@ __global__ __launch_bounds__(256) void generic_attn_kernel(AttnParams p, int n_h
     }
     if (lane == 0) {
       const int64_t sidx = c * p.s_split_stride + row;
-      if (p.lse) p.lse[sidx] = empty ? -INFINITY : (m[r] + fast_log2(l[r])) * kLn2;
-      if (p.mx) p.mx[sidx] = empty ? -INFINITY : m[r] * kLn2;
+      if (p.lse) p.lse[sidx] = empty ? -INFINITY : (M + fast_log2(L)) * kLn2;
+      if (p.mx) p.mx[sidx] = empty ? -INFINITY : M * kLn2;
     }
   }
 }
@@ -146,7 +177,7 @@ hipError_t launch_dims(const AttnParams& p, hipStream_t stream) {
   const int n_hb = (p.group + kHB - 1) / kHB;
   const int64_t n_items = (int64_t)p.total_q * p.num_kv_heads * n_hb;
   if (n_items == 0) return hipSuccess;
-  dim3 grid((unsigned)((n_items + kWaves - 1) / kWaves), (unsigned)p.num_splits);
+  dim3 grid((unsigned)n_items, (unsigned)p.num_splits);
   dim3 block(64 * kWaves);
   if (p.dqk == 64 && p.dvo == 64)
     generic_attn_kernel<QT, KT, 1, 1><<<grid, block, 0, stream>>>(p, n_hb, n_items);

@@ -517,6 +517,34 @@ __device__ __forceinline__ void dma_page_fp8(const AttnParams& p, int page, uint
                                              int we, int wbP, const PageLanes<true>& pl, int w) {
   PA_DMA_PAGE_BODY(uint8_t, kDma8, PageLanes<true>)
 }
+using PageLanesQ = PageLanes<true, 2>;  // fp8 stages of the fp8-query kernel
+// The same with the per-lane part computed per call from a laundered lane index
+// (not held in registers across the caller's loop): the many-rows kernels, whose
+// registers are taken by Q^T and O^T.
+__device__ __forceinline__ void dma_page_bf16_inl(const AttnParams& p, int page, uint8_t* stage, int jb,
+                                                  int we, int wbP, int g, int w, int lane) {
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  PageLanes<false> pl;
+  pl.init(p, g, w, ln);
+  PA_DMA_PAGE_BODY(uint16_t, kDma, PageLanes<false>)
+}
+__device__ __forceinline__ void dma_page_fp8q_inl(const AttnParams& p, int page, uint8_t* stage, int jb,
+                                                  int we, int wbP, int g, int w, int lane) {
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  PageLanesQ pl;
+  pl.init(p, g, w, ln);
+  PA_DMA_PAGE_BODY(uint8_t, kDma8, PageLanesQ)
+}
+__device__ __forceinline__ void dma_page_fp8_inl(const AttnParams& p, int page, uint8_t* stage, int jb,
+                                                 int we, int wbP, int g, int w, int lane) {
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  PageLanes<true> pl;
+  pl.init(p, g, w, ln);
+  PA_DMA_PAGE_BODY(uint8_t, kDma8, PageLanes<true>)
+}
 using PageLanes8S = PageLanes<true, 1>;  // swizzled fp8 stages
 __device__ __forceinline__ void dma_page_fp8s(const AttnParams& p, int page, uint8_t* stage, int jb,
                                               int we, int wbP, const PageLanes8S& pl, int w) {
@@ -611,7 +639,7 @@ __device__ __forceinline__ void mla_rows_tile(const uint8_t* kv, int jb, int lim
   // S^T[token][row] = K Q^T: two 16-token blocks.  The 36 K operands (k-step
   // kk, block st: f = 2 kk + st) are read kPF ahead of their MFMAs from a ring
   // of registers; the scheduling barriers keep that order.
-  constexpr int kPF = 2;
+  constexpr int kPF = 4;
   f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
   // K operand of k-step kk, block st: row 16 st + l16, piece 4 kk + lg, whose
   // low three bits are 4 (kk % 2) + lg; swz(row) is the same for both blocks
@@ -680,7 +708,7 @@ __device__ __forceinline__ void mla_rows_tile(const uint8_t* kv, int jb, int lim
   const int hp = (l16 & 3) >> 1;
   const int vq[4] = {vb + 16 * ((0 + hp) ^ vsw), vb + 16 * ((2 + hp) ^ vsw),
                      vb + 16 * ((4 + hp) ^ vsw), vb + 16 * ((6 + hp) ^ vsw)};
-  constexpr int kPV = 2;  // V^T operands in flight
+  constexpr int kPV = 3;  // V^T operands in flight
   i16x8_t vring[kPV];
   auto vfrag = [&](int d) __attribute__((always_inline)) {
     const uint16_t* a0 = reinterpret_cast<const uint16_t*>(kv + vq[d & 3] + 128 * (d >> 2));
@@ -774,22 +802,37 @@ __device__ __forceinline__ void mla_rows_range(const AttnParams& p, int b, int g
       constexpr int kWaitImm = (kWait & 0xF) | ((kWait >> 4) << 14) | 0x70 | 0xF00;
       const int wbP = wb * P;
       auto tile_at = [&](int k) { return ws + min(k, nk - 1) * kTK2; };
-      auto dma = [&](uint8_t* stage, int jb) __attribute__((always_inline)) {
-        if constexpr (FP8)
+      // tiles within one page (page size a multiple of the tile, page-aligned
+      // range): lane i of ptab holds the page id of tile 64 (k / 64) + i, and a
+      // tile's loads take it with one uniform lane read (tiles are issued in
+      // order 0, 1, 2, ...) instead of a per-lane page-table walk through LDS
+      const bool page_tiles = P % kTK2 == 0 && ws % kTK2 == 0;
+      int ptab = 0;
+      auto dma = [&](uint8_t* stage, int k) __attribute__((always_inline)) {
+        const int jb = tile_at(k);
+        if (page_tiles) {
+          if ((k & 63) == 0) ptab = s_pages[div_by_magic((uint32_t)(tile_at(k + lane) - wbP), p.page_magic)];
+          const int page = __builtin_amdgcn_readlane(ptab, k & 63);
+          if constexpr (FP8)
+            dma_page_fp8_inl(p, page, stage, jb, we, wbP, g, w, lane);
+          else
+            dma_page_bf16_inl(p, page, stage, jb, we, wbP, g, w, lane);
+        } else if constexpr (FP8) {
           dma_tile8(p, s_pages, stage, jb, we, wbP, g, w, lane);
-        else
+        } else {
           dma_tile(p, s_pages, stage, jb, we, wbP, g, w, lane);
+        }
       };
-      dma(s_kv0, tile_at(0));
-      dma(s_kv1, tile_at(1));
-      dma(s_kv2, tile_at(2));
+      dma(s_kv0, 0);
+      dma(s_kv1, 1);
+      dma(s_kv2, 2);
       // fp8: the landed stage is widened into s_wide (a second barrier publishes
       // it; the first one also says every wave is done with the previous tile)
 #define PA_MLA_STEP(K, CUR, NEXT3)                                                            \
   {                                                                                         \
     __builtin_amdgcn_s_waitcnt(kWaitImm); /* this wave's loads of tile K are done */        \
     lds_barrier(); /* every wave's; no wait for the tiles behind it */                      \
-    dma(NEXT3, tile_at((K) + 3));                                                           \
+    dma(NEXT3, (K) + 3);                                                                    \
     const uint8_t* src = CUR;                                                               \
     if constexpr (FP8) {                                                                    \
       convert_tile(CUR, s_wide, tid);                                                       \
@@ -1109,17 +1152,27 @@ __device__ __forceinline__ void mla_rows8_range(const AttnParams& p, int b, int 
       constexpr int kWaitImm = (kWait & 0xF) | ((kWait >> 4) << 14) | 0x70 | 0xF00;
       const int wbP = wb * P;
       auto tile_at = [&](int k) { return ws + min(k, nk - 1) * kTK2; };
-      auto dma = [&](uint8_t* stage, int jb) __attribute__((always_inline)) {
-        dma_tile8<2>(p, s_pages, stage, jb, we, wbP, g, w, lane);
+      // page-aligned tiles: one page id per tile from the per-wave table (as in
+      // the many-rows kernel)
+      const bool page_tiles = P % kTK2 == 0 && ws % kTK2 == 0;
+      int ptab = 0;
+      auto dma = [&](uint8_t* stage, int k) __attribute__((always_inline)) {
+        const int jb = tile_at(k);
+        if (page_tiles) {
+          if ((k & 63) == 0) ptab = s_pages[div_by_magic((uint32_t)(tile_at(k + lane) - wbP), p.page_magic)];
+          dma_page_fp8q_inl(p, __builtin_amdgcn_readlane(ptab, k & 63), stage, jb, we, wbP, g, w, lane);
+        } else {
+          dma_tile8<2>(p, s_pages, stage, jb, we, wbP, g, w, lane);
+        }
       };
-      dma(s_kv0, tile_at(0));
-      dma(s_kv1, tile_at(1));
-      dma(s_kv2, tile_at(2));
+      dma(s_kv0, 0);
+      dma(s_kv1, 1);
+      dma(s_kv2, 2);
 #define PA_MLA8_STEP(K, CUR, NEXT3)                                                             \
   {                                                                                           \
     __builtin_amdgcn_s_waitcnt(kWaitImm); /* this wave's loads of tile K are done */          \
     lds_barrier(); /* every wave's; no wait for the tiles behind it */                        \
-    dma(NEXT3, tile_at((K) + 3));                                                             \
+    dma(NEXT3, (K) + 3);                                                                      \
     const int jb = ws + (K) * kTK2;                                                           \
     if (wave_live)                                                                            \
       mla_rows8_tile(CUR, jb, lim, jb + kTK2 > wave_lim_min, qreg, qk_scale, st, oacc, lane); \

@@ -4,6 +4,7 @@
 // section), workspace planning, launch on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdio>
@@ -195,8 +196,8 @@ struct Plan {
   int ws_rows = 16;           // workspace row slots per (batch, KV head, chunk)
   int bal_blocks = 0;         // balanced split over this many workgroups (0: none)
   int bal_unit = 0;           // its unit of work in KV tokens
-  int bal_rt = 1;             // row tiles per (batch, KV head) item of the balanced split
-  int bal_xcd = 0;            // consecutive shares on one XCD
+  int bal_co = 1;             // workgroups (row tiles) per share of the balanced split
+  int bal_xcd = 0;            // the row tiles of a share on one XCD
   size_t workspace = 0;
   const char* name = "generic";
 };
@@ -264,10 +265,10 @@ int device_cus() {
   });
 }
 
-// Workspace of a balanced split: partial states in slots item + workgroup, then
-// the first/last workgroup of every item ((batch, KV head, row tile)).
-size_t balanced_workspace(const AttnParams& p, int blocks, int ws_rows, int bal_rt) {
-  const int64_t items = (int64_t)p.batch * p.num_kv_heads * bal_rt;
+// Workspace of a balanced split over `blocks` shares: partial states in slots
+// item + share, then the first/last share of every item ((batch, KV head)).
+size_t balanced_workspace(const AttnParams& p, int blocks, int ws_rows) {
+  const int64_t items = (int64_t)p.batch * p.num_kv_heads;
   const size_t rows = (size_t)pa::bal_slots(items, blocks) * ws_rows;
   return align256(rows * p.dvo * 4) + 2 * align256(rows * 4) + align256((size_t)items * 8);
 }
@@ -320,7 +321,7 @@ Plan make_plan(const AttnParams& p, uint32_t flags) {
     if (decode_chunk_tokens(p, flags) > 0) {
       pl.bal_unit = 32;
       pl.bal_blocks = gqa_occupancy(p, same) * device_cus();
-      pl.workspace = balanced_workspace(p, pl.bal_blocks, 16, 1);
+      pl.workspace = balanced_workspace(p, pl.bal_blocks, 16);
     }
     return pl;
   }
@@ -336,17 +337,20 @@ Plan make_plan(const AttnParams& p, uint32_t flags) {
                                           : "mla_decode_mfma";
     const int ct = mla_chunk_tokens(p, flags);
     if (ct > 0) {
-      // balanced split over one wave of workgroups; items are (request, KV head,
-      // 128-row tile), and with several row tiles the consecutive shares (the
-      // row tiles of one token range) run on one XCD, sharing its L2
+      // balanced split over one wave of workgroups; with several 128-row tiles
+      // per request, a share is taken by one workgroup per row tile, on one XCD
+      // (they stream the same KV tokens together, read once into its L2), and
+      // the shares are as many as such groups fit, in whole groups per XCD
       const int R = p.q_len * p.group;
       const int rt = pa::mla_rows_per_tile(p);
-      pl.bal_rt = (R + rt - 1) / rt;
+      const int nrt = (R + rt - 1) / rt;
+      const int wgs = mla_occupancy(p) * device_cus();
+      pl.bal_co = nrt;
       pl.bal_unit = 32;
-      pl.bal_blocks = mla_occupancy(p) * device_cus();
-      pl.bal_xcd = pl.bal_rt > 1 && pl.bal_blocks % 8 == 0;
-      pl.ws_rows = pl.bal_rt > 1 ? rt : R;
-      pl.workspace = balanced_workspace(p, pl.bal_blocks, pl.ws_rows, pl.bal_rt);
+      pl.bal_blocks = nrt > 1 && wgs >= 8 * nrt ? wgs / nrt / 8 * 8 : std::max(1, wgs / nrt);
+      pl.bal_xcd = nrt > 1 && pl.bal_blocks % 8 == 0;
+      pl.ws_rows = R;
+      pl.workspace = balanced_workspace(p, pl.bal_blocks, pl.ws_rows);
       return pl;
     }
     pl.chunk_tokens = ct;
@@ -381,8 +385,7 @@ int run_plan(const Plan& pl, AttnParams p, void* ws, size_t ws_bytes, void* cons
   p.ws_rows = pl.ws_rows;
   p.bal_blocks = pl.bal_blocks;
   p.bal_unit = pl.bal_unit;
-  p.bal_rt = pl.bal_rt;
-  p.bal_rows = pl.ws_rows;
+  p.bal_co = pl.bal_co;
   p.bal_xcd = pl.bal_xcd;
   if (pl.bal_blocks > 0) {
     const int64_t items = pa::bal_items(p);
@@ -423,7 +426,7 @@ int run_plan(const Plan& pl, AttnParams p, void* ws, size_t ws_bytes, void* cons
   if (pl.chunk_tokens > 0 || pl.bal_blocks > 0) {
     // many states per row (few long items over many workgroups): split each
     // row's states over the lane groups of a workgroup
-    const int64_t items = (int64_t)p.batch * p.num_kv_heads * pl.bal_rt;
+    const int64_t items = (int64_t)p.batch * p.num_kv_heads;
     const bool wide = (pl.bal_blocks > 0 && pl.bal_blocks >= 32 * items) || pl.max_chunks >= 32;
     e = pa::launch_chunk_merge(p, wide, stream);
   }

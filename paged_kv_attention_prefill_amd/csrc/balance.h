@@ -2,22 +2,27 @@
 // pages only fix that split partial states merge through their LSE, which is how
 // the pieces below are recombined).
 //
-// The work is the sequence of items (query batch b, KV head g, row tile), b-major
-// (row tiles only for MLA with several 128-row tiles per request; the cursor's g
-// runs over KV heads x row tiles); item (b, g) has nu(b) = max(1, ceil(L_b /
-// unit)) units of `unit` KV tokens (an empty KV batch still has one unit, so
-// that some workgroup writes its empty result).
-// With T units in total and NB workgroups (as many as are co-resident on the
-// device), workgroup i takes units [i Qc, min(T, (i+1) Qc)), Qc = ceil(T / NB):
-// every workgroup streams the same number of KV tokens (up to one unit), so all
-// of them finish together instead of in rounds of fixed-size chunks.
+// The work is the sequence of items (query batch b, KV head g), b-major; item
+// (b, g) has nu(b) = max(1, ceil(L_b / unit)) units of `unit` KV tokens (an
+// empty KV batch still has one unit, so that some workgroup writes its empty
+// result).  With T units in total and NB shares (as many as there are
+// co-resident workgroups, or that many over the row tiles below), share i takes
+// units [i Qc, min(T, (i+1) Qc)), Qc = ceil(T / NB): every share streams the
+// same number of KV tokens (up to one unit), so all of them finish together
+// instead of in rounds of fixed-size chunks.
 //
-// A workgroup's range crosses items; each crossing closes a segment.  A segment
+// When the rows of an item span several row tiles (MLA with more than 128 rows
+// per request), a share is taken by one workgroup per row tile, placed on one
+// XCD and dispatched together: they walk the same KV tokens in the same order,
+// so the share's KV is read from HBM once into that XCD's L2.
+//
+// A share's range crosses items; each crossing closes a segment.  A segment
 // that covers a whole item writes the final O / LSE; otherwise it writes a
 // partial state (O normalised by its own sum, LSE, max) to workspace slot
-// item + i, which is unique because item and workgroup indices both grow along
-// the sequence.  The workgroup that takes an item's first unit records the
-// first and last workgroup of the item in ws_seg[item], for the merge launch.
+// item + i, which is unique because item and share indices both grow along
+// the sequence (the row tiles of a share write disjoint rows of the slot).
+// The share that takes an item's first unit records the
+// first and last share of the item in ws_seg[item], for the merge launch.
 #pragma once
 
 #include "device_common.h"
@@ -58,21 +63,22 @@ struct BalCursor {
   int take;      // units of the current segment
   int64_t pos;   // global unit index of the segment's start
   int64_t left;  // units left for this workgroup, current segment included
-  int64_t Qc;    // units per workgroup
+  int64_t Qc;    // units per share
   int i;         // this workgroup's share
+  int rt;        // and row tile
 
   __device__ __forceinline__ int j0(const AttnParams& p) const { return min(L, u * p.bal_unit); }
   __device__ __forceinline__ int j1(const AttnParams& p) const { return min(L, (u + take) * p.bal_unit); }
   __device__ __forceinline__ bool whole() const { return u == 0 && take == nu; }
   __device__ __forceinline__ int64_t slot(const AttnParams& p) const {
-    return (int64_t)(b * p.num_kv_heads * p.bal_rt + g) + i;
+    return (int64_t)(b * p.num_kv_heads + g) + i;
   }
 
-  // the item's first workgroup records the item's span for the merge
+  // the item's first share (its first row tile) records the item's span for the merge
   __device__ __forceinline__ void open(const AttnParams& p) {
     take = uni(left < nu - u ? (int)left : nu - u);
-    if (u == 0 && threadIdx.x == 0) {
-      const int item = b * p.num_kv_heads * p.bal_rt + g;
+    if (u == 0 && rt == 0 && threadIdx.x == 0) {
+      const int item = b * p.num_kv_heads + g;
       p.ws_seg[2 * item] = i;
       p.ws_seg[2 * item + 1] = (int)((pos + nu - 1) / Qc);
     }
@@ -80,10 +86,13 @@ struct BalCursor {
 
   __device__ __forceinline__ bool start(const AttnParams& p, int wg) {
     const int lane = threadIdx.x & 63;
-    const int B = p.batch, H = p.num_kv_heads * p.bal_rt, unit = p.bal_unit;
-    // workgroups are dealt round-robin to the 8 XCDs: with bal_xcd, the shares
-    // of one XCD are consecutive
-    i = p.bal_xcd ? (wg % 8) * (p.bal_blocks / 8) + wg / 8 : wg;
+    const int B = p.batch, H = p.num_kv_heads, unit = p.bal_unit;
+    // workgroups are dealt round-robin to the 8 XCDs: with bal_xcd, the virtual
+    // workgroups of one XCD are consecutive, and so are the row tiles of a share
+    const int nwg = p.bal_blocks * p.bal_co;
+    const int v = p.bal_xcd ? (wg % 8) * (nwg / 8) + wg / 8 : wg;
+    i = v / p.bal_co;
+    rt = v - i * p.bal_co;
     int64_t tot = 0;
     for (int base = 0; base < B; base += 64) {
       const int bb = base + lane;
@@ -127,7 +136,7 @@ struct BalCursor {
     u += take;
     if (u == nu) {
       u = 0;
-      if (++g == p.num_kv_heads * p.bal_rt) {
+      if (++g == p.num_kv_heads) {
         g = 0;
         ++b;
         L = uni(kv_len_of(p, b));

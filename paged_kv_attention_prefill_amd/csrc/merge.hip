@@ -123,11 +123,10 @@ __device__ __forceinline__ int row_states(const AttnParams& p, int b, int g, int
   const int WR = p.ws_rows;
   const int item = b * p.num_kv_heads + g;
   if (p.bal_blocks > 0) {
-    // balanced split: the partial states of item (b, g, row tile of r) sit in
-    // slots item + i for its workgroup shares i = first..last, rows tile-relative
-    const int vitem = item * p.bal_rt + r / p.bal_rows;
-    const int i0 = p.ws_seg[2 * vitem], i1 = p.ws_seg[2 * vitem + 1];
-    wrow0 = ((int64_t)vitem + i0) * WR + r % p.bal_rows;
+    // balanced split: the partial states of item (b, g) sit in slots item + i
+    // for its shares i = first..last
+    const int i0 = p.ws_seg[2 * item], i1 = p.ws_seg[2 * item + 1];
+    wrow0 = ((int64_t)item + i0) * WR + r;
     return i1 - i0 + 1;
   }
   const int kb = p.broadcast ? 0 : b;

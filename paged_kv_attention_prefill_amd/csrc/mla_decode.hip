@@ -866,7 +866,7 @@ __device__ __forceinline__ void mla_rows_range(const AttnParams& p, int b, int g
   const int64_t rid = (int64_t)(b * p.q_len + row / p.group) * p.num_qo_heads + (int64_t)g * p.group +
                       row % p.group;
   // workspace rows: per request (chunks), or per row tile (balanced split with row tiles)
-  const int64_t wrow = wslot * p.ws_rows + (p.bal_rt > 1 ? row - row0 : row);
+  const int64_t wrow = wslot * p.ws_rows + row;
 #pragma unroll
   for (int d = 0; d < NDT; ++d) {
     const int dim = 16 * d + 4 * lg;
@@ -899,8 +899,8 @@ __device__ __forceinline__ void mla_rows_range(const AttnParams& p, int b, int g
 
 // Workgroups: (request, KV head, row tile, chunk or explicit split) items, the
 // row tiles of one item on one XCD so its KV chunk is read once into that L2;
-// or, under the balanced split (one row tile), equal shares of the (request,
-// KV head, 32-token unit) sequence.
+// or, under the balanced split, equal shares of the (request, KV head, 32-token
+// unit) sequence, each taken by one workgroup per row tile on one XCD.
 template <bool FP8>
 __global__ __launch_bounds__(64 * kNW2, 1) void mla_rows_kernel(AttnParams p, int nrt, int ngroups) {
   // four stages (distinct LDS objects, so the compiler's wait counting tells
@@ -916,7 +916,7 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_rows_kernel(AttnParams p, in
     BalCursor cur;
     if (!cur.start(p, blockIdx.x)) return;
     do {
-      mla_rows_range<FP8>(p, cur.b, cur.g / p.bal_rt, cur.g % p.bal_rt, cur.L, cur.j0(p), cur.j1(p),
+      mla_rows_range<FP8>(p, cur.b, cur.g, cur.rt, cur.L, cur.j0(p), cur.j1(p),
                           !cur.whole(), cur.slot(p), 0, s_kv0, s_kv1, s_kv2, s_kv3, s_wide, s_pages);
     } while (cur.next(p));
     return;
@@ -1200,7 +1200,7 @@ __device__ __forceinline__ void mla_rows8_range(const AttnParams& p, int b, int 
   const int64_t rid = (int64_t)(b * p.q_len + row / p.group) * p.num_qo_heads + (int64_t)g * p.group +
                       row % p.group;
   // workspace rows: per request (chunks), or per row tile (balanced split with row tiles)
-  const int64_t wrow = wslot * p.ws_rows + (p.bal_rt > 1 ? row - row0 : row);
+  const int64_t wrow = wslot * p.ws_rows + row;
 #pragma unroll
   for (int d = 0; d < NDT; ++d) {
     const int dim = 16 * d + 4 * lg;
@@ -1242,7 +1242,7 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_rows8_kernel(AttnParams p, i
     BalCursor cur;
     if (!cur.start(p, blockIdx.x)) return;
     do {
-      mla_rows8_range(p, cur.b, cur.g / p.bal_rt, cur.g % p.bal_rt, cur.L, cur.j0(p), cur.j1(p),
+      mla_rows8_range(p, cur.b, cur.g, cur.rt, cur.L, cur.j0(p), cur.j1(p),
                       !cur.whole(), cur.slot(p), 0, s_kv0, s_kv1, s_kv2, s_kv3, s_pages);
     } while (cur.next(p));
     return;
@@ -2157,7 +2157,7 @@ hipError_t launch_rows(const AttnParams& p, hipStream_t stream) {
   AttnParams q = p;
   if (p.chunk_tokens <= 0) q.max_chunks = items;
   const int ngroups = p.batch * p.num_kv_heads * items;
-  const int blocks = p.bal_blocks > 0 ? p.bal_blocks : nrt * 8 * ((ngroups + 7) / 8);
+  const int blocks = p.bal_blocks > 0 ? p.bal_blocks * p.bal_co : nrt * 8 * ((ngroups + 7) / 8);
   if (R <= kRW) {
     if (p.kv_dtype == FP8)
       mla_narrow_kernel<true><<<blocks, 64 * kNW2, 0, stream>>>(q, ngroups);

@@ -52,21 +52,20 @@ struct AttnParams {
   // ws_seg[2 item + 1] receive the item's first and last workgroup
   int32_t bal_blocks;
   int32_t bal_unit;
-  int32_t* ws_seg;          // [B * Hkv * bal_rt][2]
-  // items of the balanced split are (batch, KV head, row tile): bal_rt row tiles
-  // of bal_rows rows per (batch, KV head) (1 and all rows, except for MLA with
-  // more than one 128-row tile); a slot holds the rows of one row tile
-  int32_t bal_rt;
-  int32_t bal_rows;
-  // 1: workgroup w takes share (w % 8) * (bal_blocks / 8) + w / 8, so that
-  // consecutive shares (the row tiles of one token range) run on one XCD
+  int32_t* ws_seg;          // [B * Hkv][2]
+  // row tiles per share (MLA with more than one 128-row tile, else 1): the launch
+  // has bal_blocks * bal_co workgroups, bal_co per share, one per row tile; they
+  // stream the same KV range at the same time, so it is read once into their L2
+  int32_t bal_co;
+  // 1: workgroup w is virtual workgroup (w % 8) * (launch / 8) + w / 8 (share v /
+  // bal_co, row tile v % bal_co), so that the row tiles of one share run on one XCD
   int32_t bal_xcd;
 };
 
 // Workspace slots of a balanced split: item + workgroup < items + blocks - 1.
 inline int64_t bal_slots(int64_t items, int blocks) { return items + blocks - 1; }
-// Items of a balanced split: (batch, KV head, row tile).
-inline int64_t bal_items(const AttnParams& p) { return (int64_t)p.batch * p.num_kv_heads * p.bal_rt; }
+// Items of a balanced split: (batch, KV head).
+inline int64_t bal_items(const AttnParams& p) { return (int64_t)p.batch * p.num_kv_heads; }
 
 // Number of chunks of a KV batch of L tokens under internal chunking.
 __host__ __device__ inline int num_chunks(int L, int chunk_tokens, int max_chunks) {

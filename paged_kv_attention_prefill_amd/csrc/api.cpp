@@ -191,9 +191,7 @@ AttnParams params_prefill(const pa_prefill_args* a) {
 struct Plan {
   enum Kind { GENERIC, GQA_DECODE, FLASH, MLA_DECODE } kind = GENERIC;
   bool same_strides = false;  // V offsets reuse K offsets (equal K/V strides)
-  int chunk_tokens = 0;       // internal KV chunking (0: none)
-  int max_chunks = 0;
-  int ws_rows = 16;           // workspace row slots per (batch, KV head, chunk)
+  int ws_rows = 16;           // workspace row slots per (batch, KV head, share)
   int bal_blocks = 0;         // balanced split over this many workgroups (0: none)
   int bal_unit = 0;           // its unit of work in KV tokens
   int bal_co = 1;             // workgroups (row tiles) per share of the balanced split
@@ -208,20 +206,18 @@ bool equal_kv_strides(const AttnParams& p) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Internal chunk size for the folded-GQA decode: fixed-size chunks bound the
-// longest work item, so the dispatcher can balance ragged KV lengths over the
-// 256 CUs.  Decided from host values only (identical for the size query and
-// the launch), never from device state.
-int decode_chunk_tokens(const AttnParams& p, uint32_t flags) {
-  if ((flags & PA_FLAG_NO_INTERNAL_SPLIT) || p.num_splits != 1 || p.max_kv_len <= 0) return 0;
+// Whether the folded-GQA decode splits its KV over workgroups (the balanced
+// split): when the longest KV exceeds one piece of about 2048 tokens (less with
+// few (batch, head) items, so that there are ~1536 pieces; page aligned).
+// Decided from host values only (identical for the size query and the launch),
+// never from device state.
+bool decode_split_kv(const AttnParams& p, uint32_t flags) {
+  if ((flags & PA_FLAG_NO_INTERNAL_SPLIT) || p.num_splits != 1 || p.max_kv_len <= 0) return false;
   const int64_t items = (int64_t)p.batch * p.num_kv_heads;
   int c = 2048;
-  // few (batch, head) items: smaller chunks so that there are enough workgroups
   while (c > 256 && items * ((p.max_kv_len + c - 1) / c) < 1536) c /= 2;
-  // chunk starts must be page aligned (tiles never straddle a page-id window)
   c = (c + p.page_size - 1) / p.page_size * p.page_size;
-  if (p.max_kv_len <= c) return 0;
-  return c;
+  return p.max_kv_len > c;
 }
 
 // Per-device values read once with HIP device queries (compute-unit count,
@@ -273,19 +269,19 @@ size_t balanced_workspace(const AttnParams& p, int blocks, int ws_rows) {
   return align256(rows * p.dvo * 4) + 2 * align256(rows * 4) + align256((size_t)items * 8);
 }
 
-// Chunk size for the MLA decode: the largest power of two (512..8192 tokens,
-// page aligned) that still gives about a thousand workgroups; bigger chunks
-// mean fewer partial states to write and merge.
-int mla_chunk_tokens(const AttnParams& p, uint32_t flags) {
-  if ((flags & PA_FLAG_NO_INTERNAL_SPLIT) || p.num_splits != 1 || p.max_kv_len <= 0) return 0;
+// Whether the MLA decode splits its KV over workgroups (the balanced split):
+// when the longest KV exceeds one piece of the largest power of two (512..8192
+// tokens, page aligned) that still gives about a thousand (request, row tile,
+// piece) work items.
+bool mla_split_kv(const AttnParams& p, uint32_t flags) {
+  if ((flags & PA_FLAG_NO_INTERNAL_SPLIT) || p.num_splits != 1 || p.max_kv_len <= 0) return false;
   const int R = p.q_len * p.group;
   const int rt = pa::mla_rows_per_tile(p);
   const int64_t tiles = (int64_t)p.batch * p.num_kv_heads * ((R + rt - 1) / rt);
   int c = 8192;
   while (c > 512 && tiles * ((p.max_kv_len + c - 1) / c) < 1024) c /= 2;
   c = (c + p.page_size - 1) / p.page_size * p.page_size;
-  if (p.max_kv_len <= c) return 0;
-  return c;
+  return p.max_kv_len > c;
 }
 
 // Workgroups per CU of the balanced GQA decode kernel variant, per device.
@@ -318,7 +314,7 @@ Plan make_plan(const AttnParams& p, uint32_t flags) {
     // KV long enough to be worth splitting: a balanced split over one wave of
     // co-resident workgroups (every workgroup streams the same number of
     // 32-token tiles, so none idles at the end)
-    if (decode_chunk_tokens(p, flags) > 0) {
+    if (decode_split_kv(p, flags)) {
       pl.bal_unit = 32;
       pl.bal_blocks = gqa_occupancy(p, same) * device_cus();
       pl.workspace = balanced_workspace(p, pl.bal_blocks, 16);
@@ -335,8 +331,7 @@ Plan make_plan(const AttnParams& p, uint32_t flags) {
     pl.name = p.q_dtype == PA_FP8_E4M3    ? "mla_decode_mfma_fp8q"
               : p.kv_dtype == PA_FP8_E4M3 ? "mla_decode_mfma_fp8"
                                           : "mla_decode_mfma";
-    const int ct = mla_chunk_tokens(p, flags);
-    if (ct > 0) {
+    if (mla_split_kv(p, flags)) {
       // balanced split over one wave of workgroups; with several 128-row tiles
       // per request, a share is taken by one workgroup per row tile, on one XCD
       // (they stream the same KV tokens together, read once into its L2), and
@@ -351,14 +346,6 @@ Plan make_plan(const AttnParams& p, uint32_t flags) {
       pl.bal_xcd = nrt > 1 && pl.bal_blocks % 8 == 0;
       pl.ws_rows = R;
       pl.workspace = balanced_workspace(p, pl.bal_blocks, pl.ws_rows);
-      return pl;
-    }
-    pl.chunk_tokens = ct;
-    if (pl.chunk_tokens > 0) {
-      pl.max_chunks = (p.max_kv_len + pl.chunk_tokens - 1) / pl.chunk_tokens;
-      pl.ws_rows = p.q_len * p.group;
-      const size_t rows = (size_t)p.batch * p.num_kv_heads * pl.max_chunks * pl.ws_rows;
-      pl.workspace = align256(rows * p.dvo * 4) + 2 * align256(rows * 4);
     }
     return pl;
   }
@@ -377,11 +364,9 @@ int run_plan(const Plan& pl, AttnParams p, void* ws, size_t ws_bytes, void* cons
   if (log_enabled())
     std::fprintf(stderr,
                  "[paged_attn] kernel=%s total_q=%d Hq=%d Hkv=%d dqk=%d dvo=%d splits=%d "
-                 "chunk=%d x%d balanced=%d x%d ws=%zu\n",
+                 "balanced=%d x%d x%d ws=%zu\n",
                  pl.name, p.total_q, p.num_qo_heads, p.num_kv_heads, p.dqk, p.dvo, p.num_splits,
-                 pl.chunk_tokens, pl.max_chunks, pl.bal_blocks, pl.bal_unit, pl.workspace);
-  p.chunk_tokens = pl.chunk_tokens;
-  p.max_chunks = pl.max_chunks;
+                 pl.bal_blocks, pl.bal_co, pl.bal_unit, pl.workspace);
   p.ws_rows = pl.ws_rows;
   p.bal_blocks = pl.bal_blocks;
   p.bal_unit = pl.bal_unit;
@@ -395,12 +380,6 @@ int run_plan(const Plan& pl, AttnParams p, void* ws, size_t ws_bytes, void* cons
     p.ws_lse = reinterpret_cast<float*>(w + align256(rows * p.dvo * 4));
     p.ws_mx = reinterpret_cast<float*>(w + align256(rows * p.dvo * 4) + align256(rows * 4));
     p.ws_seg = reinterpret_cast<int32_t*>(w + align256(rows * p.dvo * 4) + 2 * align256(rows * 4));
-  } else if (pl.chunk_tokens > 0) {
-    const size_t rows = (size_t)p.batch * p.num_kv_heads * pl.max_chunks * pl.ws_rows;
-    char* w = static_cast<char*>(ws);
-    p.ws_o = reinterpret_cast<float*>(w);
-    p.ws_lse = reinterpret_cast<float*>(w + align256(rows * p.dvo * 4));
-    p.ws_mx = reinterpret_cast<float*>(w + align256(rows * p.dvo * 4) + align256(rows * 4));
   }
   const bool timed = events && events[0] && events[1];
   if (timed && hipEventRecord(static_cast<hipEvent_t>(events[0]), stream) != hipSuccess)
@@ -423,11 +402,11 @@ int run_plan(const Plan& pl, AttnParams p, void* ws, size_t ws_bytes, void* cons
   if (e != hipSuccess) return PA_ERR_HIP;
   if (timed && hipEventRecord(static_cast<hipEvent_t>(events[1]), stream) != hipSuccess)
     return PA_ERR_HIP;
-  if (pl.chunk_tokens > 0 || pl.bal_blocks > 0) {
-    // many states per row (few long items over many workgroups): split each
-    // row's states over the lane groups of a workgroup
+  if (pl.bal_blocks > 0) {
+    // many states per row (few long items over many shares): split each row's
+    // states over the lane groups of a workgroup
     const int64_t items = (int64_t)p.batch * p.num_kv_heads;
-    const bool wide = (pl.bal_blocks > 0 && pl.bal_blocks >= 32 * items) || pl.max_chunks >= 32;
+    const bool wide = pl.bal_blocks >= 32 * items;
     e = pa::launch_chunk_merge(p, wide, stream);
   }
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;

@@ -21,13 +21,13 @@
 //   (running max m, running sum l, rescale by exp2(m_old - m_new)) with
 //   cross-lane reductions over the four 16-lane groups.
 //
-// A workgroup = (KV head, query batch, KV chunk or explicit split) with four
-// waves that take the range's tiles round-robin and merge their states in LDS
-// at the end — the in-workgroup split-and-merge of the SM110 XQA
-// split kernel (kernel-design section).
-// Internal chunking cuts long KV batches into fixed-size chunks whose partial
-// states (O normalised by the chunk's own sum, LSE, max) go to the workspace for
-// the chunk-merge launch; explicit splits write the caller's partial states.
+// A workgroup = (KV head, query batch, explicit split), or a share of the
+// balanced split, with four waves that take the range's tiles round-robin and
+// merge their states in LDS at the end — the in-workgroup split-and-merge of the
+// SM110 XQA split kernel (kernel-design section).  Pieces of a balanced split
+// leave partial states (O normalised by the piece's own sum, LSE, max) in the
+// workspace for the merge launch; explicit splits write the caller's partial
+// states.
 #include "balance.h"
 #include "mfma_common.h"
 
@@ -43,28 +43,22 @@ struct Geo {
   static constexpr int CPR = D / 8;          // 16-byte pieces per head row
   static constexpr int RPI = 64 / CPR;       // rows per load instruction
   static constexpr int NI = kTile / RPI;     // load instructions per tile (each of K, V)
-  static constexpr int KP = D * 2 + 16;      // LDS pitch of a K row (conflict-free operand reads)
-  static constexpr int VP = D * 2 + 32;      // LDS pitch of a V row (conflict-free tr reads)
+  // LDS pitch of a K and of a V row: 2D + 32 bytes puts the K operand reads
+  // (ds_read_b128: four cycles of 16 lanes, by lane / 32 and the parity of the
+  // quad index) and the transposed V reads (two cycles of 32 lanes) on distinct
+  // banks of the 64 (as measured with the LDS bank-conflict counter); 2D + 16
+  // leaves the K reads 2-way conflicted
+  static constexpr int KP = D * 2 + 32;
+  static constexpr int VP = D * 2 + 32;
   static constexpr int VBUF = kTile * VP;    // bytes of one wave's tile buffer (K, then V)
 };
 
-// Token range of work item c of a KV batch with n pages / L tokens.
-// Returns false if the item does not exist (beyond the batch's chunks).
-__device__ __forceinline__ bool item_range(const AttnParams& p, int c, int n, int L, int& j0,
-                                           int& j1, bool& to_ws) {
-  to_ws = false;
-  if (p.chunk_tokens > 0) {
-    const int nch = num_chunks(L, p.chunk_tokens, p.max_chunks);
-    if (c >= nch) return false;
-    j0 = c * p.chunk_tokens;
-    j1 = (c == nch - 1) ? L : j0 + p.chunk_tokens;
-    to_ws = nch > 1;
-  } else {
-    const int S = p.num_splits;
-    j0 = (int)(((int64_t)c * n / S) * p.page_size);
-    j1 = min((int)(((int64_t)(c + 1) * n / S) * p.page_size), L);
-  }
-  return true;
+// Token range of explicit split c of a KV batch with n pages / L tokens: pages
+// [c n / S, (c + 1) n / S).
+__device__ __forceinline__ void item_range(const AttnParams& p, int c, int n, int L, int& j0, int& j1) {
+  const int S = p.num_splits;
+  j0 = (int)(((int64_t)c * n / S) * p.page_size);
+  j1 = min((int)(((int64_t)(c + 1) * n / S) * p.page_size), L);
 }
 
 // Q^T B operand of this lane's row (lane%16), zero for rows beyond q_len*G.
@@ -322,7 +316,7 @@ __device__ __forceinline__ void decode_range(const AttnParams& p, int b, int g, 
   }
 }
 
-// Workgroups: (KV head, query batch, chunk or explicit split) on a 3-D grid, or,
+// Workgroups: (KV head, query batch, explicit split) on a 3-D grid, or,
 // under the balanced split, a 1-D grid whose workgroups walk their share of the
 // (batch, KV head, 32-token unit) sequence.
 template <int DT, int D, bool SAME, int NW>
@@ -347,10 +341,8 @@ __global__ __launch_bounds__(64 * NW, (D > 128 ? 1 : 3)) void gqa_decode_split_k
   const int n = p.kv_indptr[kb + 1] - p.kv_indptr[kb];
   const int L = n ? (n - 1) * p.page_size + p.kv_last[kb] : 0;
   int j0, j1;
-  bool to_ws;
-  if (!item_range(p, c, n, L, j0, j1, to_ws)) return;
-  decode_range<DT, D, SAME, NW>(p, b, g, L, j0, j1, to_ws,
-                                (int64_t)(b * p.num_kv_heads + g) * p.max_chunks + c, c, smem, s_pages);
+  item_range(p, c, n, L, j0, j1);
+  decode_range<DT, D, SAME, NW>(p, b, g, L, j0, j1, false, 0, c, smem, s_pages);
 }
 
 template <int DT, int D>
@@ -358,7 +350,7 @@ hipError_t launch_d(const AttnParams& p, bool same, hipStream_t stream) {
   constexpr int NW = 4;
   const dim3 grid = p.bal_blocks > 0
                         ? dim3(p.bal_blocks)
-                        : dim3(p.num_kv_heads, p.batch, p.chunk_tokens > 0 ? p.max_chunks : p.num_splits);
+                        : dim3(p.num_kv_heads, p.batch, p.num_splits);
   if (same)
     gqa_decode_split_kernel<DT, D, true, NW><<<grid, 64 * NW, 0, stream>>>(p);
   else

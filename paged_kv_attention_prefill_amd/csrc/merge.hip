@@ -116,24 +116,17 @@ hipError_t launch_vt(const void* v, const float* s, int S, int64_t rows, int D, 
   return hipGetLastError();
 }
 
-// Where the partial states of folded row (b, KV head g, r) sit: the number of
-// states and the workspace row of the first (the next ones are WR rows apart).
+// Where the partial states of folded row (b, KV head g, r) of a balanced split
+// sit: the number of states and the workspace row of the first (the next ones
+// are WR rows apart).  The states of item (b, g) sit in slots item + i for its
+// shares i = first..last.
 __device__ __forceinline__ int row_states(const AttnParams& p, int b, int g, int r,
                                           int64_t& wrow0) {
   const int WR = p.ws_rows;
   const int item = b * p.num_kv_heads + g;
-  if (p.bal_blocks > 0) {
-    // balanced split: the partial states of item (b, g) sit in slots item + i
-    // for its shares i = first..last
-    const int i0 = p.ws_seg[2 * item], i1 = p.ws_seg[2 * item + 1];
-    wrow0 = ((int64_t)item + i0) * WR + r;
-    return i1 - i0 + 1;
-  }
-  const int kb = p.broadcast ? 0 : b;
-  const int n = p.kv_indptr[kb + 1] - p.kv_indptr[kb];
-  const int L = n ? (n - 1) * p.page_size + p.kv_last[kb] : 0;
-  wrow0 = (int64_t)item * p.max_chunks * WR + r;
-  return num_chunks(L, p.chunk_tokens, p.max_chunks);
+  const int i0 = p.ws_seg[2 * item], i1 = p.ws_seg[2 * item + 1];
+  wrow0 = ((int64_t)item + i0) * WR + r;
+  return i1 - i0 + 1;
 }
 
 // Running merge state of one lane: LSE maximum M, weight sum, the lane's four
@@ -207,7 +200,7 @@ __device__ __forceinline__ void store_row(const AttnParams& p, int b, int g, int
   }
 }
 
-// Merge of internal KV chunks or balanced-split segments (the same LSE formula):
+// Merge of the balanced split's partial states (the same LSE formula):
 // one group of D/4 lanes per folded row (b, KV head g, row r < q_len*G; the
 // workspace's padding row slots get no lanes); rows whose item was done in one
 // piece were written directly by the attention kernel and are skipped here.

@@ -12,9 +12,8 @@
 //     waves and the partial scores are summed in LDS;
 //   mla_mid_kernel (17..64 rows): the same scheme for two or four 16-row blocks;
 //   mla_rows_kernel (> 64 rows): the flash-attention shape, 16 rows per wave.
-// Chunks or balanced shares of long KV batches leave partial states (O
-// normalised by the piece's own sum, LSE, max) in the workspace for the
-// chunk-merge launch.
+// Balanced shares of long KV batches leave partial states (O normalised by the
+// piece's own sum, LSE, max) in the workspace for the merge launch.
 #include "balance.h"
 #include "mfma_common.h"
 
@@ -26,7 +25,7 @@ constexpr int kPageWinM = 256;               // page ids staged in LDS at a time
 
 // ---------------------------------------------------------------------------
 // Many rows per request (q_len x H > 64, bf16 KV): the flash-attention shape.
-// A workgroup = (request, 128-row tile, KV chunk) with 8 waves of 16 rows each;
+// A workgroup = (request, 128-row tile, KV range) with 8 waves of 16 rows each;
 // every wave keeps its rows' Q^T (16 x 576) in registers and its rows' whole
 // O^T (512 x 16, fp32) in accumulation registers, so a KV tile in LDS feeds all
 // 128 rows with no exchange between waves.  Per 32-token tile:
@@ -608,26 +607,13 @@ __device__ __forceinline__ void convert_tile(const uint8_t* src, uint8_t* dst, i
   }
 }
 
-// Token range of work item c (internal chunk or explicit split) of request b;
-// false if the item does not exist.
-__device__ __forceinline__ bool mla_item_range(const AttnParams& p, int b, int c, int& L, int& j0, int& j1,
-                                               bool& to_ws) {
+// Token range of explicit split c of request b (pages [c n / S, (c + 1) n / S)).
+__device__ __forceinline__ void mla_item_range(const AttnParams& p, int b, int c, int& L, int& j0, int& j1) {
   const int kb = p.broadcast ? 0 : b;
   const int n = p.kv_indptr[kb + 1] - p.kv_indptr[kb];
   L = n ? (n - 1) * p.page_size + p.kv_last[kb] : 0;
-  to_ws = false;
-  if (p.chunk_tokens > 0) {
-    const int nch = num_chunks(L, p.chunk_tokens, p.max_chunks);
-    if (c >= nch) return false;
-    j0 = c * p.chunk_tokens;
-    j1 = (c == nch - 1) ? L : j0 + p.chunk_tokens;
-    to_ws = nch > 1;
-  } else {
-    if (c >= p.num_splits) return false;
-    j0 = (int)(((int64_t)c * n / p.num_splits) * p.page_size);
-    j1 = min((int)(((int64_t)(c + 1) * n / p.num_splits) * p.page_size), L);
-  }
-  return true;
+  j0 = (int)(((int64_t)c * n / p.num_splits) * p.page_size);
+  j1 = min((int)(((int64_t)(c + 1) * n / p.num_splits) * p.page_size), L);
 }
 
 struct MlaRow {
@@ -873,8 +859,7 @@ __device__ __forceinline__ void mla_rows_range(const AttnParams& p, int b, int g
   const float scale = empty ? 0.f : p.v_scale / ltot;
   const int64_t rid = (int64_t)(b * p.q_len + row / p.group) * p.num_qo_heads + (int64_t)g * p.group +
                       row % p.group;
-  // workspace rows: per request (chunks), or per row tile (balanced split with row tiles)
-  const int64_t wrow = wslot * p.ws_rows + row;
+  const int64_t wrow = wslot * p.ws_rows + row;  // workspace row (balanced split)
 #pragma unroll
   for (int d = 0; d < NDT; ++d) {
     const int dim = 16 * d + 4 * lg;
@@ -905,10 +890,10 @@ __device__ __forceinline__ void mla_rows_range(const AttnParams& p, int b, int g
   }
 }
 
-// Workgroups: (request, KV head, row tile, chunk or explicit split) items, the
-// row tiles of one item on one XCD so its KV chunk is read once into that L2;
-// or, under the balanced split, equal shares of the (request, KV head, 32-token
-// unit) sequence, each taken by one workgroup per row tile on one XCD.
+// Workgroups: (request, KV head, row tile, explicit split) items, the row tiles
+// of one item on one XCD so its KV range is read once into that L2; or, under
+// the balanced split, equal shares of the (request, KV head, 32-token unit)
+// sequence, each taken by one workgroup per row tile on one XCD.
 template <bool FP8>
 __global__ __launch_bounds__(64 * kNW2, 1) void mla_rows_kernel(AttnParams p, int nrt, int ngroups) {
   // four stages (distinct LDS objects, so the compiler's wait counting tells
@@ -934,13 +919,12 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_rows_kernel(AttnParams p, in
   const int rt = k8 % nrt;
   const int gi = (k8 / nrt) * 8 + xcd;
   if (gi >= ngroups) return;
-  const int b = gi / (p.num_kv_heads * p.max_chunks);
-  const int g = (gi / p.max_chunks) % p.num_kv_heads;
-  const int c = gi % p.max_chunks;
+  const int b = gi / (p.num_kv_heads * p.num_splits);
+  const int g = (gi / p.num_splits) % p.num_kv_heads;
+  const int c = gi % p.num_splits;
   int L, j0, j1;
-  bool to_ws;
-  if (!mla_item_range(p, b, c, L, j0, j1, to_ws)) return;
-  mla_rows_range<FP8>(p, b, g, rt, L, j0, j1, to_ws, (int64_t)(b * p.num_kv_heads + g) * p.max_chunks + c,
+  mla_item_range(p, b, c, L, j0, j1);
+  mla_rows_range<FP8>(p, b, g, rt, L, j0, j1, false, 0,
                       c, s_kv0, s_kv1, s_kv2, s_kv3, s_wide, s_pages);
 }
 
@@ -1207,8 +1191,7 @@ __device__ __forceinline__ void mla_rows8_range(const AttnParams& p, int b, int 
   const float scale = empty ? 0.f : p.v_scale / ltot;
   const int64_t rid = (int64_t)(b * p.q_len + row / p.group) * p.num_qo_heads + (int64_t)g * p.group +
                       row % p.group;
-  // workspace rows: per request (chunks), or per row tile (balanced split with row tiles)
-  const int64_t wrow = wslot * p.ws_rows + row;
+  const int64_t wrow = wslot * p.ws_rows + row;  // workspace row (balanced split)
 #pragma unroll
   for (int d = 0; d < NDT; ++d) {
     const int dim = 16 * d + 4 * lg;
@@ -1260,13 +1243,12 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_rows8_kernel(AttnParams p, i
   const int rt = k8 % nrt;
   const int gi = (k8 / nrt) * 8 + xcd;
   if (gi >= ngroups) return;
-  const int b = gi / (p.num_kv_heads * p.max_chunks);
-  const int g = (gi / p.max_chunks) % p.num_kv_heads;
-  const int c = gi % p.max_chunks;
+  const int b = gi / (p.num_kv_heads * p.num_splits);
+  const int g = (gi / p.num_splits) % p.num_kv_heads;
+  const int c = gi % p.num_splits;
   int L, j0, j1;
-  bool to_ws;
-  if (!mla_item_range(p, b, c, L, j0, j1, to_ws)) return;
-  mla_rows8_range(p, b, g, rt, L, j0, j1, to_ws, (int64_t)(b * p.num_kv_heads + g) * p.max_chunks + c, c,
+  mla_item_range(p, b, c, L, j0, j1);
+  mla_rows8_range(p, b, g, rt, L, j0, j1, false, 0, c,
                   s_kv0, s_kv1, s_kv2, s_kv3, s_pages);
 }
 
@@ -1665,7 +1647,7 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
   }
 }
 
-// Workgroups: (request, KV head, chunk or explicit split) items, or, under the
+// Workgroups: (request, KV head, explicit split) items, or, under the
 // balanced split, equal shares of the (request, KV head, 32-token unit) sequence.
 template <bool FP8>
 __global__ __launch_bounds__(64 * kNW2, 1) void mla_narrow_kernel(AttnParams p, int ngroups) {
@@ -1692,13 +1674,12 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_narrow_kernel(AttnParams p, 
   }
   const int gi = blockIdx.x;
   if (gi >= ngroups) return;
-  const int b = gi / (p.num_kv_heads * p.max_chunks);
-  const int g = (gi / p.max_chunks) % p.num_kv_heads;
-  const int c = gi % p.max_chunks;
+  const int b = gi / (p.num_kv_heads * p.num_splits);
+  const int g = (gi / p.num_splits) % p.num_kv_heads;
+  const int c = gi % p.num_splits;
   int L, j0, j1;
-  bool to_ws;
-  if (!mla_item_range(p, b, c, L, j0, j1, to_ws)) return;
-  mla_narrow_range<FP8>(p, b, g, L, j0, j1, to_ws, (int64_t)(b * p.num_kv_heads + g) * p.max_chunks + c,
+  mla_item_range(p, b, c, L, j0, j1);
+  mla_narrow_range<FP8>(p, b, g, L, j0, j1, false, 0,
                         c, s_kv0, s_kv1, s_kv2, s_kv3, s_part, s_x, s_pages);
 }
 
@@ -2148,45 +2129,41 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_mid_kernel(AttnParams p, int
   }
   const int gi = blockIdx.x;
   if (gi >= ngroups) return;
-  const int b = gi / (p.num_kv_heads * p.max_chunks);
-  const int g = (gi / p.max_chunks) % p.num_kv_heads;
-  const int c = gi % p.max_chunks;
+  const int b = gi / (p.num_kv_heads * p.num_splits);
+  const int g = (gi / p.num_splits) % p.num_kv_heads;
+  const int c = gi % p.num_splits;
   int L, j0, j1;
-  bool to_ws;
-  if (!mla_item_range(p, b, c, L, j0, j1, to_ws)) return;
-  mla_mid_range<FP8, NRB>(p, b, g, L, j0, j1, to_ws, (int64_t)(b * p.num_kv_heads + g) * p.max_chunks + c,
+  mla_item_range(p, b, c, L, j0, j1);
+  mla_mid_range<FP8, NRB>(p, b, g, L, j0, j1, false, 0,
                           c, s_kv0, s_kv1, s_kv2, s_part, s_x, s_pages);
 }
 
 hipError_t launch_rows(const AttnParams& p, hipStream_t stream) {
   const int R = p.q_len * p.group;
   const int nrt = (R + kRT2 - 1) / kRT2;
-  const int items = p.chunk_tokens > 0 ? p.max_chunks : p.num_splits;
-  AttnParams q = p;
-  if (p.chunk_tokens <= 0) q.max_chunks = items;
-  const int ngroups = p.batch * p.num_kv_heads * items;
+  const int ngroups = p.batch * p.num_kv_heads * p.num_splits;
   const int blocks = p.bal_blocks > 0 ? p.bal_blocks * p.bal_co : nrt * 8 * ((ngroups + 7) / 8);
   if (R <= kRW) {
     if (p.kv_dtype == FP8)
-      mla_narrow_kernel<true><<<blocks, 64 * kNW2, 0, stream>>>(q, ngroups);
+      mla_narrow_kernel<true><<<blocks, 64 * kNW2, 0, stream>>>(p, ngroups);
     else
-      mla_narrow_kernel<false><<<blocks, 64 * kNW2, 0, stream>>>(q, ngroups);
+      mla_narrow_kernel<false><<<blocks, 64 * kNW2, 0, stream>>>(p, ngroups);
   } else if (R <= 2 * kRW) {
     if (p.kv_dtype == FP8)
-      mla_mid_kernel<true, 2><<<blocks, 64 * kNW2, 0, stream>>>(q, ngroups);
+      mla_mid_kernel<true, 2><<<blocks, 64 * kNW2, 0, stream>>>(p, ngroups);
     else
-      mla_mid_kernel<false, 2><<<blocks, 64 * kNW2, 0, stream>>>(q, ngroups);
+      mla_mid_kernel<false, 2><<<blocks, 64 * kNW2, 0, stream>>>(p, ngroups);
   } else if (R <= 4 * kRW) {
     if (p.kv_dtype == FP8)
-      mla_mid_kernel<true, 4><<<blocks, 64 * kNW2, 0, stream>>>(q, ngroups);
+      mla_mid_kernel<true, 4><<<blocks, 64 * kNW2, 0, stream>>>(p, ngroups);
     else
-      mla_mid_kernel<false, 4><<<blocks, 64 * kNW2, 0, stream>>>(q, ngroups);
+      mla_mid_kernel<false, 4><<<blocks, 64 * kNW2, 0, stream>>>(p, ngroups);
   } else if (p.q_dtype == FP8) {
-    mla_rows8_kernel<<<blocks, 64 * kNW2, 0, stream>>>(q, nrt, ngroups);
+    mla_rows8_kernel<<<blocks, 64 * kNW2, 0, stream>>>(p, nrt, ngroups);
   } else if (p.kv_dtype == FP8) {
-    mla_rows_kernel<true><<<blocks, 64 * kNW2, 0, stream>>>(q, nrt, ngroups);
+    mla_rows_kernel<true><<<blocks, 64 * kNW2, 0, stream>>>(p, nrt, ngroups);
   } else {
-    mla_rows_kernel<false><<<blocks, 64 * kNW2, 0, stream>>>(q, nrt, ngroups);
+    mla_rows_kernel<false><<<blocks, 64 * kNW2, 0, stream>>>(p, nrt, ngroups);
   }
   return hipGetLastError();
 }

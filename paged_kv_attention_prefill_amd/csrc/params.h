@@ -37,19 +37,14 @@ struct AttnParams {
   int32_t q_dtype, kv_dtype, o_dtype;
   int32_t max_kv_len;       // host hint (0 unknown)
   int32_t max_q_len;        // host hint: >= every q_b
-  // internal KV chunking (load balance): chunk_tokens > 0 cuts every KV batch into
-  // chunks of that many tokens (the last of max_chunks takes the rest); rows with
-  // more than one chunk leave partial states in the workspace for a merge launch
-  int32_t chunk_tokens;
-  int32_t max_chunks;
-  int32_t ws_rows;          // row slots per (batch, KV head, chunk) in the workspace
-  float* ws_o;              // [B][Hkv][max_chunks][ws_rows][dvo], or [slots][ws_rows][dvo]
-  float* ws_lse;            // [B][Hkv][max_chunks][ws_rows], or [slots][ws_rows]
+  int32_t ws_rows;          // row slots per workspace slot (balanced split)
+  float* ws_o;              // [slots][ws_rows][dvo]
+  float* ws_lse;            // [slots][ws_rows]
   float* ws_mx;             // same as ws_lse
-  // work-balanced split (decode, instead of chunks when bal_blocks > 0): bal_blocks
-  // workgroups take equal shares of the (batch, KV head, unit) sequence, units of
-  // bal_unit tokens; partial states go to slot item + workgroup, and ws_seg[2 item],
-  // ws_seg[2 item + 1] receive the item's first and last workgroup
+  // work-balanced split (decode, when bal_blocks > 0): bal_blocks shares of equal
+  // size of the (batch, KV head, unit) sequence, units of bal_unit tokens; partial
+  // states go to slot item + share, and ws_seg[2 item], ws_seg[2 item + 1] receive
+  // the item's first and last share
   int32_t bal_blocks;
   int32_t bal_unit;
   int32_t* ws_seg;          // [B * Hkv][2]
@@ -62,16 +57,10 @@ struct AttnParams {
   int32_t bal_xcd;
 };
 
-// Workspace slots of a balanced split: item + workgroup < items + blocks - 1.
+// Workspace slots of a balanced split: item + share < items + shares - 1.
 inline int64_t bal_slots(int64_t items, int blocks) { return items + blocks - 1; }
 // Items of a balanced split: (batch, KV head).
 inline int64_t bal_items(const AttnParams& p) { return (int64_t)p.batch * p.num_kv_heads; }
-
-// Number of chunks of a KV batch of L tokens under internal chunking.
-__host__ __device__ inline int num_chunks(int L, int chunk_tokens, int max_chunks) {
-  const int n = L > 0 ? (L + chunk_tokens - 1) / chunk_tokens : 1;
-  return n < max_chunks ? n : max_chunks;
-}
 
 // Size of the library-owned scratch array of the allocation-free decode entry
 // point (one per GPU); noalloc_scratch() returns its device address on the

@@ -424,7 +424,7 @@ static_assert(kTK2 * kPieces8 % 64 == 0, "an fp8 tile is a whole number of 1-KB 
 
 // fp8 stage layout read in place by the narrow and mid kernels: piece p of row r at slot
 // p ^ swz8(r), within p's aligned group of four (36 pieces per row).  With the
-// bank model below, the 8-byte K operand reads (32 lanes: rows 0..15, two
+// bank model above, the 8-byte K operand reads (32 lanes: rows 0..15, two
 // halves) fall on distinct banks; the transposed V reads of a 32-lane cycle
 // hold rows t and t + 16 (the token order of P^T), which sit on the same banks
 // for any swizzle of bits 0..3, so they take two cycles; a swizzle with bit 4

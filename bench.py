@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2516.6      # dense bf16/fp16 MFMA, TFLOP/s
+PEAK_FP8_TFLOPS = 5033.2       # dense fp8 MFMA, TFLOP/s
 METRIC = ("decode attn µs/step + achieved HBM GB/s (% peak); "
           "prefill TFLOP/s (% MFMA)")
 
@@ -244,6 +245,17 @@ def side_workload(name: str, steps: int, warmup: int, iters: int):
     return rec
 
 
+def mfma_peak(w, kernel_name):
+    """(peak TFLOP/s, dtype) of the attention kernel's matrix products: fp8
+    queries over an fp8 cache with more than 64 rows per request run both
+    products on the fp8 MFMA (P.V as two fp8 products, hi and lo parts of P);
+    every other MLA, GQA and prefill kernel multiplies in bf16/fp16."""
+    rows = (w.q_len or 0) * (w.num_qo_heads // w.num_kv_heads)
+    if kernel_name == "mla_decode_mfma_fp8q" and rows > 64:
+        return PEAK_FP8_TFLOPS, "fp8"
+    return PEAK_BF16_TFLOPS, "bf16"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -297,15 +309,17 @@ def main(argv=None):
     gbs = step_bytes / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
     decode_like = w.q_len is not None
-    bound_hbm = (attn_bytes / PEAK_HBM_GBS) >= (flops / PEAK_BF16_TFLOPS / 1e3)
+    peak_mfma, mfma_dtype = mfma_peak(w, call.attention_kernel_name)
+    bound_hbm = (attn_bytes / PEAK_HBM_GBS) >= (flops / peak_mfma / 1e3)
     if bound_hbm:
         ach = attn_bytes / (attn_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}
     else:
         ach = flops / (attn_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak_mfma,
+                "unit": "TFLOP/s", "frac": round(ach / peak_mfma, 4), "traffic": None,
+                "mfma_dtype": mfma_dtype}
     roof["traffic"] = recorded_traffic(a.workload, call.attention_kernel_name)
     roof["kernel"] = call.attention_kernel_name
     roof["kernel_ms"] = round(attn_ms, 5)
@@ -336,7 +350,7 @@ def main(argv=None):
         "achieved_hbm_gbs": round(gbs, 1),
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "achieved_tflops": round(tflops, 2),
-        "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "mfma_frac": round(tflops / peak_mfma, 4),
         "roofline": roof,
     }
     line["timing"] = step_distribution(call, stream, a.iters)

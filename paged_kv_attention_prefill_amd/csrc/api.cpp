@@ -341,7 +341,7 @@ Plan make_plan(const AttnParams& p, uint32_t flags) {
       const int nrt = (R + rt - 1) / rt;
       const int wgs = mla_occupancy(p) * device_cus();
       pl.bal_co = nrt;
-      pl.bal_unit = 32;
+      pl.bal_unit = pa::mla_tile_tokens(p);
       pl.bal_blocks = nrt > 1 && wgs >= 8 * nrt ? wgs / nrt / 8 * 8 : std::max(1, wgs / nrt);
       pl.bal_xcd = nrt > 1 && pl.bal_blocks % 8 == 0;
       pl.ws_rows = R;

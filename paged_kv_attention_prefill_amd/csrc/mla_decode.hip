@@ -929,97 +929,212 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_rows_kernel(AttnParams p, in
 }
 
 // ---------------------------------------------------------------------------
-// fp8 queries over an fp8 cache, more than 64 rows per request: Q.K on the fp8
-// matrix cores (the FP8 MLA decode that the FlashInfer PR #3309 analysis
-// targets, introduction).  The workgroup shape and the tile pipeline are those
-// of the many-rows kernel (8 waves x 16 rows, 32-token tiles streamed HBM ->
-// LDS by direct loads, four stages), but the tile stays as fp8 codes in LDS
-// (swzq layout) and nothing is widened in LDS:
+// fp8 queries over an fp8 cache, more than 64 rows per request: both products
+// on the fp8 matrix cores (the FP8 MLA decode that the FlashInfer PR #3309
+// analysis targets, introduction).  The workgroup shape is that of the many-rows
+// kernel (8 waves x 16 rows), but a tile is 128 tokens, one k-step of the fp8
+// MFMA along the tokens, kept as fp8 codes in LDS (swzq layout) in two stages of
+// 72 KB fed by direct loads (the load of tile k + 1 runs during the math of
+// tile k); nothing is widened:
 //   S^T = K Q^T on v_mfma_scale_f32_16x16x128_f8f6f4 with unit block scales
 //   (the per-tensor query and cache scales are in the score scale): K codes
 //   from LDS as the A operand (32 per lane, two 16-byte reads), the rows' Q^T
-//   codes in registers as the B operand (40 registers instead of 72 for
-//   bf16); the 576 dims are four 128-dim k-steps and one of 64 dims, whose
-//   other half is zero in both operands;
-//   online softmax as in mla_rows_tile;
-//   O^T += V^T P^T on the bf16 16x16x32 MFMA, V^T read by transposed 8-bit
-//   reads (ds_read_b64_tr_b8) in P^T's token order and widened exactly to
-//   bf16 in registers.
+//   codes in registers as the B operand (40 registers); the 576 dims are four
+//   128-dim k-steps and one of 64 dims, whose other half is zero in Q^T;
+//   online softmax as in mla_rows_tile, over 128 tokens at a time;
+//   O^T += V^T P^T on the same MFMA, V^T read by transposed 8-bit reads
+//   (ds_read_b64_tr_b8, four per operand) in P^T's token order.  P in e4m3
+//   alone (4 significant bits) is too coarse for the fp8-KV error bar when a
+//   few tokens dominate a row, so P = hi + lo / 16 with hi = e4m3(P) and
+//   lo = e4m3(16 (P - hi)), two MFMAs per 16-dim block of O, the second with
+//   the block scale 2^-4 on P^T: about 8 significant bits, as bf16.
 // The two operands of the fp8 MFMA pair their (lane group, byte) positions
 // identically (checked on the device), so a lane group's 32 bytes may hold any
-// 32 dims as long as K and Q^T hold the same dims in the same places.
+// 32 dims (or tokens) as long as both operands hold the same ones in the same
+// places.
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 constexpr int kKS8 = 5;  // k-steps of 128 dims (the last one half used)
+constexpr int kTKQ = 128;                       // KV tokens per tile
+constexpr int kDmaQ = kTKQ * kPieces8 / 64;     // 1-KB direct loads per tile (72)
+constexpr int kStageQ = kDmaQ * 1024;           // 73728 bytes
+constexpr int kRoundsQ = kDmaQ / kNW2;          // loads per wave per tile (9)
+constexpr int kQuarterQ = 32 * kPieces8 * 16;   // bytes of 32 token rows
+static_assert(kDmaQ % kNW2 == 0, "every wave issues the same number of tile loads");
+static_assert(kRoundsQ * 1024 == 16 * kPieces8 * 16, "each wave's loads fill 16 whole rows");
 
+// Block scales (E8M0) of the fp8 MFMAs: byte 0 = 127 (2^0), byte 1 = 123 (2^-4),
+// one register for both (the instruction picks a byte of its scale operands).
+constexpr int kScales = 127 | (123 << 8);
 __device__ __forceinline__ f32x4_t mfma_fp8(const i32x8_t& a, const i32x8_t& b, f32x4_t c) {
-  // format 0 (e4m3) for both operands, block scales 2^0 (E8M0 127)
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  // format 0 (e4m3) for both operands, block scales 2^0
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, kScales, 0, kScales);
+}
+__device__ __forceinline__ f32x4_t mfma_fp8_b16th(const i32x8_t& a, const i32x8_t& b, f32x4_t c) {
+  // the same with the B operand's block scale 2^-4
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, kScales, 1, kScales);
 }
 
-// One 32-token tile of math for this wave's 16 rows (lane: row l16, group lg).
+// One direct HBM -> LDS load of 16 bytes per lane (lane l fills LDS bytes
+// [lds + 16 l, lds + 16 l + 16)), issued in asm: the compiler does not count it,
+// so it inserts no waits for it before LDS reads that it cannot tell apart from
+// the stage being filled (the caller waits with an explicit vmcnt(0) and a
+// barrier before a stage is read).  M0 holds the LDS address; one wait state
+// between its write and the load.
+__device__ __forceinline__ void lds_dma16(const void* gaddr, uint8_t* lds) {
+  const uint32_t a = (uint32_t)(uintptr_t)(PA_LDS uint8_t*)lds;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gaddr), "s"(a)
+               : "memory", "m0");
+}
+
+// Direct loads of tile rows [jb, jb + 128) (rows past `we` load row we - 1):
+// wave w fills LDS bytes [9216 w, 9216 w + 9216), tile rows 16 w .. 16 w + 15,
+// with nine loads; lane l of load r fills slot v = 64 r + l of those rows, i.e.
+// row 16 w + v / 36, slot v mod 36, with piece (v mod 36) ^ swzq(row).  PAGED:
+// the page size and the window-relative tile start are multiples of 64, so
+// each 64-row half of the tile (waves 0..3, waves 4..7) lies in one page, whose
+// base comes from scalar registers; otherwise every lane looks up its row's page.
+template <bool PAGED>
+__device__ __forceinline__ void dma_tileq(const AttnParams& p, const int* s_pages, uint8_t* stage,
+                                          int jb, int we, int wbP, int g, int w, int lane) {
+  const uint8_t* kbase = static_cast<const uint8_t*>(p.k);
+  const uint32_t ks0 = (uint32_t)p.ks0, ks1 = (uint32_t)p.ks1;
+  const uint32_t kc = (uint32_t)(g * p.ks2);
+  const int last = we - 1 - jb;
+  int ln = lane;  // recomputed per call rather than held across the tile loop
+  asm volatile("" : "+v"(ln));
+  uint64_t hbase = 0;
+  int hdelta = 0;
+  if constexpr (PAGED) {
+    // the 64-token block holding the wave's half's first row (or row we - 1)
+    const uint32_t rel = (uint32_t)(min(jb + (w >= 4 ? 64 : 0), we - 1) - wbP) & ~63u;
+    const uint32_t pi = div_by_magic(rel, p.page_magic);
+    const uint32_t page = (uint32_t)s_pages[pi];
+    hbase = (uint64_t)page * ks0 + (uint64_t)((rel - pi * (uint32_t)p.page_size) * ks1 + kc);
+    hdelta = jb - wbP - (int)rel;  // tile row + delta: row within the block
+  }
+  const int sw4 = (w & 1) << 1;  // bit 4 of row 16 w + lr (lr < 16), as swzq's bit 1
+#pragma unroll
+  for (int r = 0; r < kRoundsQ; ++r) {
+    const int v = 64 * r + ln;
+    const int lr = (v * 1821) >> 16;  // v / 36 for v < 576
+    const int q = v - 36 * lr;
+    const int row = 16 * w + lr;
+    const uint32_t pc = 16 * (q ^ (((lr >> 2) & 1) | sw4));
+    const int rr = min(row, last);
+    uint64_t off;
+    if constexpr (PAGED) {
+      off = hbase + (uint32_t)((rr + hdelta) * (int)ks1) + pc;
+    } else {
+      const uint32_t jj = (uint32_t)(jb + rr - wbP);
+      const uint32_t pi = div_by_magic(jj, p.page_magic);
+      const uint32_t pslot = jj - pi * (uint32_t)p.page_size;
+      const uint32_t page = (uint32_t)s_pages[pi];
+      off = (uint64_t)page * ks0 + (pslot * ks1 + kc + pc);
+    }
+    lds_dma16(kbase + off, stage + 1024 * (kRoundsQ * w + r));
+  }
+}
+
+// Splits eight probabilities (tokens 4 apart in the lane's order) into e4m3
+// words: hi = e4m3(p), lo = e4m3(16 (p - hi)) (p - hi exact in fp32).
+__device__ __forceinline__ void split_p8(const float (&p)[4], int& hi, int& lo) {
+  // (the first conversion of a word keeps the other half of its third operand:
+  // any live value, overwritten by the second)
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __float_as_int(p[0]), false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], hi, true);
+  // 16 hi, exactly (e4m3 values times a power of two)
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 16.f, false);
+  const auto b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 16.f, true);
+  const float r0 = fmaf(p[0], 16.f, -a[0]), r1 = fmaf(p[1], 16.f, -a[1]);
+  const float r2 = fmaf(p[2], 16.f, -b[0]), r3 = fmaf(p[3], 16.f, -b[1]);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, __float_as_int(r0), false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(r2, r3, lo, true);
+}
+
+// One 128-token tile of math for this wave's 16 rows (lane: row l16, group lg).
 __device__ __forceinline__ void mla_rows8_tile(const uint8_t* kv, int jb, int lim, bool need_mask,
                                                const i32x8_t (&qreg)[kKS8], float qk_scale,
                                                MlaRow& st, f32x4_t (&oacc)[kDvo / 16], int lane) {
   constexpr int NDT = kDvo / 16;
   constexpr int kPitch = kPieces8 * 16;  // 576-byte fp8 rows
+  constexpr int NB = kTKQ / 16;          // 16-token blocks (8)
   int ln = lane;  // per-lane offsets recomputed per tile, not held across the loop
   asm volatile("" : "+v"(ln));
   const int l16 = ln & 15, lg = ln >> 4;
-  // K operand of k-step ks, block st: row 16 st + l16, pieces 8 ks + 2 lg + e
-  // (e = 0, 1), i.e. slot 8 ks + 4 (lg >> 1) + ((2 (lg & 1) + e) ^ swzq(row)):
-  // four per-lane bases (st, e), the k-step adding 128 ks bytes; k-step 4 has
-  // pieces 32..35 only (lane groups 0 and 1)
-  // (addresses stay pointers into the stage, so the compiler's wait counting
+  // K operand of k-step ks, block t: row 16 t + l16, pieces 8 ks + 2 lg + e
+  // (e = 0, 1), i.e. slot 8 ks + 4 (lg >> 1) + ((2 (lg & 1) + e) ^ swzq(row)).
+  // swzq depends on row bits 2 and 4 only: four per-lane bases (t & 1, e), the
+  // block pair t >> 1 adding 32 rows and the k-step 128 bytes.  K-step 4 has
+  // pieces 32..35 only (lane groups 0 and 1); lane groups 2 and 3 read pieces
+  // 32..35 of their row again (in bounds, finite codes) against zero Q^T codes.
+  // (Addresses stay pointers into the stage, so the compiler's wait counting
   // sees which stage a read touches and does not wait for the loads in flight
-  // into the other stages)
-  const int sw0 = swzq(l16);  // block 1 rows: sw0 ^ 2
-  int kb[2][2];  // byte offsets in the stage
+  // into the other one.)
+  const int sw0 = swzq(l16);  // odd blocks: sw0 ^ 2
+  int kb[2][2];
 #pragma unroll
-  for (int stb = 0; stb < 2; ++stb)
+  for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
     for (int e = 0; e < 2; ++e)
-      kb[stb][e] = (16 * stb + l16) * kPitch + 64 * (lg >> 1) + 16 * ((2 * (lg & 1) + e) ^ (sw0 ^ (2 * stb)));
-  // k-step 4 (dims 512..575): lane groups 2 and 3 would address pieces 36..39,
-  // past the row; they read pieces 32..35 of their row instead (in bounds, a
-  // plain read for every lane) and their operand is zeroed by a select
-  const int tail_back = lg >= 2 ? 64 : 0;
+      kb[tb][e] = (16 * tb + l16) * kPitch + 64 * (lg >> 1) + 16 * ((2 * (lg & 1) + e) ^ (sw0 ^ (2 * tb)));
+  // fragment f: k-step f / NB, block f % NB (the blocks' accumulators independent)
   auto kfrag = [&](int f) __attribute__((always_inline)) {
-    const int ks = f >> 1, stb = f & 1;
-    const int back = ks == kKS8 - 1 ? tail_back : 0;
-    const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(kv + kb[stb][0] + 128 * ks - back);
-    const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(kv + kb[stb][1] + 128 * ks - back);
+    const int ks = f / NB, t = f % NB;
+    int b0 = kb[t & 1][0], b1 = kb[t & 1][1];
+    if (ks == kKS8 - 1) {
+      // lane groups 2 and 3: back by 64 bytes (computed here, per read, rather
+      // than kept as per-lane offset constants)
+      const int back = ln & 32 ? 64 : 0;
+      b0 -= back;
+      b1 -= back;
+      asm volatile("" : "+v"(b0), "+v"(b1));
+    }
+    const int o = kQuarterQ * (t >> 1) + 128 * ks;
+    const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(kv + b0 + o);
+    const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(kv + b1 + o);
     return i32x8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   };
+  constexpr int NF = NB * kKS8;
   constexpr int kPF = 2;  // K operands in flight
-  f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  f32x4_t sacc[NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t) sacc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   i32x8_t ring[kPF];
 #pragma unroll
   for (int f = 0; f < kPF; ++f) ring[f] = kfrag(f);
 #pragma unroll
-  for (int f = 0; f < 2 * kKS8; ++f) {
-    i32x8_t a = ring[f % kPF];
-    if (f + kPF < 2 * kKS8) ring[f % kPF] = kfrag(f + kPF);
-    if (f >= 2 * (kKS8 - 1)) {
-      const i32x8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
-      a = tail_back ? z : a;
-    }
-    sacc[f & 1] = mfma_fp8(a, qreg[f >> 1], sacc[f & 1]);
+  for (int f = 0; f < NF; ++f) {
+    const i32x8_t a = ring[f % kPF];
+    if (f + kPF < NF) ring[f % kPF] = kfrag(f + kPF);
+    sacc[f % NB] = mfma_fp8(a, qreg[f / NB], sacc[f % NB]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  // lane holds row l16, tokens jb + 16st + 4lg + i
-  float sv[2][4];
+  // lane holds row l16, tokens jb + 16 t + 4 lg + i
+  float sv[NB][4];
   float tmax = -INFINITY;
+  if (need_mask) {
+    const int rel = lim - jb - 4 * lg;  // token 16 t + 4 lg + i is in range iff 16 t + i < rel
 #pragma unroll
-  for (int st2 = 0; st2 < 2; ++st2)
+    for (int t = 0; t < NB; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = jb + 16 * st2 + 4 * lg + i;
-      sv[st2][i] = (!need_mask || j < lim) ? sacc[st2][i] : -INFINITY;
-      tmax = fmaxf(tmax, sv[st2][i]);
-    }
+      for (int i = 0; i < 4; ++i) {
+        sv[t][i] = 16 * t + i < rel ? sacc[t][i] : -INFINITY;
+        tmax = fmaxf(tmax, sv[t][i]);
+      }
+  } else {
+#pragma unroll
+    for (int t = 0; t < NB; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[t][i] = sacc[t][i];
+        tmax = fmaxf(tmax, sv[t][i]);
+      }
+  }
   tmax = xor32_max(xor16_max(tmax)) * qk_scale;
   st.true_max = fmaxf(st.true_max, tmax);
-  // lazily re-based reference max (as in mla_rows_tile)
+  // lazily re-based reference max (as in mla_rows_tile): P <= 2^8, inside e4m3
   const bool grow = tmax > st.m + 8.f;
   if (__ballot(grow)) {
     const float mnew = grow ? tmax : st.m;
@@ -1032,39 +1147,52 @@ __device__ __forceinline__ void mla_rows8_tile(const uint8_t* kv, int jb, int li
     st.m = mnew;
   }
   const float nmref = -(st.m == -INFINITY ? 0.f : st.m);
-  float e[8];
+  // P^T operands: byte 4 t + i of lane (row, lg) is token 16 t + 4 lg + i
+  i32x8_t phi, plo;
+  float psum = 0.f;
 #pragma unroll
-  for (int st2 = 0; st2 < 2; ++st2)
+  for (int t = 0; t < NB; ++t) {
+    float e[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) e[4 * st2 + i] = fast_exp2(fmaf(sv[st2][i], qk_scale, nmref));
-  const uint4 bits = make_uint4(pack2<BF16>(e[0], e[1]), pack2<BF16>(e[2], e[3]),
-                                pack2<BF16>(e[4], e[5]), pack2<BF16>(e[6], e[7]));
-  const i16x8_t pb = as_i16x8(bits);
-  st.lsum = sum2<BF16>(bits.x, sum2<BF16>(bits.y, sum2<BF16>(bits.z, sum2<BF16>(bits.w, st.lsum))));
-  // O^T += V^T P^T: in each 16-lane group q, lane 2j + h addresses bytes 8h..8h+7
-  // of the dim block's piece in token row trow(q, j), and lane c receives dim c of
-  // the group's eight rows: tokens 4q + j (j < 4) and 16 + 4q + (j - 4), the
-  // token order of P^T above
+    for (int i = 0; i < 4; ++i) e[i] = fast_exp2(fmaf(sv[t][i], qk_scale, nmref));
+    psum += (e[0] + e[1]) + (e[2] + e[3]);
+    int hw, lw;
+    split_p8(e, hw, lw);
+    phi[t] = hw;
+    plo[t] = lw;
+  }
+  st.lsum += psum;
+  // O^T += V^T P^T: V^T operand of dim block d, read r (bytes 8r..8r+7 = blocks
+  // 2r, 2r + 1): in each 16-lane group q, lane 2j + h addresses bytes 8h..8h+7 of
+  // the dim block's piece in token row 32 r + trow(q, j), and lane c receives dim
+  // c of the group's eight rows: tokens 32 r + 4q + j (j < 4) and
+  // 32 r + 16 + 4q + (j - 4), the token order of P^T above
   const int q = ln >> 4, jr = (ln & 15) >> 1, h = ln & 1;
   const int trow = jr < 4 ? 4 * q + jr : 12 + 4 * q + jr;
-  const int tsw = swzq(trow);
+  const int tsw = swzq(trow);  // = swzq(trow + 32 r)
   // dim block d sits at slot 4 (d >> 2) + ((d & 3) ^ tsw): four per-lane bases
   // (d mod 4), the block group adding 64 (d >> 2) bytes
   int vb[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) vb[u] = trow * kPitch + 8 * h + 16 * (u ^ tsw);
   auto vfrag = [&](int d) __attribute__((always_inline)) {
-    return __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2_t*)(kv + vb[d & 3] + 64 * (d >> 2)));
+    const uint8_t* a = kv + vb[d & 3] + 64 * (d >> 2);
+    const i32x2_t x0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2_t*)(a));
+    const i32x2_t x1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2_t*)(a + kQuarterQ));
+    const i32x2_t x2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2_t*)(a + 2 * kQuarterQ));
+    const i32x2_t x3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PA_LDS i32x2_t*)(a + 3 * kQuarterQ));
+    return i32x8_t{x0.x, x0.y, x1.x, x1.y, x2.x, x2.y, x3.x, x3.y};
   };
-  constexpr int kPV = 4;  // V^T operands in flight
-  i32x2_t vring[kPV];
+  constexpr int kPV = 2;  // V^T operands in flight
+  i32x8_t vring[kPV];
 #pragma unroll
   for (int d = 0; d < kPV; ++d) vring[d] = vfrag(d);
 #pragma unroll
   for (int d = 0; d < NDT; ++d) {
-    const i16x8_t va = fp8x8_to_bf16(vring[d % kPV]);
+    const i32x8_t va = vring[d % kPV];
     if (d + kPV < NDT) vring[d % kPV] = vfrag(d + kPV);
-    oacc[d] = mfma16<BF16>(va, pb, oacc[d]);
+    oacc[d] = mfma_fp8(va, phi, oacc[d]);
+    oacc[d] = mfma_fp8_b16th(va, plo, oacc[d]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -1073,8 +1201,7 @@ __device__ __forceinline__ void mla_rows8_tile(const uint8_t* kv, int jb, int li
 // many-rows kernel; output as for the narrow kernel.  Called by every thread.
 __device__ __forceinline__ void mla_rows8_range(const AttnParams& p, int b, int g, int rt, int L, int j0,
                                                 int j1, bool to_ws, int64_t wslot, int c, uint8_t* s_kv0,
-                                                uint8_t* s_kv1, uint8_t* s_kv2, uint8_t* s_kv3,
-                                                int* s_pages) {
+                                                uint8_t* s_kv1, int* s_pages) {
   constexpr int NDT = kDvo / 16;  // 32 16-dim tiles of O
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1104,6 +1231,7 @@ __device__ __forceinline__ void mla_rows8_range(const AttnParams& p, int b, int 
   if (p.causal) jhi = min(j1, L - p.q_len + (min(row0 + kRT2, R) - 1) / p.group + 1);
 
   // Q^T codes: k-step ks, lane group lg holds dims 128 ks + 32 lg .. + 31 of row
+  // (k-step 4: dims 512..575 in lane groups 0 and 1, zeros in 2 and 3)
   i32x8_t qreg[kKS8];
   {
     const int qi = row_ok ? row / p.group : 0, qh = row_ok ? row % p.group : 0;
@@ -1135,50 +1263,32 @@ __device__ __forceinline__ void mla_rows8_range(const AttnParams& p, int b, int 
       for (int i = tid; i < npw; i += 64 * kNW2) s_pages[i] = p.kv_indices[pbeg + wb + i];
       __syncthreads();
       const int ws = max(j0, wb * P), we = min(jhi, (wb + npw) * P);
-      const int nk = (we - ws + kTK2 - 1) / kTK2;
-      // tile k in stage k % 4, tiles k+1..k+3 in flight during its math (as in
-      // the many-rows kernel)
-      constexpr int kMinDma = kDma8 / kNW2;  // direct loads per wave per tile
-      constexpr int kWait = 2 * kMinDma;     // vmcnt that leaves only tiles k+1, k+2 in flight
-      static_assert(kWait < 64, "vmcnt field");
-      constexpr int kWaitImm = (kWait & 0xF) | ((kWait >> 4) << 14) | 0x70 | 0xF00;
+      const int nk = (we - ws + kTKQ - 1) / kTKQ;
       const int wbP = wb * P;
-      auto tile_at = [&](int k) { return ws + min(k, nk - 1) * kTK2; };
-      // page-aligned tiles: one page id per tile from the per-wave table (as in
-      // the many-rows kernel)
-      const bool page_tiles = P % kTK2 == 0 && ws % kTK2 == 0;
-      int ptab = 0;
-      auto dma = [&](uint8_t* stage, int k) __attribute__((always_inline)) {
-        const int jb = tile_at(k);
-        if (page_tiles) {
-          if ((k & 63) == 0) ptab = s_pages[div_by_magic((uint32_t)(tile_at(k + lane) - wbP), p.page_magic)];
-          dma_page_fp8q_inl(p, __builtin_amdgcn_readlane(ptab, k & 63), stage, jb, we, wbP, g, w, lane);
-        } else {
-          dma_tile8<2>(p, s_pages, stage, jb, we, wbP, g, w, lane);
-        }
+      // tile k in stage k % 2; the load of tile k + 1 runs during the math of
+      // tile k (one step per loop iteration, the stages picked at run time: the
+      // loads are issued in asm, so no wait is inserted for them)
+      // tile k in stage k % 2; the load of tile k + 1 runs during the math of
+      // tile k (one step per loop iteration, the stages picked at run time: the
+      // loads are issued in asm, so no wait is inserted for them)
+      const bool paged = P % 64 == 0 && (ws - wbP) % 64 == 0;
+      auto dma = [&](uint8_t* stage, int jb) __attribute__((always_inline)) {
+        if (paged)
+          dma_tileq<true>(p, s_pages, stage, jb, we, wbP, g, w, lane);
+        else
+          dma_tileq<false>(p, s_pages, stage, jb, we, wbP, g, w, lane);
       };
-      dma(s_kv0, 0);
-      dma(s_kv1, 1);
-      dma(s_kv2, 2);
-#define PA_MLA8_STEP(K, CUR, NEXT3)                                                             \
-  {                                                                                           \
-    __builtin_amdgcn_s_waitcnt(kWaitImm); /* this wave's loads of tile K are done */          \
-    lds_barrier(); /* every wave's; no wait for the tiles behind it */                        \
-    dma(NEXT3, (K) + 3);                                                                      \
-    const int jb = ws + (K) * kTK2;                                                           \
-    if (wave_live)                                                                            \
-      mla_rows8_tile(CUR, jb, lim, jb + kTK2 > wave_lim_min, qreg, qk_scale, st, oacc, lane); \
-  }
-      for (int k = 0; k < nk; k += 4) {
-        PA_MLA8_STEP(k, s_kv0, s_kv3);
-        if (k + 1 >= nk) break;
-        PA_MLA8_STEP(k + 1, s_kv1, s_kv0);
-        if (k + 2 >= nk) break;
-        PA_MLA8_STEP(k + 2, s_kv2, s_kv1);
-        if (k + 3 >= nk) break;
-        PA_MLA8_STEP(k + 3, s_kv3, s_kv2);
+      dma(s_kv0, ws);
+      for (int k = 0; k < nk; ++k) {
+        uint8_t* cur = k & 1 ? s_kv1 : s_kv0;
+        uint8_t* nxt = k & 1 ? s_kv0 : s_kv1;
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile k are done
+        lds_barrier();                       // every wave's; the other stage's readers are done
+        const int jb = ws + k * kTKQ;
+        if (k + 1 < nk) dma(nxt, jb + kTKQ);
+        __builtin_amdgcn_sched_barrier(0);  // the loads' addresses die before the math
+        if (wave_live) mla_rows8_tile(cur, jb, lim, jb + kTKQ > wave_lim_min, qreg, qk_scale, st, oacc, lane);
       }
-#undef PA_MLA8_STEP
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no loads in flight into the stages
       __syncthreads();
     }
@@ -1189,9 +1299,12 @@ __device__ __forceinline__ void mla_rows8_range(const AttnParams& p, int b, int 
   if (!row_ok) return;
   const bool empty = !(ltot > 0.f);
   const float scale = empty ? 0.f : p.v_scale / ltot;
-  const int64_t rid = (int64_t)(b * p.q_len + row / p.group) * p.num_qo_heads + (int64_t)g * p.group +
-                      row % p.group;
-  const int64_t wrow = wslot * p.ws_rows + row;  // workspace row (balanced split)
+  // (the row's indices recomputed here, not kept in registers across the loop)
+  int rw = row;
+  asm volatile("" : "+v"(rw));
+  const int64_t rid = (int64_t)(b * p.q_len + rw / p.group) * p.num_qo_heads + (int64_t)g * p.group +
+                      rw % p.group;
+  const int64_t wrow = wslot * p.ws_rows + rw;  // workspace row (balanced split)
 #pragma unroll
   for (int d = 0; d < NDT; ++d) {
     const int dim = 16 * d + 4 * lg;
@@ -1224,17 +1337,15 @@ __device__ __forceinline__ void mla_rows8_range(const AttnParams& p, int b, int 
 
 // Workgroups as for the many-rows kernel.
 __global__ __launch_bounds__(64 * kNW2, 1) void mla_rows8_kernel(AttnParams p, int nrt, int ngroups) {
-  __shared__ __align__(16) uint8_t s_kv0[kStage8];
-  __shared__ __align__(16) uint8_t s_kv1[kStage8];
-  __shared__ __align__(16) uint8_t s_kv2[kStage8];
-  __shared__ __align__(16) uint8_t s_kv3[kStage8];
+  __shared__ __align__(16) uint8_t s_kv0[kStageQ];
+  __shared__ __align__(16) uint8_t s_kv1[kStageQ];
   __shared__ int s_pages[kPageWinM];
   if (p.bal_blocks > 0) {
     BalCursor cur;
     if (!cur.start(p, blockIdx.x)) return;
     do {
       mla_rows8_range(p, cur.b, cur.g, cur.rt, cur.L, cur.j0(p), cur.j1(p),
-                      !cur.whole(), cur.slot(p), 0, s_kv0, s_kv1, s_kv2, s_kv3, s_pages);
+                      !cur.whole(), cur.slot(p), 0, s_kv0, s_kv1, s_pages);
     } while (cur.next(p));
     return;
   }
@@ -1248,8 +1359,7 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_rows8_kernel(AttnParams p, i
   const int c = gi % p.num_splits;
   int L, j0, j1;
   mla_item_range(p, b, c, L, j0, j1);
-  mla_rows8_range(p, b, g, rt, L, j0, j1, false, 0, c,
-                  s_kv0, s_kv1, s_kv2, s_kv3, s_pages);
+  mla_rows8_range(p, b, g, rt, L, j0, j1, false, 0, c, s_kv0, s_kv1, s_pages);
 }
 
 // ---------------------------------------------------------------------------
@@ -2189,6 +2299,10 @@ bool mla_decode_supported(const AttnParams& p) {
 }
 
 int mla_rows_per_tile(const AttnParams&) { return kRT2; }
+
+int mla_tile_tokens(const AttnParams& p) {
+  return p.q_dtype == FP8 && p.q_len * p.group > 4 * kRW ? kTKQ : kTK2;
+}
 
 
 int mla_blocks_per_cu(const AttnParams& p) {

@@ -76,6 +76,7 @@ int gqa_decode_blocks_per_cu(const AttnParams& p, bool same_strides);
 bool mla_decode_supported(const AttnParams& p);
 bool mla_rows_path(const AttnParams& p);
 int mla_rows_per_tile(const AttnParams& p);
+int mla_tile_tokens(const AttnParams& p);  // KV tokens per tile of the kernel taken
 int mla_blocks_per_cu(const AttnParams& p);
 hipError_t launch_mla_decode(const AttnParams& p, hipStream_t stream);
 bool flash_attn_supported(const AttnParams& p);

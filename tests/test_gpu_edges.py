@@ -101,10 +101,18 @@ def test_score_jumps(name, gain):
     both = np.isfinite(mx2[0]) & np.isfinite(mx2[1])
     jump = (mx2[1][both] - mx2[0][both]) * np.log2(np.e)
     assert both.any() and (jump > (8 if gain == 8.0 else 20)).mean() > 0.5, np.median(jump)
-    run_and_check(w, f"jump {name} gain {gain}", expect_plan=PLAN_OF[name.split("_")[0]])
+    stats = [run_and_check(w, f"jump {name} gain {gain}", expect_plan=PLAN_OF[name.split("_")[0]])]
     if name.startswith(("mla", "gqa")):
         # one workgroup walks each row's whole range: the jump lands mid-range
-        run_and_check(w, f"jump {name} gain {gain} unsplit", flags=B.FLAG_NO_INTERNAL_SPLIT)
+        stats.append(run_and_check(w, f"jump {name} gain {gain} unsplit", flags=B.FLAG_NO_INTERNAL_SPLIT))
+    if name.startswith("mla_rows") and name.endswith("fp8q"):
+        # the fp8-query many-rows kernel multiplies P.V on the fp8 MFMA with P
+        # split into two e4m3 terms (about 8 significant bits, as bf16): its
+        # error stays at the level of the bf16-P kernels (about 1.6e-2 here),
+        # where P in one e4m3 term (4 significant bits) reaches 5e-2 to 8e-2 on
+        # these cases in a CPU emulation of the kernel's arithmetic
+        for s in stats:
+            assert s["max_err_o"] <= 3e-2, s
 
 
 def test_score_jumps_split_partials():

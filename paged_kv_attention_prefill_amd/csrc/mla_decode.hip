@@ -658,14 +658,24 @@ __device__ __forceinline__ void mla_rows_tile(const uint8_t* kv, int jb, int lim
   // lane holds row l16, tokens jb + 16st + 4lg + i
   float sv[2][4];
   float tmax = -INFINITY;
+  if (need_mask) {
+    const int rel = lim - jb - 4 * lg;  // token 16 st + 4 lg + i is in range iff 16 st + i < rel
 #pragma unroll
-  for (int st2 = 0; st2 < 2; ++st2)
+    for (int st2 = 0; st2 < 2; ++st2)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = jb + 16 * st2 + 4 * lg + i;
-      sv[st2][i] = (!need_mask || j < lim) ? sacc[st2][i] : -INFINITY;
-      tmax = fmaxf(tmax, sv[st2][i]);
-    }
+      for (int i = 0; i < 4; ++i) {
+        sv[st2][i] = 16 * st2 + i < rel ? sacc[st2][i] : -INFINITY;
+        tmax = fmaxf(tmax, sv[st2][i]);
+      }
+  } else {
+#pragma unroll
+    for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[st2][i] = sacc[st2][i];
+        tmax = fmaxf(tmax, sv[st2][i]);
+      }
+  }
   tmax = xor32_max(xor16_max(tmax)) * qk_scale;
   st.true_max = fmaxf(st.true_max, tmax);
   // lazily re-based reference max: O is rescaled only when a row max grows by

@@ -5,13 +5,17 @@
 // shared by all heads and queries.  Here all q_len x H rows of a request form
 // row blocks (r = token*H + head), so one KV tile in LDS feeds every row.
 //
-// Three kernels by rows per request, all streaming 32-token tiles of whole
+// Four kernels by rows per request and query type, all streaming tiles of whole
 // latent rows HBM -> LDS with direct-to-LDS loads (bf16 rows, or fp8 e4m3 codes
 // with a per-tensor scale):
 //   mla_narrow_kernel (<= 16 rows): the 576-dim contraction is split over the
-//     waves and the partial scores are summed in LDS;
-//   mla_mid_kernel (17..64 rows): the same scheme for two or four 16-row blocks;
-//   mla_rows_kernel (> 64 rows): the flash-attention shape, 16 rows per wave.
+//     waves and the partial scores are summed in LDS; 32-token tiles;
+//   mla_mid_kernel (17..64 rows, bf16 queries): the same scheme for two or four
+//     16-row blocks;
+//   mla_rows_kernel (> 64 rows, bf16 queries): the flash-attention shape, 16
+//     rows per wave, 32-token tiles;
+//   mla_rows8_kernel (> 16 rows, fp8 queries over an fp8 cache): the same shape
+//     with both products on the fp8 matrix cores, 128-token tiles.
 // Balanced shares of long KV batches leave partial states (O normalised by the
 // piece's own sum, LSE, max) in the workspace for the merge launch.
 #include "balance.h"
@@ -939,7 +943,7 @@ __global__ __launch_bounds__(64 * kNW2, 1) void mla_rows_kernel(AttnParams p, in
 }
 
 // ---------------------------------------------------------------------------
-// fp8 queries over an fp8 cache, more than 64 rows per request: both products
+// fp8 queries over an fp8 cache, more than 16 rows per request: both products
 // on the fp8 matrix cores (the FP8 MLA decode that the FlashInfer PR #3309
 // analysis targets, introduction).  The workgroup shape is that of the many-rows
 // kernel (8 waves x 16 rows), but a tile is 128 tokens, one k-step of the fp8
@@ -2263,7 +2267,11 @@ hipError_t launch_rows(const AttnParams& p, hipStream_t stream) {
   const int nrt = (R + kRT2 - 1) / kRT2;
   const int ngroups = p.batch * p.num_kv_heads * p.num_splits;
   const int blocks = p.bal_blocks > 0 ? p.bal_blocks * p.bal_co : nrt * 8 * ((ngroups + 7) / 8);
-  if (R <= kRW) {
+  if (p.q_dtype == FP8 && R > kRW) {
+    // fp8 queries, more than 16 rows: both products on the fp8 MFMA (waves
+    // without rows only load and wait)
+    mla_rows8_kernel<<<blocks, 64 * kNW2, 0, stream>>>(p, nrt, ngroups);
+  } else if (R <= kRW) {
     if (p.kv_dtype == FP8)
       mla_narrow_kernel<true><<<blocks, 64 * kNW2, 0, stream>>>(p, ngroups);
     else
@@ -2278,8 +2286,6 @@ hipError_t launch_rows(const AttnParams& p, hipStream_t stream) {
       mla_mid_kernel<true, 4><<<blocks, 64 * kNW2, 0, stream>>>(p, ngroups);
     else
       mla_mid_kernel<false, 4><<<blocks, 64 * kNW2, 0, stream>>>(p, ngroups);
-  } else if (p.q_dtype == FP8) {
-    mla_rows8_kernel<<<blocks, 64 * kNW2, 0, stream>>>(p, nrt, ngroups);
   } else if (p.kv_dtype == FP8) {
     mla_rows_kernel<true><<<blocks, 64 * kNW2, 0, stream>>>(p, nrt, ngroups);
   } else {
@@ -2311,14 +2317,15 @@ bool mla_decode_supported(const AttnParams& p) {
 int mla_rows_per_tile(const AttnParams&) { return kRT2; }
 
 int mla_tile_tokens(const AttnParams& p) {
-  return p.q_dtype == FP8 && p.q_len * p.group > 4 * kRW ? kTKQ : kTK2;
+  return p.q_dtype == FP8 && p.q_len * p.group > kRW ? kTKQ : kTK2;
 }
 
 
 int mla_blocks_per_cu(const AttnParams& p) {
   const bool fp8 = p.kv_dtype == FP8;
   const int R = p.q_len * p.group;
-  const void* f = R <= kRW       ? (fp8 ? reinterpret_cast<const void*>(&mla_narrow_kernel<true>)
+  const void* f = p.q_dtype == FP8 && R > kRW ? reinterpret_cast<const void*>(&mla_rows8_kernel)
+                  : R <= kRW       ? (fp8 ? reinterpret_cast<const void*>(&mla_narrow_kernel<true>)
                                         : reinterpret_cast<const void*>(&mla_narrow_kernel<false>))
                   : R <= 2 * kRW ? (fp8 ? reinterpret_cast<const void*>(&mla_mid_kernel<true, 2>)
                                         : reinterpret_cast<const void*>(&mla_mid_kernel<false, 2>))

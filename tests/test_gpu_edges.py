@@ -84,6 +84,9 @@ def jump_cases():
                                         q_dtype=W.DT_FP8),
         "mla_narrow_fp8q": lambda g: mla(411, 16, 1, [1, 700, 3000, 4100], dt=W.DT_FP8, gain=g,
                                          q_dtype=W.DT_FP8),
+        # 64 rows on the fp8-MFMA many-rows kernel (waves 4..7 hold no rows)
+        "mla_rows_h16q4_fp8q": lambda g: mla(412, 16, 4, [2, 900, 3300], dt=W.DT_FP8, gain=g,
+                                             q_dtype=W.DT_FP8),
     }
 
 

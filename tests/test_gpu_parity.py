@@ -128,8 +128,9 @@ def test_mla_fp8_queries_row_tiles_and_page_sizes(heads, q_len, page_size):
     run_and_check(w, label + " unsplit", flags=B.FLAG_NO_INTERNAL_SPLIT)
 
 
-def test_mla_fp8_queries_explicit_splits():
-    w = mla_build(1191, 128, 2, [0, 5, 640, 999], 64, dt=W.DT_FP8, q_dtype=W.DT_FP8)
+@pytest.mark.parametrize("heads,q_len", [(128, 2), (16, 2)])
+def test_mla_fp8_queries_explicit_splits(heads, q_len):
+    w = mla_build(1191 + heads, heads, q_len, [0, 5, 640, 999], 64, dt=W.DT_FP8, q_dtype=W.DT_FP8)
     d = R.upload(w)
     S = 3
     res = R.run(d, num_kv_splits=S)

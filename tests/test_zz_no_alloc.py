@@ -21,7 +21,8 @@ def decode_both(w, label):
     d = R.upload(w)
     q4 = d.q.view(w.batch, w.q_len, w.num_qo_heads, w.head_dim_qk)
     common = dict(head_dim_vo=w.head_dim_vo, kv_dtype=w.kv_dtype, k_scale=w.k_scale,
-                  v_scale=w.v_scale, max_kv_len=int(w.kv_lens.max()), sm_scale=w.sm_scale,
+                  v_scale=w.v_scale, q_scale=w.q_scale, max_kv_len=int(w.kv_lens.max()),
+                  sm_scale=w.sm_scale,
                   causal=w.causal, kv_broadcast=w.kv_broadcast, return_max=True)
     ref_call = B.prepare_decode(q4, d.k, d.v, d.kv_indptr, d.kv_indices, d.kv_last, **common)
     assert ref_call.ws_bytes > 0, "the case must use a workspace"
@@ -39,7 +40,7 @@ def decode_both(w, label):
     check_rows(w, to64(got["o"]), to64(got["lse"]), o, lse, to64(got["mx"]), mx, label=label)
 
 
-@pytest.mark.parametrize("family", ["gqa", "mla_narrow", "mla_rows"])
+@pytest.mark.parametrize("family", ["gqa", "mla_narrow", "mla_rows", "mla_fp8_queries"])
 def test_noalloc_two_calls_second_smaller(family):
     if family == "gqa":
         big = W.config2(batch=16, min_len=1, max_len=6000)
@@ -47,8 +48,14 @@ def test_noalloc_two_calls_second_smaller(family):
     elif family == "mla_narrow":
         big = W.config4(num_heads=16, q_len=1, batch=8, min_len=1, max_len=9000)
         small = W.config4(num_heads=16, q_len=1, batch=2, min_len=1, max_len=3000)
-    else:
+    elif family == "mla_rows":
         big = W.config4(num_heads=128, q_len=2, batch=4, min_len=1, max_len=7000)
         small = W.config4(num_heads=128, q_len=2, batch=2, min_len=1, max_len=2500)
+    else:
+        # fp8 queries over an fp8 cache (the fp8-MFMA kernel, 128-token units)
+        big = W.config4(num_heads=128, q_len=2, kv_dtype=W.DT_FP8, q_dtype=W.DT_FP8, batch=4,
+                        min_len=1, max_len=7000)
+        small = W.config4(num_heads=16, q_len=4, kv_dtype=W.DT_FP8, q_dtype=W.DT_FP8, batch=2,
+                          min_len=1, max_len=2500)
     decode_both(big, f"{family} first call")
     decode_both(small, f"{family} second call, smaller")

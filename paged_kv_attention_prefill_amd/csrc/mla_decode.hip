@@ -1051,8 +1051,8 @@ __device__ __forceinline__ void dma_tileq(const AttnParams& p, const int* s_page
   }
 }
 
-// Splits eight probabilities (tokens 4 apart in the lane's order) into e4m3
-// words: hi = e4m3(p), lo = e4m3(16 (p - hi)) (p - hi exact in fp32).
+// Splits four probabilities (one lane's tokens of a 16-token block) into one
+// e4m3 word each: hi = e4m3(p), lo = e4m3(16 (p - hi)) (p - hi exact in fp32).
 __device__ __forceinline__ void split_p8(const float (&p)[4], int& hi, int& lo) {
   // (the first conversion of a word keeps the other half of its third operand:
   // any live value, overwritten by the second)

@@ -2,13 +2,18 @@
 
     python -m paged_kv_attention_prefill_amd.profiling kernels <trace_dir> [--match NAME]
     python -m paged_kv_attention_prefill_amd.profiling counters <pmc_dir> [--match NAME]
+    python -m paged_kv_attention_prefill_amd.profiling utilisation <pmc_dir> --match NAME
     python -m paged_kv_attention_prefill_amd.profiling traffic --workload W --kernel K \
         --fetch <pmc_dir> --write <pmc_dir> --copy-fetch <pmc_dir> --copy-write <pmc_dir> \
         --copy-bytes N
 
 ``kernels`` prints per-kernel dispatch counts and durations from a
 ``--kernel-trace`` run (CSV output, ``-f csv``); ``counters`` prints per-kernel
-averages of the counters of a ``--pmc`` run; ``traffic`` turns FETCH_SIZE and
+averages of the counters of a ``--pmc`` run; ``utilisation`` prints, for one
+kernel of a ``--pmc`` run that collected rocprofv3's derived ``MfmaUtil`` and
+``VALUBusy`` with ``GRBM_GUI_ACTIVE``, the matrix-core and vector-ALU busy
+fractions and the shader clock (GUI-active cycles over the dispatch's
+duration); ``traffic`` turns FETCH_SIZE and
 WRITE_SIZE (KiB per dispatch) into HBM bytes per launch, each scaled by what the
 same counter reads for a plain copy kernel of known size, and records them in
 profiles/traffic.json together with a hash of the kernel sources (the bench
@@ -88,6 +93,45 @@ def counter_stats(pmc_dir: str, match: str = ""):
     return out
 
 
+def utilisation(pmc_dir: str, match: str):
+    """Matrix-core and VALU busy percentages and the shader clock of one kernel.
+
+    Per dispatch: MfmaUtil and VALUBusy as rocprofv3 derives them (busy cycles
+    over GUI-active cycles times the SIMD or CU count), and GRBM_GUI_ACTIVE
+    divided by the dispatch's own start-to-end time.  Averages over dispatches.
+    The CSV value of GRBM_GUI_ACTIVE is summed over the XCDs (one GRBM count per
+    XCD), so the clock divides it by the GPU agent's Num_Xcc.
+    """
+    num_xcc = 1
+    for r in _csv(pmc_dir, "agent_info.csv"):
+        if r.get("Agent_Type") == "GPU":
+            num_xcc = max(1, int(r["Num_Xcc"]))
+    rows = [r for r in _csv(pmc_dir, "counter_collection.csv") if match in r.get("Kernel_Name", "")]
+    if not rows:
+        raise SystemExit(f"no dispatch of {match} in {pmc_dir}")
+    per = defaultdict(dict)
+    for r in rows:
+        d = per[r["Dispatch_Id"]]
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        d["kernel"] = r["Kernel_Name"]
+    out = dict(kernel=short(next(iter(per.values()))["kernel"]), dispatches=len(per),
+               avg_us=statistics.mean(d["us"] for d in per.values()))
+    for c in ("MfmaUtil", "VALUBusy", "LDSBankConflict"):
+        vals = [d[c] for d in per.values() if c in d]
+        if vals:
+            out[c] = statistics.mean(vals)
+    clk = [d["GRBM_GUI_ACTIVE"] / num_xcc / (d["us"] * 1e3) for d in per.values()
+           if "GRBM_GUI_ACTIVE" in d]
+    if clk:
+        out["clock_ghz"] = statistics.mean(clk)
+    for c in ("SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS"):
+        vals = [d[c] for d in per.values() if c in d]
+        if vals:
+            out[c] = statistics.mean(vals)
+    return out
+
+
 def _one(stats, counter):
     vals = [s[counter] for s in stats if counter in s]
     if not vals:
@@ -104,6 +148,9 @@ def main(argv=None):
     c = sub.add_parser("counters")
     c.add_argument("dir")
     c.add_argument("--match", default="")
+    u = sub.add_parser("utilisation")
+    u.add_argument("dir")
+    u.add_argument("--match", required=True)
     t = sub.add_parser("traffic")
     for a in ("--workload", "--kernel", "--fetch", "--write", "--copy-fetch", "--copy-write"):
         t.add_argument(a, required=True)
@@ -120,6 +167,9 @@ def main(argv=None):
     if a.cmd == "counters":
         for s in counter_stats(a.dir, a.match):
             print(json.dumps(s))
+        return 0
+    if a.cmd == "utilisation":
+        print(json.dumps(utilisation(a.dir, a.match)))
         return 0
     fetch = _one(counter_stats(a.fetch, a.kernel), "FETCH_SIZE")
     write = _one(counter_stats(a.write, a.kernel), "WRITE_SIZE")

@@ -192,6 +192,7 @@ struct Plan {
   enum Kind { GENERIC, GQA_DECODE, FLASH, MLA_DECODE } kind = GENERIC;
   bool same_strides = false;  // V offsets reuse K offsets (equal K/V strides)
   int ws_rows = 16;           // workspace row slots per (batch, KV head, share)
+  int ws_dtype = pa::F32;     // element type of the partial O in the workspace
   int bal_blocks = 0;         // balanced split over this many workgroups (0: none)
   int bal_unit = 0;           // its unit of work in KV tokens
   int bal_co = 1;             // workgroups (row tiles) per share of the balanced split
@@ -262,11 +263,15 @@ int device_cus() {
 }
 
 // Workspace of a balanced split over `blocks` shares: partial states in slots
-// item + share, then the first/last share of every item ((batch, KV head)).
-size_t balanced_workspace(const AttnParams& p, int blocks, int ws_rows) {
+// item + share (O in elements of ws_dtype, LSE and max in fp32), then the
+// first/last share of every item ((batch, KV head)).
+size_t ws_o_bytes(size_t rows, int dvo, int ws_dtype) {
+  return align256(rows * dvo * (ws_dtype == pa::F32 ? 4 : 2));
+}
+size_t balanced_workspace(const AttnParams& p, int blocks, int ws_rows, int ws_dtype) {
   const int64_t items = (int64_t)p.batch * p.num_kv_heads;
   const size_t rows = (size_t)pa::bal_slots(items, blocks) * ws_rows;
-  return align256(rows * p.dvo * 4) + 2 * align256(rows * 4) + align256((size_t)items * 8);
+  return ws_o_bytes(rows, p.dvo, ws_dtype) + 2 * align256(rows * 4) + align256((size_t)items * 8);
 }
 
 // Whether the MLA decode splits its KV over workgroups (the balanced split):
@@ -317,7 +322,7 @@ Plan make_plan(const AttnParams& p, uint32_t flags) {
     if (decode_split_kv(p, flags)) {
       pl.bal_unit = 32;
       pl.bal_blocks = gqa_occupancy(p, same) * device_cus();
-      pl.workspace = balanced_workspace(p, pl.bal_blocks, 16);
+      pl.workspace = balanced_workspace(p, pl.bal_blocks, 16, pl.ws_dtype);
     }
     return pl;
   }
@@ -345,7 +350,10 @@ Plan make_plan(const AttnParams& p, uint32_t flags) {
       pl.bal_blocks = nrt > 1 && wgs >= 8 * nrt ? wgs / nrt / 8 * 8 : std::max(1, wgs / nrt);
       pl.bal_xcd = nrt > 1 && pl.bal_blocks % 8 == 0;
       pl.ws_rows = R;
-      pl.workspace = balanced_workspace(p, pl.bal_blocks, pl.ws_rows);
+      // bf16 partial O: R rows x 512 dims per share are the bulk of the
+      // split's extra traffic (written here, read by the merge)
+      pl.ws_dtype = pa::BF16;
+      pl.workspace = balanced_workspace(p, pl.bal_blocks, pl.ws_rows, pl.ws_dtype);
     }
     return pl;
   }
@@ -368,6 +376,7 @@ int run_plan(const Plan& pl, AttnParams p, void* ws, size_t ws_bytes, void* cons
                  pl.name, p.total_q, p.num_qo_heads, p.num_kv_heads, p.dqk, p.dvo, p.num_splits,
                  pl.bal_blocks, pl.bal_co, pl.bal_unit, pl.workspace);
   p.ws_rows = pl.ws_rows;
+  p.ws_dtype = pl.ws_dtype;
   p.bal_blocks = pl.bal_blocks;
   p.bal_unit = pl.bal_unit;
   p.bal_co = pl.bal_co;
@@ -376,10 +385,11 @@ int run_plan(const Plan& pl, AttnParams p, void* ws, size_t ws_bytes, void* cons
     const int64_t items = pa::bal_items(p);
     const size_t rows = (size_t)pa::bal_slots(items, pl.bal_blocks) * pl.ws_rows;
     char* w = static_cast<char*>(ws);
-    p.ws_o = reinterpret_cast<float*>(w);
-    p.ws_lse = reinterpret_cast<float*>(w + align256(rows * p.dvo * 4));
-    p.ws_mx = reinterpret_cast<float*>(w + align256(rows * p.dvo * 4) + align256(rows * 4));
-    p.ws_seg = reinterpret_cast<int32_t*>(w + align256(rows * p.dvo * 4) + 2 * align256(rows * 4));
+    const size_t ob = ws_o_bytes(rows, p.dvo, pl.ws_dtype);
+    p.ws_o = w;
+    p.ws_lse = reinterpret_cast<float*>(w + ob);
+    p.ws_mx = reinterpret_cast<float*>(w + ob + align256(rows * 4));
+    p.ws_seg = reinterpret_cast<int32_t*>(w + ob + 2 * align256(rows * 4));
   }
   const bool timed = events && events[0] && events[1];
   if (timed && hipEventRecord(static_cast<hipEvent_t>(events[0]), stream) != hipSuccess)

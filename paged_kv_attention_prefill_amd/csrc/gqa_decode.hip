@@ -213,7 +213,7 @@ template <int EPT>
 __device__ __forceinline__ void store_row(const AttnParams& p, bool to_ws, int64_t idx,
                                          const float* x, float scale) {
   if (to_ws || p.o_dtype == F32) {
-    float* op = (to_ws ? p.ws_o : static_cast<float*>(p.o)) + idx;
+    float* op = static_cast<float*>(to_ws ? p.ws_o : p.o) + idx;
 #pragma unroll
     for (int e = 0; e < EPT; e += 4)
       *reinterpret_cast<float4*>(op + e) =

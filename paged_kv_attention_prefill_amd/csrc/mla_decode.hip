@@ -880,7 +880,8 @@ __device__ __forceinline__ void mla_rows_range(const AttnParams& p, int b, int g
     const float x0 = oacc[d][0] * scale, x1 = oacc[d][1] * scale;
     const float x2 = oacc[d][2] * scale, x3 = oacc[d][3] * scale;
     if (to_ws) {
-      *reinterpret_cast<float4*>(p.ws_o + wrow * kDvo + dim) = make_float4(x0, x1, x2, x3);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.ws_o) + wrow * kDvo + dim) =
+          make_uint2(pack2<BF16>(x0, x1), pack2<BF16>(x2, x3));  // bf16 partial state
     } else if (p.o_dtype == F32) {
       *reinterpret_cast<float4*>(static_cast<float*>(p.o) + c * p.o_split_stride + rid * kDvo + dim) =
           make_float4(x0, x1, x2, x3);
@@ -1325,7 +1326,8 @@ __device__ __forceinline__ void mla_rows8_range(const AttnParams& p, int b, int 
     const float x0 = oacc[d][0] * scale, x1 = oacc[d][1] * scale;
     const float x2 = oacc[d][2] * scale, x3 = oacc[d][3] * scale;
     if (to_ws) {
-      *reinterpret_cast<float4*>(p.ws_o + wrow * kDvo + dim) = make_float4(x0, x1, x2, x3);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.ws_o) + wrow * kDvo + dim) =
+          make_uint2(pack2<BF16>(x0, x1), pack2<BF16>(x2, x3));  // bf16 partial state
     } else if (p.o_dtype == F32) {
       *reinterpret_cast<float4*>(static_cast<float*>(p.o) + c * p.o_split_stride + rid * kDvo + dim) =
           make_float4(x0, x1, x2, x3);
@@ -1747,7 +1749,8 @@ __device__ __forceinline__ void mla_narrow_range(const AttnParams& p, int b, int
     const float x0 = oacc[d][0] * scale, x1 = oacc[d][1] * scale;
     const float x2 = oacc[d][2] * scale, x3 = oacc[d][3] * scale;
     if (to_ws) {
-      *reinterpret_cast<float4*>(p.ws_o + wrow * kDvo + dim) = make_float4(x0, x1, x2, x3);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.ws_o) + wrow * kDvo + dim) =
+          make_uint2(pack2<BF16>(x0, x1), pack2<BF16>(x2, x3));  // bf16 partial state
     } else if (p.o_dtype == F32) {
       *reinterpret_cast<float4*>(static_cast<float*>(p.o) + c * p.o_split_stride + rid * kDvo + dim) =
           make_float4(x0, x1, x2, x3);
@@ -2204,7 +2207,8 @@ __device__ __forceinline__ void mla_mid_range(const AttnParams& p, int b, int g,
       const float x0 = oacc[rb][d][0] * scale, x1 = oacc[rb][d][1] * scale;
       const float x2 = oacc[rb][d][2] * scale, x3 = oacc[rb][d][3] * scale;
       if (to_ws) {
-        *reinterpret_cast<float4*>(p.ws_o + wrow * kDvo + dim) = make_float4(x0, x1, x2, x3);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.ws_o) + wrow * kDvo + dim) =
+            make_uint2(pack2<BF16>(x0, x1), pack2<BF16>(x2, x3));  // bf16 partial state
       } else if (p.o_dtype == F32) {
         *reinterpret_cast<float4*>(static_cast<float*>(p.o) + c * p.o_split_stride + rid * kDvo + dim) =
             make_float4(x0, x1, x2, x3);

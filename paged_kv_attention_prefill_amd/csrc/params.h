@@ -38,7 +38,8 @@ struct AttnParams {
   int32_t max_kv_len;       // host hint (0 unknown)
   int32_t max_q_len;        // host hint: >= every q_b
   int32_t ws_rows;          // row slots per workspace slot (balanced split)
-  float* ws_o;              // [slots][ws_rows][dvo]
+  void* ws_o;               // [slots][ws_rows][dvo], elements of type ws_dtype
+  int32_t ws_dtype;         // F32 (GQA decode) or BF16 (MLA kernels)
   float* ws_lse;            // [slots][ws_rows]
   float* ws_mx;             // same as ws_lse
   // work-balanced split (decode, when bal_blocks > 0): bal_blocks shares of equal

@@ -54,6 +54,8 @@ struct Fetch {
   const uint16_t* kbase;
   const uint16_t* vbase;
   const int* s_pages;
+  const uint64_t* s_poff;  // PO2: element offset of each window page (page id x page stride)
+  uint32_t pshift, pmask;  // PO2: log2(P), P - 1
   uint32_t ks0, ks1, kc, vs0, vs1, vc;  // kc / vc: KV-head plus 16-byte-chunk offsets
   int tk0, P;
   uint32_t pmagic;         // ceil(2^32 / P), or 0 for P == 1
@@ -67,31 +69,43 @@ struct TileRegs {
   i16x8_t k0, k1, v0, v1;
 };
 
-template <int D, bool SAME>
+template <int D, bool SAME, bool PO2>
 __device__ __forceinline__ void fetch_chunk(const Fetch& f, int jb, int u, i16x8_t& kr,
                                             i16x8_t& vr) {
   using Gm = FGeo<D>;
-  const int j = jb + f.tk0 + Gm::TSTEP * u;
-  const int jj = j < f.we ? j : f.we - 1;  // a valid token, never a poisoned slot
-  // page within the window and slot within the page, division-free: rel < 1024 P
-  // and P <= 2048 keep rel * P < 2^32, where the rounded-up reciprocal is exact
-  const uint32_t rel = jj - f.wbP;
-  const uint32_t pw = div_by_magic(rel, f.pmagic);
-  const int slot = rel - pw * f.P;
-  const uint32_t page = f.s_pages[pw];
-  // 32x32->64-bit page offset plus a 32-bit offset within the page
-  const uint64_t koff = (uint64_t)page * f.ks0 + (slot * f.ks1 + f.kc);
-  const uint64_t voff = SAME ? koff : (uint64_t)page * f.vs0 + (slot * f.vs1 + f.vc);
-  kr = *reinterpret_cast<const i16x8_t*>(f.kbase + koff);
-  vr = *reinterpret_cast<const i16x8_t*>(f.vbase + voff);
+  if constexpr (PO2) {
+    // power-of-two page size, equal K/V strides: the page's offset comes from the
+    // window table (its 64-bit multiply done once per page when staged), the page
+    // and slot by shift and mask, the in-page offset by a 24-bit multiply
+    const int rel = min(jb - f.wbP + f.tk0 + Gm::TSTEP * u, f.we - 1 - f.wbP);
+    const uint32_t pw = (uint32_t)rel >> f.pshift;
+    const uint32_t slot = (uint32_t)rel & f.pmask;
+    const uint64_t e = f.s_poff[pw] + (__umul24(slot, f.ks1) + f.kc);  // in-page part < 2^31
+    kr = *reinterpret_cast<const i16x8_t*>(f.kbase + e);
+    vr = *reinterpret_cast<const i16x8_t*>(f.vbase + e);
+  } else {
+    const int j = jb + f.tk0 + Gm::TSTEP * u;
+    const int jj = j < f.we ? j : f.we - 1;  // a valid token, never a poisoned slot
+    // page within the window and slot within the page, division-free: rel < 1024 P
+    // and P <= 2048 keep rel * P < 2^32, where the rounded-up reciprocal is exact
+    const uint32_t rel = jj - f.wbP;
+    const uint32_t pw = div_by_magic(rel, f.pmagic);
+    const int slot = rel - pw * f.P;
+    const uint32_t page = f.s_pages[pw];
+    // 32x32->64-bit page offset plus a 32-bit offset within the page
+    const uint64_t koff = (uint64_t)page * f.ks0 + (slot * f.ks1 + f.kc);
+    const uint64_t voff = SAME ? koff : (uint64_t)page * f.vs0 + (slot * f.vs1 + f.vc);
+    kr = *reinterpret_cast<const i16x8_t*>(f.kbase + koff);
+    vr = *reinterpret_cast<const i16x8_t*>(f.vbase + voff);
+  }
 }
 
-template <int D, bool SAME>
+template <int D, bool SAME, bool PO2>
 __device__ __forceinline__ void fetch_tile(const Fetch& f, int t, TileRegs& r) {
   static_assert(FGeo<D>::LPT == 1 || FGeo<D>::LPT == 2, "tile fetch covers one or two chunks");
   const int jb = f.ws + min(t, f.nk - 1) * kKT;  // clamped: fetches are unconditional
-  fetch_chunk<D, SAME>(f, jb, 0, r.k0, r.v0);
-  if constexpr (FGeo<D>::LPT == 2) fetch_chunk<D, SAME>(f, jb, 1, r.k1, r.v1);
+  fetch_chunk<D, SAME, PO2>(f, jb, 0, r.k0, r.v0);
+  if constexpr (FGeo<D>::LPT == 2) fetch_chunk<D, SAME, PO2>(f, jb, 1, r.k1, r.v1);
 }
 
 // Rows past the range end hold a clamped valid token: finite, and their P is 0.
@@ -223,7 +237,6 @@ __device__ __forceinline__ void tile_qk_exp(const uint8_t* stage,
                                     pack2<DT>(e[8 * t + 4], e[8 * t + 5]),
                                     pack2<DT>(e[8 * t + 6], e[8 * t + 7]));
       pb[t] = as_i16x8(bits);
-      asm volatile("" : "+v"(pb[t]));  // computed here, not sunk past the mask branch
       // the row sum is taken over the rounded P that the PV step multiplies
       psum = sum2<DT>(bits.x, sum2<DT>(bits.y, sum2<DT>(bits.z, sum2<DT>(bits.w, psum))));
     }
@@ -256,14 +269,16 @@ __device__ __forceinline__ void tile_pv(const uint8_t* stage, const i16x8_t (&pb
     }
 }
 
-template <int DT, int D, bool SAME>
+template <int DT, int D, bool SAME, bool PO2>
 __global__ __launch_bounds__(kThreads, 1) void flash_attn_kernel(AttnParams p, int tiles_per_batch,
                                                                 int num_row_tiles) {
   using Gm = FGeo<D>;
   constexpr int KK = Gm::KK, NDT = Gm::NDT;
   __shared__ __align__(16) uint8_t smem[3 * Gm::STAGE];
-  __shared__ int s_pages[kPageWin];
+  // page-id window: int ids, or (PO2) the 64-bit element offset of each page
+  __shared__ uint64_t s_pagebuf[kPageWin];
   __shared__ int s_red[kNW];
+  int* const s_pages = reinterpret_cast<int*>(s_pagebuf);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -374,6 +389,9 @@ __global__ __launch_bounds__(kThreads, 1) void flash_attn_kernel(AttnParams p, i
   f.kbase = static_cast<const uint16_t*>(p.k);
   f.vbase = static_cast<const uint16_t*>(p.v);
   f.s_pages = s_pages;
+  f.s_poff = s_pagebuf;
+  f.pshift = __builtin_ctz((unsigned)p.page_size);
+  f.pmask = (uint32_t)p.page_size - 1;
   f.ks0 = (uint32_t)p.ks0;
   f.ks1 = (uint32_t)p.ks1;
   f.kc = (uint32_t)(g * p.ks2 + 8 * cc);
@@ -391,7 +409,12 @@ __global__ __launch_bounds__(kThreads, 1) void flash_attn_kernel(AttnParams p, i
     for (int wb = pfirst; wb <= plast; wb += kPageWin) {
       const int npw = min(kPageWin, plast - wb + 1);
       __syncthreads();  // previous window's readers are done
-      for (int i = tid; i < npw; i += kThreads) s_pages[i] = p.kv_indices[pbeg + wb + i];
+      if constexpr (PO2) {
+        for (int i = tid; i < npw; i += kThreads)
+          s_pagebuf[i] = (uint64_t)(uint32_t)p.kv_indices[pbeg + wb + i] * (uint32_t)p.ks0;
+      } else {
+        for (int i = tid; i < npw; i += kThreads) s_pages[i] = p.kv_indices[pbeg + wb + i];
+      }
       __syncthreads();
       f.wbP = wb * P;
       f.ws = max(j0, wb * P);
@@ -407,12 +430,12 @@ __global__ __launch_bounds__(kThreads, 1) void flash_attn_kernel(AttnParams p, i
       // clamped) so every path has the same loads in flight.
       {
         TileRegs r1;
-        fetch_tile<D, SAME>(f, 0, rg);
-        fetch_tile<D, SAME>(f, 1, r1);
+        fetch_tile<D, SAME, PO2>(f, 0, rg);
+        fetch_tile<D, SAME, PO2>(f, 1, r1);
         store_tile<D>(smem, f.tk0, cc, rg);
         store_tile<D>(smem + Gm::STAGE, f.tk0, cc, r1);
       }
-      fetch_tile<D, SAME>(f, 2, rg);
+      fetch_tile<D, SAME, PO2>(f, 2, rg);
       __syncthreads();
       f32x16_t sa[2], sb[2];
       tile_qk<DT, D>(smem, qreg, sa, lane);
@@ -427,7 +450,7 @@ __global__ __launch_bounds__(kThreads, 1) void flash_attn_kernel(AttnParams p, i
         if (more && jn + kKT > wave_lim_min) tile_mask(sn, jn, lim, lane);
         tile_pv<DT, D>(smem + cur, pb, oacc, lane);
         store_tile<D>(smem + nn, f.tk0, cc, rg);  // past the last tile: a stage nobody reads
-        fetch_tile<D, SAME>(f, k + 3, rg);
+        fetch_tile<D, SAME, PO2>(f, k + 3, rg);
         tile_max(sn, qk_scale, st, oacc, more);
         __syncthreads();
         const int t = cur;
@@ -486,10 +509,14 @@ hipError_t launch_fd(const AttnParams& p, bool same, hipStream_t stream) {
   }
   if (num_row_tiles == 0) return hipSuccess;
   const dim3 grid(num_row_tiles * p.num_kv_heads * p.num_splits);
-  if (same)
-    flash_attn_kernel<DT, D, true><<<grid, kThreads, 0, stream>>>(p, tiles_per_batch, num_row_tiles);
+  // power-of-two pages with equal K/V strides take the table-of-page-addresses fetch
+  const bool po2 = same && (p.page_size & (p.page_size - 1)) == 0 && p.ks1 < (int64_t(1) << 24);
+  if (po2)
+    flash_attn_kernel<DT, D, true, true><<<grid, kThreads, 0, stream>>>(p, tiles_per_batch, num_row_tiles);
+  else if (same)
+    flash_attn_kernel<DT, D, true, false><<<grid, kThreads, 0, stream>>>(p, tiles_per_batch, num_row_tiles);
   else
-    flash_attn_kernel<DT, D, false><<<grid, kThreads, 0, stream>>>(p, tiles_per_batch, num_row_tiles);
+    flash_attn_kernel<DT, D, false, false><<<grid, kThreads, 0, stream>>>(p, tiles_per_batch, num_row_tiles);
   return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@ runs the fp32 partial states written and read.  Flops count 2*Dqk + 2*Dvo per
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -46,8 +47,9 @@ def make_workload(name: str):
         return W.config5(poison=False)
     if name == "long_decode_b1":
         # one request, 131072 KV tokens: all parallelism comes from splitting the KV
-        return W.config2(batch=1, min_len=131072, max_len=131072, dtype=W.DT_F16, page_size=128,
-                         num_qo_heads=32, num_kv_heads=8, poison=False)
+        w = W.config2(batch=1, min_len=131072, max_len=131072, dtype=W.DT_F16, page_size=128,
+                      num_qo_heads=32, num_kv_heads=8, poison=False)
+        return dataclasses.replace(w, name="long_decode_b1_131072_f16")
     if name.startswith("sparse"):
         # sparse_<mla|gqa>_h<heads>_<bf16|fp8>: top-2048 selected rows per query
         _, kind, h, dt = name.split("_")
@@ -148,29 +150,40 @@ def cpu_baseline(w, target_s: float = 15.0, threads: int = 0):
 
 
 COPY_BYTES = 1 << 30  # calibration copy: reads and writes this many bytes per launch
+COPY2_BYTES = 1 << 28  # second calibration kernel (a device-to-device copy)
 
 
 def copy_calibration(steps: int) -> int:
-    """A plain streaming kernel of known size (elementwise negate of a 1 GiB fp32
-    tensor: 1 GiB read, 1 GiB written per launch) for scaling HBM byte counters."""
+    """Plain streaming kernels of known size for scaling HBM byte counters:
+    torch's elementwise negate of a 1 GiB fp32 tensor (1 GiB read, 1 GiB written
+    per launch) and a 256 MiB device-to-device tensor copy (the runtime's copy
+    kernel: 256 MiB read, 256 MiB written), a second point for the scale."""
     import torch
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
     for _ in range(steps):
         torch.neg(src, out=dst)
+    src2 = src[: COPY2_BYTES // 4]
+    dst2 = torch.empty_like(src2)
+    for _ in range(steps):
+        dst2.copy_(src2)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "launches": steps}))
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "copy2_calibration_bytes": COPY2_BYTES,
+                      "launches": steps}))
     return 0
 
 
-def recorded_traffic(workload: str, kernel: str):
-    """HBM bytes per launch from profiles/traffic.json if it was measured for this
-    workload and kernel with the current kernel sources, else None."""
+def recorded_traffic(workload: str):
+    """HBM bytes per launch of the workload's attention kernel from
+    profiles/traffic.json if it was measured with the current sources of that
+    kernel, else None."""
     from paged_kv_attention_prefill_amd import profiling
     if not os.path.exists(profiling.TRAFFIC_JSON):
         return None
     rec = json.load(open(profiling.TRAFFIC_JSON)).get(workload)
-    if not rec or rec.get("source_hash") != profiling.kernel_source_hash():
+    # the record names the kernel as the profiler does; its hash covers the
+    # sources that build that kernel family
+    if not rec or rec.get("source_hash") != profiling.kernel_source_hash(rec.get("kernel", "")):
         return None
     return int(rec["traffic_bytes"])
 
@@ -191,7 +204,9 @@ def step_distribution(call, stream, iters: int):
     written back during the timed step).  Each step is bracketed by its own
     event pair on the stream it runs on."""
     import torch
-    scratch = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda:0")
+    # fp32, so that the sum reads the buffer in place (an int32 sum would first
+    # write an int64 copy of it)
+    scratch = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
     out = {}
     for mode in ("warm", "cold"):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -320,7 +335,7 @@ def main(argv=None):
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak_mfma,
                 "unit": "TFLOP/s", "frac": round(ach / peak_mfma, 4), "traffic": None,
                 "mfma_dtype": mfma_dtype}
-    roof["traffic"] = recorded_traffic(a.workload, call.attention_kernel_name)
+    roof["traffic"] = recorded_traffic(a.workload)
     roof["kernel"] = call.attention_kernel_name
     roof["kernel_ms"] = round(attn_ms, 5)
     roof["bytes_per_launch"] = attn_bytes

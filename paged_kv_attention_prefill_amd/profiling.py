@@ -16,8 +16,8 @@ fractions and the shader clock (GUI-active cycles over the dispatch's
 duration); ``traffic`` turns FETCH_SIZE and
 WRITE_SIZE (KiB per dispatch) into HBM bytes per launch, each scaled by what the
 same counter reads for a plain copy kernel of known size, and records them in
-profiles/traffic.json together with a hash of the kernel sources (the bench
-reports the record only while the sources are unchanged).
+profiles/traffic.json together with a hash of the sources that build that
+kernel (the bench reports the record only while they are unchanged).
 """
 from __future__ import annotations
 
@@ -36,12 +36,48 @@ ROOT = os.path.dirname(PKG)
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the library's kernel and host sources."""
+# the source file that holds each kernel family (matched by name prefix)
+KERNEL_SOURCES = (("gqa_decode", "gqa_decode.hip"), ("flash_attn", "flash_attn.hip"),
+                  ("mla_", "mla_decode.hip"), ("generic", "generic.hip"),
+                  ("chunk_merge", "merge.hip"), ("merge", "merge.hip"))
+
+
+def _with_includes(name: str, seen: set) -> None:
+    """`name` and, transitively, the local headers it includes."""
+    if name in seen:
+        return
+    seen.add(name)
+    with open(os.path.join(PKG, "csrc", name)) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith('#include "'):
+                inc = line.split('"')[1]
+                if os.path.exists(os.path.join(PKG, "csrc", inc)):
+                    _with_includes(inc, seen)
+
+
+def kernel_sources(kernel: str = "") -> list:
+    """The csrc files that build `kernel`: its own file, the headers it includes,
+    and api.cpp (the host plan that sets its grid, split and workspace).  With no
+    kernel name, or one of no known family: every source."""
+    for prefix, src in KERNEL_SOURCES:
+        if kernel.startswith(prefix):
+            seen: set = set()
+            _with_includes(src, seen)
+            _with_includes("api.cpp", seen)
+            return sorted(seen)
+    seen = set()
+    for path in glob.glob(os.path.join(PKG, "csrc", "*")):
+        _with_includes(os.path.basename(path), seen)
+    return sorted(seen)
+
+
+def kernel_source_hash(kernel: str = "") -> str:
+    """sha256 over kernel_sources(kernel)."""
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(PKG, "csrc", "*"))):
-        with open(path, "rb") as f:
-            h.update(os.path.basename(path).encode())
+    for name in kernel_sources(kernel):
+        with open(os.path.join(PKG, "csrc", name), "rb") as f:
+            h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -177,7 +213,7 @@ def main(argv=None):
     cw = _one(counter_stats(a.copy_write, "neg_kernel"), "WRITE_SIZE")
     f_scale = a.copy_bytes / (cf * 1024.0)
     w_scale = a.copy_bytes / (cw * 1024.0)
-    rec = dict(workload=a.workload, kernel=a.kernel, source_hash=kernel_source_hash(),
+    rec = dict(workload=a.workload, kernel=a.kernel, source_hash=kernel_source_hash(a.kernel),
                fetch_kib=fetch, write_kib=write, copy_fetch_kib=cf, copy_write_kib=cw,
                copy_bytes=a.copy_bytes, fetch_scale=f_scale, write_scale=w_scale,
                fetch_bytes=fetch * 1024.0 * f_scale, write_bytes=write * 1024.0 * w_scale)

@@ -54,3 +54,17 @@ def test_kernel_stats_from_a_trace(tmp_path):
     assert stats[0]["calls"] == 2 and stats[0]["avg_us"] == pytest.approx(4.0)
     assert stats[0]["min_us"] == pytest.approx(3.0) and stats[0]["max_us"] == pytest.approx(5.0)
     assert os.path.basename(PR.TRAFFIC_JSON) == "traffic.json"
+
+
+def test_kernel_sources_follow_each_family_and_its_includes():
+    from paged_kv_attention_prefill_amd import profiling as P
+    gqa = P.kernel_sources("gqa_decode_split_kernel")
+    assert {"gqa_decode.hip", "balance.h", "mfma_common.h", "device_common.h", "params.h",
+            "api.cpp"} <= set(gqa)
+    assert "mla_decode.hip" not in gqa and "flash_attn.hip" not in gqa
+    flash = P.kernel_sources("flash_attn_kernel")
+    assert "flash_attn.hip" in flash and "balance.h" not in flash
+    assert "mla_decode.hip" in P.kernel_sources("mla_rows8_kernel")
+    # unknown names hash every source
+    assert set(P.kernel_sources("")) >= set(gqa) | set(flash)
+    assert P.kernel_source_hash("gqa_decode_split_kernel") != P.kernel_source_hash("flash_attn_kernel")

@@ -226,16 +226,24 @@ def step_distribution(call, stream, iters: int):
     return out
 
 
+# Warm-up of the side workloads: under back-to-back MFMA-heavy launches the
+# shader clock takes some 30-40 calls to settle (config 3: ~450 us in the first
+# calls, ~520 us a few calls later, ~430 us settled), so the timed steps start
+# after that.
+SIDE_WARMUP = 40
+
+
 def side_workload(name: str, steps: int, warmup: int, iters: int):
-    """Timing of a second workload in the same run (same protocol as the main one):
-    step µs, the attention kernel's µs, and its rate against its binding roof."""
+    """Timing of a second workload in the same run (same protocol as the main one,
+    with at least SIDE_WARMUP warm-up steps): step µs, the attention kernel's µs,
+    and its rate against its binding roof."""
     import torch
     from paged_kv_attention_prefill_amd import runner as R
     w = make_workload(name)
     d = R.upload(w, "cuda:0")
     stream = torch.cuda.current_stream()
     call = R.prepare(d)
-    for _ in range(warmup):
+    for _ in range(max(warmup, SIDE_WARMUP)):
         call()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

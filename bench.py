@@ -295,7 +295,7 @@ def main(argv=None):
                     help="run only the HBM-counter calibration copy kernel")
     a = ap.parse_args(argv)
     if a.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {a.gpus}); run with --gpus 1", file=sys.stderr)
         return 2
 

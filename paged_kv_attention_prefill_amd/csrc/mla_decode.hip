@@ -26,6 +26,11 @@ namespace {
 
 constexpr int kDqk = 576, kDvo = 512;
 constexpr int kPageWinM = 256;               // page ids staged in LDS at a time
+// Cache policy of the KV tile loads: non-temporal (the nt bit).  Every latent
+// row is read once per launch (the row tiles of a share read it together), and
+// streaming it past the caches measured 9% faster on a bf16 cache of 16-row
+// requests (H16 q1: 139 -> 126 us) and no slower elsewhere.
+constexpr int kKvCpol = 2;
 
 // ---------------------------------------------------------------------------
 // Many rows per request (q_len x H > 64, bf16 KV): the flash-attention shape.
@@ -413,7 +418,7 @@ __device__ __forceinline__ void dma_tile(const AttnParams& p, const int* s_pages
     const uint32_t page = s_pages[pi];
     const uint64_t off = (uint64_t)page * ks0 + (pslot * ks1 + kc + 8 * piece);
     if (i < kDma)
-      __builtin_amdgcn_global_load_lds(kbase + off, (PA_LDS void*)(stage + 1024 * i), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(kbase + off, (PA_LDS void*)(stage + 1024 * i), 16, 0, kKvCpol);
   }
 }
 
@@ -473,7 +478,7 @@ __device__ __forceinline__ void dma_tile8(const AttnParams& p, const int* s_page
     const uint32_t page = s_pages[pi];
     const uint64_t off = (uint64_t)page * ks0 + (pslot * ks1 + kc + 16 * (piece ^ fp8_swz<SW>(row)));
     if (i < kDma8)
-      __builtin_amdgcn_global_load_lds(kbase + off, (PA_LDS void*)(stage + 1024 * i), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(kbase + off, (PA_LDS void*)(stage + 1024 * i), 16, 0, kKvCpol);
   }
 }
 
@@ -518,7 +523,7 @@ struct PageLanes {
     const int i = r * kNW2 + w;                                                               \
     const uint32_t off = (uint32_t)min(pl.row[r], last) * ks1 + pl.off[r];                    \
     if (i < KD)                                                                               \
-      __builtin_amdgcn_global_load_lds(kbase + base + off, (PA_LDS void*)(stage + 1024 * i), 16, 0, 0); \
+      __builtin_amdgcn_global_load_lds(kbase + base + off, (PA_LDS void*)(stage + 1024 * i), 16, 0, kKvCpol); \
   }
 __device__ __forceinline__ void dma_page_bf16(const AttnParams& p, int page, uint8_t* stage, int jb,
                                               int we, int wbP, const PageLanes<false>& pl, int w) {
@@ -994,10 +999,10 @@ __device__ __forceinline__ f32x4_t mfma_fp8_b16th(const i32x8_t& a, const i32x8_
 // so it inserts no waits for it before LDS reads that it cannot tell apart from
 // the stage being filled (the caller waits with an explicit vmcnt(0) and a
 // barrier before a stage is read).  M0 holds the LDS address; one wait state
-// between its write and the load.
+// between its write and the load; non-temporal, as kKvCpol.
 __device__ __forceinline__ void lds_dma16(const void* gaddr, uint8_t* lds) {
   const uint32_t a = (uint32_t)(uintptr_t)(PA_LDS uint8_t*)lds;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                :
                : "v"(gaddr), "s"(a)
                : "memory", "m0");

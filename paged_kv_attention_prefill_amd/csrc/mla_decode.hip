@@ -29,7 +29,9 @@ constexpr int kPageWinM = 256;               // page ids staged in LDS at a time
 // Cache policy of the KV tile loads: non-temporal (the nt bit).  Every latent
 // row is read once per launch (the row tiles of a share read it together), and
 // streaming it past the caches measured 9% faster on a bf16 cache of 16-row
-// requests (H16 q1: 139 -> 126 us) and no slower elsewhere.
+// requests (H16 q1: 139 -> 126 us by events), within 1-2% on the other shapes,
+// and 3% slower only on the fp8 page-size-1 row gather (576-byte rows that
+// share 128-byte lines).
 constexpr int kKvCpol = 2;
 
 // ---------------------------------------------------------------------------
